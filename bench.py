@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Benchmark of the online-softmax attention hot path on one MI355X.
+
+One step runs every operation of the path once on its standard workload,
+inputs already resident in HBM:
+
+  softmax   osm_softmax_rows        4096 x 32000 fp32, N(0,9) + one spike/row in [20,90)
+  fwd       osm_attn_fwd            bf16 B=4 H=32 N=4096 d=128, non-causal   (the headline)
+  fwd_causal osm_attn_fwd           bf16 B=8 H=16 N=8192 d=128, causal, lengths U[1024,8192]
+  decode    osm_attn_decode_splitkv bf16 B=16 Hq=32 Hkv=8 d=128, L U[4096,32768], 256-key pieces
+                                    (piece summaries + merge)
+
+Each call is timed with HIP events on the stream it runs on (torch's current
+stream); ``value`` is the headline forward's TFLOP/s.  The CPU oracle is timed
+on a bounded sample of the headline workload as a reported baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s & % MFMA peak (N=4K/32K); softmax/decode GB/s & % HBM peak"
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12     # 2516.6 dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+PROFILE_FWD = os.path.join(ROOT, "profiles", "attn_fwd_bf16_d128_B4_H32_N4096.md")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def bf16_dev(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+def traffic_from_profile(path):
+    """HBM bytes per launch recorded with the last rocprofv3 counter runs of
+    the headline forward, or None when absent or stale."""
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.startswith("traffic_bytes_per_launch:"):
+                    v = line.split(":", 1)[1].strip()
+                    return None if v in ("", "null", "stale") else float(v)
+    except OSError:
+        return None
+    return None
+
+
+def cpu_baseline(inp, seconds):
+    """The oracle on the first rows of the headline workload, sized to take
+    about `seconds` on the host's cores."""
+    import oracle
+    orc = oracle.load()
+    q, k, v = inp.widened()
+    B, H, N, d = q.shape
+    flops_per_row = 4.0 * N * d
+    n = 64
+    t0 = time.perf_counter()
+    orc.attention(q, k, v, scale=inp.scale, rows=np.arange(n))
+    dt = time.perf_counter() - t0
+    n = int(min(B * H * N, max(64, n * seconds / max(dt, 1e-3))))
+    t0 = time.perf_counter()
+    orc.attention(q, k, v, scale=inp.scale, rows=np.arange(n))
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(n * flops_per_row / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"first {n} query rows (of {B * H * N}) of the B{B} H{H} N{N} d{d} "
+                      f"non-causal forward, fp64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", choices=["softmax", "fwd", "fwd_causal", "decode"], default=None,
+                    help="run one operation only (for profiling)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by batch/head with no exchange; see DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_attention_online_softmax_amd as osm
+    from exact_attention_online_softmax_amd import inputs
+
+    osm.load_library()
+    torch.cuda.set_device(0)
+    names = ["softmax", "fwd", "fwd_causal", "decode"] if args.only is None else [args.only]
+    calls, work = {}, {}
+
+    if "softmax" in names:
+        log("inputs: softmax 4096 x 32000")
+        x = torch.from_numpy(inputs.config2()).to("cuda")
+        y = torch.empty_like(x)
+        calls["softmax"] = lambda: osm.softmax_rows(x, out=y)
+        # one HBM read + one HBM write per element: the row stays in registers
+        work["softmax"] = ("hbm", 8.0 * x.numel(), "4096 x 32000 fp32, 8 B/elem")
+    if "fwd" in names or args.only is None:
+        log("inputs: fwd B4 H32 N4096 d128")
+        inp3 = inputs.config3()
+        q3, k3, v3 = (bf16_dev(a, torch) for a in (inp3.q, inp3.k, inp3.v))
+        o3 = torch.empty_like(q3)
+        l3 = torch.empty(q3.shape[:3], dtype=torch.float32, device="cuda")
+        if "fwd" in names:
+            calls["fwd"] = lambda: osm.attn_fwd(q3, k3, v3, scale=inp3.scale, out=o3, lse=l3)
+            B, H, N, d = q3.shape
+            work["fwd"] = ("mfma", 4.0 * B * H * N * N * d, "B4 H32 N4096 d128 non-causal")
+    if "fwd_causal" in names:
+        log("inputs: fwd causal B8 H16 N8192 d128 varlen")
+        inp4 = inputs.config4()
+        q4, k4, v4 = (bf16_dev(a, torch) for a in (inp4.q, inp4.k, inp4.v))
+        o4 = torch.empty_like(q4)
+        l4 = torch.empty(q4.shape[:3], dtype=torch.float32, device="cuda")
+        lens4 = torch.from_numpy(inp4.seqlens_q).to("cuda")
+        scale4 = inp4.scale
+        calls["fwd_causal"] = lambda: osm.attn_fwd(q4, k4, v4, scale=scale4, causal=True,
+                                                   seqlens_q=lens4, seqlens_k=lens4, out=o4, lse=l4)
+        Lb = inp4.seqlens_q.astype(np.float64)
+        work["fwd_causal"] = ("mfma", 4.0 * 128 * 16 * float(np.sum(Lb * (Lb + 1) / 2)),
+                              "B8 H16 N8192 d128 causal, L_b U[1024,8192]")
+        del inp4
+    if "decode" in names:
+        log("inputs: decode B16 Hq32 Hkv8 L<=32768 d128")
+        inp5 = inputs.config5()
+        q5 = bf16_dev(inp5.q[:, :, 0, :], torch)
+        k5, v5 = bf16_dev(inp5.k, torch), bf16_dev(inp5.v, torch)
+        lens5 = torch.from_numpy(inp5.seqlens_k).to("cuda")
+        ws5 = torch.empty(osm.decode_workspace_bytes(16, 32, 32768, 128, 256), dtype=torch.uint8,
+                          device="cuda")
+        o5 = torch.empty_like(q5)
+        l5 = torch.empty((16, 32), dtype=torch.float32, device="cuda")
+        scale5 = inp5.scale
+        calls["decode"] = lambda: osm.attn_decode_splitkv(q5, k5, v5, lens5, scale=scale5,
+                                                          split_size=256, workspace=ws5, out=o5,
+                                                          lse=l5)
+        Lb = inp5.seqlens_k.astype(np.float64)
+        pieces = np.ceil(Lb / 256)
+        kv = float(np.sum(Lb)) * 8 * 128 * 2 * 2
+        io = 16 * 32 * 128 * 2 * 2 + 16 * 32 * 4
+        partials = 2.0 * float(np.sum(pieces)) * 32 * (128 + 2) * 4
+        work["decode"] = ("hbm", kv + io + partials, "B16 Hq32 Hkv8 d128, L_b U[4096,32768], split 256")
+        del inp5
+
+    # ---- warmup, then K timed steps --------------------------------------
+    for _ in range(args.warmup):
+        for n in names:
+            calls[n]()
+    torch.cuda.synchronize()
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for n in names}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for n in names:
+            a, b = ev[n][s]
+            a.record()
+            calls[n]()
+            b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in names}
+
+    comps = {}
+    for n in names:
+        bound, amount, desc = work[n]
+        t = ms[n] / 1e3
+        if bound == "mfma":
+            ach, peak, unit = amount / t / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+        else:
+            ach, peak, unit = amount / t / 1e9, PEAK_HBM_GBS, "GB/s"
+        comps[n] = {"workload": desc, "ms": round(ms[n], 4), "achieved": round(ach, 2),
+                    "unit": unit, "bound": "hbm" if bound == "hbm" else "mfma",
+                    "peak": round(peak, 1), "frac": round(ach / peak, 4),
+                    "algorithmic": amount}
+    head = "fwd" if "fwd" in comps else names[0]
+    hc = comps[head]
+    roofline = {"bound": hc["bound"], "achieved": hc["achieved"], "peak": hc["peak"],
+                "unit": hc["unit"], "frac": hc["frac"],
+                "traffic": traffic_from_profile(PROFILE_FWD) if head == "fwd" else None}
+    out = {"metric": METRIC, "value": hc["achieved"], "unit": hc["unit"], "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"attn_fwd {hc['workload']}" if head == "fwd" else hc["workload"],
+                      "step": "softmax_rows + attn_fwd (non-causal) + attn_fwd (causal varlen) "
+                              "+ attn_decode_splitkv" if args.only is None else args.only,
+                      "global_batch": 4, "seq_len": 4096, "parallelism": "none (1 GPU)"},
+           "roofline": roofline, "components": comps}
+    if not args.no_cpu_baseline and args.only is None:
+        log("cpu baseline: oracle on a sample of the headline workload")
+        out["cpu_baseline"] = cpu_baseline(inp3, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,111 @@
+// abi.cpp -- the C ABI of libosm: argument validation on the host, then
+// dispatch to the gfx950 kernels on the caller's stream.  Declared in
+// include/osm.h, which documents every argument, layout and error code.
+//
+// Every check runs before any HIP call, so an error other than OSM_ERR_HIP
+// means nothing was launched and no output was touched.  No C++ exception
+// escapes (none is thrown here, and HIP's C API throws none).
+#include <math.h>
+
+#include "../../include/osm.h"
+#include "osm_internal.h"
+
+namespace {
+
+inline osm_status hip_status(hipError_t e) { return e == hipSuccess ? OSM_OK : OSM_ERR_HIP; }
+
+constexpr int64_t kMaxDecodeScores = 16384;   // heads-per-group * split_size (64 KiB of LDS)
+
+}  // namespace
+
+extern "C" {
+
+const char *osm_status_str(osm_status status) {
+    switch (status) {
+        case OSM_OK: return "OSM_OK";
+        case OSM_ERR_NULL: return "OSM_ERR_NULL: a required pointer is NULL";
+        case OSM_ERR_SHAPE: return "OSM_ERR_SHAPE: invalid or inconsistent sizes";
+        case OSM_ERR_UNSUPPORTED: return "OSM_ERR_UNSUPPORTED: dtype/head_dim/layout not implemented";
+        case OSM_ERR_WORKSPACE: return "OSM_ERR_WORKSPACE: workspace missing or too small";
+        case OSM_ERR_HIP: return "OSM_ERR_HIP: a HIP runtime call failed";
+    }
+    return "OSM_ERR_UNKNOWN";
+}
+
+osm_status osm_softmax_rows(const float *x, float *y, int64_t rows, int64_t cols, int64_t ld_x,
+                            int64_t ld_y, float *row_max, float *row_sum, osm_stream stream) {
+    if (rows < 0 || cols < 0 || ld_x < cols || ld_y < cols) return OSM_ERR_SHAPE;
+    if (rows == 0) return OSM_OK;
+    if ((!x || !y) && cols > 0) return OSM_ERR_NULL;
+    if (cols == 0 && !row_max && !row_sum) return OSM_OK;
+    osm::SoftmaxArgs a{x, y, rows, cols, ld_x, ld_y, row_max, row_sum};
+    const osm::SoftmaxPlan p = osm::plan_softmax_rows(cols, 0);
+    return hip_status(osm::launch_softmax_rows(a, p, static_cast<hipStream_t>(stream)));
+}
+
+osm_status osm_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                        osm_dtype dtype, int32_t batch, int32_t heads_q, int32_t heads_kv,
+                        int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                        const int32_t *seqlens_q, const int32_t *seqlens_k, float scale,
+                        int32_t causal, osm_stream stream) {
+    if (batch < 1 || heads_q < 1 || heads_kv < 1 || head_dim < 1 || seqlen_q < 0 || seqlen_k < 0 ||
+        heads_q % heads_kv != 0 || !(scale > 0.0f) || !isfinite(scale) || (causal != 0 && causal != 1))
+        return OSM_ERR_SHAPE;
+    if (dtype != OSM_BF16 || head_dim != 128) return OSM_ERR_UNSUPPORTED;
+    if (seqlen_q == 0) return OSM_OK;
+    if (!q || !o || (seqlen_k > 0 && (!k || !v))) return OSM_ERR_NULL;
+    osm::AttnFwdArgs a{q, k, v, o, lse, batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim,
+                       seqlens_q, seqlens_k, scale, causal};
+    return hip_status(osm::launch_attn_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t osm_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t max_seqlen_k,
+                                  int32_t head_dim, int32_t split_size) {
+    if (batch < 1 || heads_q < 1 || max_seqlen_k < 1 || head_dim < 1 || split_size < 1) return 0;
+    return osm::decode_layout(batch, heads_q, max_seqlen_k, head_dim, split_size).total;
+}
+
+osm_status osm_attn_decode_splitkv(const void *q, const void *k_cache, const void *v_cache,
+                                   void *o, float *lse, osm_dtype dtype, int32_t batch,
+                                   int32_t heads_q, int32_t heads_kv, int32_t max_seqlen_k,
+                                   int32_t head_dim, const int32_t *seqlens_k, float scale,
+                                   int32_t split_size, void *workspace, size_t workspace_bytes,
+                                   osm_stream stream) {
+    if (batch < 1 || heads_q < 1 || heads_kv < 1 || max_seqlen_k < 1 || head_dim < 1 ||
+        heads_q % heads_kv != 0 || !(scale > 0.0f) || !isfinite(scale) || split_size < 1)
+        return OSM_ERR_SHAPE;
+    const int group = heads_q / heads_kv;
+    if ((dtype != OSM_F32 && dtype != OSM_BF16) || (head_dim != 64 && head_dim != 128) ||
+        (group != 1 && group != 2 && group != 4 && group != 8) || split_size % 64 != 0 ||
+        split_size > 8192 || (int64_t)group * split_size > kMaxDecodeScores)
+        return OSM_ERR_UNSUPPORTED;
+    if (!q || !k_cache || !v_cache || !o || !seqlens_k) return OSM_ERR_NULL;
+    const osm::DecodeLayout lay = osm::decode_layout(batch, heads_q, max_seqlen_k, head_dim, split_size);
+    if (!workspace || workspace_bytes < lay.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
+        return OSM_ERR_WORKSPACE;
+    osm::DecodeArgs a{q, k_cache, v_cache, o, lse, dtype == OSM_BF16 ? 1 : 0, batch, heads_q,
+                      heads_kv, max_seqlen_k, head_dim, seqlens_k, scale, split_size, workspace};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = osm::launch_decode_split(a, lay, s);
+    if (e != hipSuccess) return OSM_ERR_HIP;
+    const char *ws = static_cast<const char *>(workspace);
+    osm::MergeArgs m{reinterpret_cast<const float *>(ws + lay.off_m),
+                     reinterpret_cast<const float *>(ws + lay.off_l),
+                     reinterpret_cast<const float *>(ws + lay.off_o),
+                     lay.rows, lay.chunks, head_dim, o, a.dtype, lse};
+    return hip_status(osm::launch_merge_partials(m, s));
+}
+
+osm_status osm_merge_partials(const float *part_m, const float *part_l, const float *part_o,
+                              int64_t rows, int32_t num_splits, int32_t head_dim, void *o,
+                              osm_dtype out_dtype, float *lse, osm_stream stream) {
+    if (rows < 0 || num_splits < 1 || head_dim < 1) return OSM_ERR_SHAPE;
+    if ((out_dtype != OSM_F32 && out_dtype != OSM_BF16) || head_dim > 512) return OSM_ERR_UNSUPPORTED;
+    if (rows == 0) return OSM_OK;
+    if (!part_m || !part_l || !part_o || !o) return OSM_ERR_NULL;
+    osm::MergeArgs m{part_m, part_l, part_o, rows, num_splits, head_dim, o,
+                     out_dtype == OSM_BF16 ? 1 : 0, lse};
+    return hip_status(osm::launch_merge_partials(m, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// osm_internal.h -- host-side launch interfaces between the C ABI layer and
+// the kernel translation units of libosm (not installed, not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace osm {
+
+// ---- row softmax ----------------------------------------------------------
+struct SoftmaxArgs {
+    const float *x;
+    float *y;
+    int64_t rows, cols, ld_x, ld_y;
+    float *row_max, *row_sum;
+};
+struct SoftmaxPlan {
+    bool resident;   // row held in registers (one HBM read) vs two streaming passes
+    int nv;          // float4 vectors per lane (resident)
+    int threads;     // workgroup size
+};
+// force_variant: 0 = automatic, 1 = streaming
+SoftmaxPlan plan_softmax_rows(int64_t cols, int force_variant);
+hipError_t launch_softmax_rows(const SoftmaxArgs &a, const SoftmaxPlan &p, hipStream_t s);
+
+// ---- fused attention forward ---------------------------------------------
+struct AttnFwdArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    int batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim;
+    const int32_t *seqlens_q, *seqlens_k;
+    float scale;
+    int causal;
+};
+hipError_t launch_attn_fwd(const AttnFwdArgs &a, hipStream_t s);
+
+// ---- split-KV decode + merge ----------------------------------------------
+struct DecodeLayout {
+    int64_t rows;        // batch * heads_q
+    int32_t chunks;      // C = ceil(max_seqlen_k / split)
+    size_t off_m, off_l, off_o, total;
+};
+DecodeLayout decode_layout(int64_t batch, int64_t heads_q, int64_t max_seqlen_k, int64_t head_dim,
+                           int64_t split);
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    int dtype;           // 0 f32, 1 bf16
+    int batch, heads_q, heads_kv, max_seqlen_k, head_dim;
+    const int32_t *seqlens_k;
+    float scale;
+    int split;
+    void *workspace;
+};
+hipError_t launch_decode_split(const DecodeArgs &a, const DecodeLayout &lay, hipStream_t s);
+
+struct MergeArgs {
+    const float *part_m, *part_l, *part_o;
+    int64_t rows;
+    int num_splits, head_dim;
+    void *o;
+    int out_dtype;       // 0 f32, 1 bf16
+    float *lse;
+};
+hipError_t launch_merge_partials(const MergeArgs &a, hipStream_t s);
+
+}  // namespace osm

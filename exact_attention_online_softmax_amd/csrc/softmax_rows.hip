@@ -1,0 +1,237 @@
+// softmax_rows.hip -- row softmax with the online normalizer, gfx950.
+//
+// [P3] "Two numbers that can be updated" / "The recurrence, and a proof that
+// it is right": a running maximum m and a running sum l of exp(x - m),
+// rescaled by exp(m_old - m_new) when the maximum grows; [P3] "Merging
+// partial results": summaries of disjoint pieces of a row merge exactly, in
+// any order.  [P3] "Three passes, and why that is a problem" counts memory
+// accesses per element: safe softmax 4, the two-pass online normalizer 3.
+//
+// One workgroup per row.  Each lane owns a strided set of float4 vectors of
+// the row (consecutive lanes read consecutive 16-byte vectors, so every wave
+// load is a contiguous 1 KiB).  Two variants:
+//
+//  * resident (cols <= 4 * NV * blockDim): the row is read from HBM once and
+//    stays in VGPRs.  Each lane summarizes its piece as (m_lane, l_lane) and
+//    keeps e_i = exp(x_i - m_lane); the lane summaries are merged across the
+//    wave (butterfly) and across waves (LDS); then y_i = e_i * exp(m_lane -
+//    m) / l.  HBM traffic: one load and one store per element (8 B).
+//
+//  * streaming (any cols): pass 1 reads the row and runs the recurrence per
+//    lane, one rescale per float4 vector; lane summaries are merged as above;
+//    pass 2 reads the row again and writes y = exp(x - m) / l.  HBM traffic:
+//    two loads and one store per element (12 B), the pages' count.
+#include "osm_device.h"
+#include "osm_internal.h"
+
+namespace osm {
+
+namespace {
+
+constexpr int kMaxWaves = 16;   // blockDim <= 1024
+
+// Merge the per-lane (m, l) of a whole workgroup; every thread gets the row's.
+__device__ __forceinline__ void block_merge_ml(float &m, float &l, float *sm, float *sl) {
+    wave_merge_ml(m, l);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nwaves = blockDim.x >> 6;
+    if (lane == 0) {
+        sm[wave] = m;
+        sl[wave] = l;
+    }
+    __syncthreads();
+    m = kNegInf;
+    l = 0.0f;
+    for (int w = 0; w < nwaves; ++w) merge_ml(m, l, sm[w], sl[w]);
+    __syncthreads();   // sm/sl are reused by the next row
+}
+
+__device__ __forceinline__ float max4(float4 v) {
+    return fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+}
+
+// Load vector `vec` (elements 4*vec .. 4*vec+3) of a row; entries at or past
+// `cols` read as -inf.  ALIGNED: the row start is 16-byte aligned.
+template <bool ALIGNED>
+__device__ __forceinline__ float4 load_vec(const float *row, int64_t vec, int64_t cols) {
+    int64_t e = vec * 4;
+    if (ALIGNED && e + 4 <= cols) return *reinterpret_cast<const float4 *>(row + e);
+    float4 v;
+    v.x = (e + 0 < cols) ? row[e + 0] : kNegInf;
+    v.y = (e + 1 < cols) ? row[e + 1] : kNegInf;
+    v.z = (e + 2 < cols) ? row[e + 2] : kNegInf;
+    v.w = (e + 3 < cols) ? row[e + 3] : kNegInf;
+    return v;
+}
+
+template <bool ALIGNED>
+__device__ __forceinline__ void store_vec(float *row, int64_t vec, int64_t cols, float4 v) {
+    int64_t e = vec * 4;
+    if (ALIGNED && e + 4 <= cols) {
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<f32x4 *>(row + e));
+        return;
+    }
+    if (e + 0 < cols) row[e + 0] = v.x;
+    if (e + 1 < cols) row[e + 1] = v.y;
+    if (e + 2 < cols) row[e + 2] = v.z;
+    if (e + 3 < cols) row[e + 3] = v.w;
+}
+
+template <int NV, bool ALIGNED>
+__global__ void __launch_bounds__(1024)
+softmax_rows_resident(const float *x, float *y, int64_t rows,
+                      int64_t cols, int64_t ld_x, int64_t ld_y, float *__restrict__ row_max,
+                      float *__restrict__ row_sum) {
+    __shared__ float sm[kMaxWaves], sl[kMaxWaves];
+    const int64_t nvec = (cols + 3) / 4;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const float *xr = x + r * ld_x;
+        float4 v[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            int64_t vec = threadIdx.x + (int64_t)i * blockDim.x;
+            v[i] = (vec < nvec) ? load_vec<ALIGNED>(xr, vec, cols)
+                                : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+        }
+        // this lane's piece: maximum, then e_i = exp(x_i - m_lane) and their sum
+        float m_lane = kNegInf;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) m_lane = fmaxf(m_lane, max4(v[i]));
+        float l_lane = 0.0f;
+        const bool empty = (m_lane == kNegInf);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            v[i].x = empty ? 0.0f : exp_acc(v[i].x - m_lane);
+            v[i].y = empty ? 0.0f : exp_acc(v[i].y - m_lane);
+            v[i].z = empty ? 0.0f : exp_acc(v[i].z - m_lane);
+            v[i].w = empty ? 0.0f : exp_acc(v[i].w - m_lane);
+            l_lane += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+        }
+        float m = m_lane, l = l_lane;
+        block_merge_ml(m, l, sm, sl);
+        // rebase this lane's numerators on the row maximum and divide once
+        float w = (empty || m == kNegInf) ? 0.0f : exp_acc(m_lane - m) / l;
+        float *yr = y + r * ld_y;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            int64_t vec = threadIdx.x + (int64_t)i * blockDim.x;
+            if (vec < nvec) {
+                float4 o = make_float4(v[i].x * w, v[i].y * w, v[i].z * w, v[i].w * w);
+                store_vec<ALIGNED>(yr, vec, cols, o);
+            }
+        }
+        if (threadIdx.x == 0) {
+            if (row_max) row_max[r] = m;
+            if (row_sum) row_sum[r] = l;
+        }
+    }
+}
+
+template <bool ALIGNED>
+__global__ void __launch_bounds__(1024)
+softmax_rows_streaming(const float *x, float *y, int64_t rows,
+                       int64_t cols, int64_t ld_x, int64_t ld_y, float *__restrict__ row_max,
+                       float *__restrict__ row_sum) {
+    __shared__ float sm[kMaxWaves], sl[kMaxWaves];
+    const int64_t nvec = (cols + 3) / 4;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const float *xr = x + r * ld_x;
+        // pass 1: the recurrence over this lane's vectors, one rescale per vector
+        float m = kNegInf, l = 0.0f;
+        for (int64_t vec = threadIdx.x; vec < nvec; vec += blockDim.x) {
+            float4 v = load_vec<ALIGNED>(xr, vec, cols);
+            float mn = fmaxf(m, max4(v));
+            if (mn == kNegInf) continue;          // nothing visible yet
+            float alpha = (m == kNegInf) ? 0.0f : exp_acc(m - mn);
+            float ms = mn * kLog2e;
+            float s = fast_exp2(fmaf(v.x, kLog2e, -ms)) + fast_exp2(fmaf(v.y, kLog2e, -ms)) +
+                      fast_exp2(fmaf(v.z, kLog2e, -ms)) + fast_exp2(fmaf(v.w, kLog2e, -ms));
+            l = fmaf(l, alpha, s);
+            m = mn;
+        }
+        block_merge_ml(m, l, sm, sl);
+        // pass 2: read again, write y = exp(x - m) / l
+        const float inv_l = (m == kNegInf) ? 0.0f : 1.0f / l;
+        float *yr = y + r * ld_y;
+        for (int64_t vec = threadIdx.x; vec < nvec; vec += blockDim.x) {
+            float4 v = load_vec<ALIGNED>(xr, vec, cols);
+            float4 o;
+            if (m == kNegInf) {
+                o = make_float4(0.f, 0.f, 0.f, 0.f);
+            } else {
+                o.x = exp_acc(v.x - m) * inv_l;
+                o.y = exp_acc(v.y - m) * inv_l;
+                o.z = exp_acc(v.z - m) * inv_l;
+                o.w = exp_acc(v.w - m) * inv_l;
+            }
+            store_vec<ALIGNED>(yr, vec, cols, o);
+        }
+        if (threadIdx.x == 0) {
+            if (row_max) row_max[r] = m;
+            if (row_sum) row_sum[r] = l;
+        }
+    }
+}
+
+template <int NV, bool A>
+hipError_t launch_resident(const SoftmaxArgs &a, int threads, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((softmax_rows_resident<NV, A>), dim3(grid), dim3(threads), 0, s, a.x, a.y,
+                       a.rows, a.cols, a.ld_x, a.ld_y, a.row_max, a.row_sum);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Plan: smallest power-of-two workgroup (64..1024 threads) for which the row
+// fits in NV float4 registers per lane; rows too long for 1024 x 16 vectors
+// take the streaming two-pass kernel.
+SoftmaxPlan plan_softmax_rows(int64_t cols, int force_variant) {
+    SoftmaxPlan p{};
+    const int64_t nvec = (cols + 3) / 4;
+    if (force_variant != 1) {
+        for (int nv : {4, 8, 16}) {
+            for (int t = 64; t <= 1024; t *= 2) {
+                if ((int64_t)t * nv >= nvec) {
+                    // prefer >= 256 threads for long rows (more loads in flight)
+                    if (nvec > 4096 && t < 256) continue;
+                    p.resident = true;
+                    p.nv = nv;
+                    p.threads = t;
+                    return p;
+                }
+            }
+        }
+    }
+    p.resident = false;
+    p.nv = 0;
+    p.threads = 1024;
+    return p;
+}
+
+hipError_t launch_softmax_rows(const SoftmaxArgs &a, const SoftmaxPlan &p, hipStream_t s) {
+    if (a.rows == 0) return hipSuccess;
+    const bool aligned = ((reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.y)) % 16 == 0) &&
+                         (a.ld_x % 4 == 0) && (a.ld_y % 4 == 0);
+    const int grid = (int)(a.rows < 1048576 ? a.rows : 1048576);
+    if (p.resident) {
+        switch (p.nv) {
+            case 4: return aligned ? launch_resident<4, true>(a, p.threads, grid, s)
+                                   : launch_resident<4, false>(a, p.threads, grid, s);
+            case 8: return aligned ? launch_resident<8, true>(a, p.threads, grid, s)
+                                   : launch_resident<8, false>(a, p.threads, grid, s);
+            default: return aligned ? launch_resident<16, true>(a, p.threads, grid, s)
+                                    : launch_resident<16, false>(a, p.threads, grid, s);
+        }
+    }
+    if (aligned)
+        hipLaunchKernelGGL((softmax_rows_streaming<true>), dim3(grid), dim3(p.threads), 0, s, a.x,
+                           a.y, a.rows, a.cols, a.ld_x, a.ld_y, a.row_max, a.row_sum);
+    else
+        hipLaunchKernelGGL((softmax_rows_streaming<false>), dim3(grid), dim3(p.threads), 0, s, a.x,
+                           a.y, a.rows, a.cols, a.ld_x, a.ld_y, a.row_max, a.row_sum);
+    return hipGetLastError();
+}
+
+}  // namespace osm

@@ -1,0 +1,207 @@
+/*
+ * osm.h -- exact softmax attention via the online-softmax recurrence,
+ * for AMD Instinct MI355X (gfx950).  C ABI of libosm.so.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [P1] "Online softmax: how FlashAttention skips the N x N matrix" (dev.to)
+ *   [P2] "Online softmax" (guide.dupenodi.dev)
+ *   [P3] "Online softmax" (zerotofrontier.app, efficient-attention chapter)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every data pointer is DEVICE memory owned by the caller (for example a
+ *   PyTorch tensor's data_ptr()).  The library never allocates, frees or
+ *   retains memory, keeps no global mutable state and is safe to call from
+ *   several host threads.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *   runs asynchronously.  Outputs are valid after the stream is synchronized.
+ *   Faults inside a kernel surface at the caller's next synchronization.
+ * - Tensors are contiguous, row-major.  Attention tensors are
+ *   [batch][heads][positions][head_dim]; per-query LSE is [batch][heads][positions].
+ * - Every argument check happens on the host BEFORE any HIP call: on any
+ *   error code other than OSM_ERR_HIP nothing was launched and no output was
+ *   touched.  OSM_ERR_HIP means a HIP runtime call (device query or launch)
+ *   failed; some kernels of the call may already have been enqueued.
+ * - No C++ exception crosses this interface.  Sizes and offsets are 64-bit
+ *   where a tensor can exceed 2^31 elements.
+ * - Device-side length arrays are clamped to [0, extent] by the kernels.
+ * - Natural logarithms throughout the interface (m, LSE).  Kernels work in
+ *   base 2 internally ([P3] "Precision, and what can still go wrong": fold
+ *   log2(e) into the score scale, convert the stored log-sum-exp back).
+ * - A query row with no visible key (fully masked, padded, or zero keys)
+ *   produces O = +0 and LSE = -inf ([P3] same section: a row masked
+ *   everywhere ends with l = 0 and is handled explicitly; [P3] "Merging
+ *   partial results": the empty set's summary is (-inf, 0, 0)).
+ */
+#ifndef OSM_H
+#define OSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    OSM_OK = 0,
+    OSM_ERR_NULL = 1,        /* a required pointer is NULL */
+    OSM_ERR_SHAPE = 2,       /* a size is negative, zero where it must not be, or inconsistent */
+    OSM_ERR_UNSUPPORTED = 3, /* valid request this build does not implement (dtype, head_dim, alignment) */
+    OSM_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than osm_decode_workspace_bytes() */
+    OSM_ERR_HIP = 5          /* a HIP runtime call failed (no device, launch failure) */
+} osm_status;
+
+typedef enum {
+    OSM_F32 = 0,             /* IEEE fp32 */
+    OSM_BF16 = 1             /* bfloat16 (8-bit exponent, 7-bit mantissa), round-to-nearest-even on output */
+} osm_dtype;
+
+typedef void *osm_stream;    /* hipStream_t */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *osm_status_str(osm_status status);
+
+/*
+ * osm_softmax_rows -- softmax of each row of an fp32 matrix with the
+ * two-pass online normalizer.
+ *
+ * [P3] "Two numbers that can be updated" and "The recurrence, and a proof
+ * that it is right": pass 1 keeps a running maximum m and a running sum l of
+ * exp(x - m), rescaling l by exp(m_old - m_new) whenever the maximum grows;
+ * partial (m, l) pairs of pieces of a row are combined with the merge of
+ * [P3] "Merging partial results".  Pass 2 writes y_i = exp(x_i - m) / l.
+ * [P2] "Walking through it" gives the same per-tile procedure.
+ *
+ *   x        fp32, row r at x + r*ld_x, `cols` valid entries (read only)
+ *   y        fp32, row r at y + r*ld_y (written, `cols` entries per row)
+ *   rows, cols  rows >= 0, cols >= 0 (rows == 0: nothing is launched)
+ *   ld_x, ld_y  row strides in elements, >= cols
+ *   row_max  optional fp32 [rows]: m = max_i x_i (natural units)
+ *   row_sum  optional fp32 [rows]: l = sum_i exp(x_i - m)
+ * A row of all -inf (or cols == 0) gives y = 0, m = -inf, l = 0.
+ * +inf or NaN inside a row is not special-cased (NaN results).
+ * x and y may not overlap unless they are the same buffer with ld_x == ld_y.
+ * Errors: OSM_ERR_NULL (x or y NULL with rows*cols > 0), OSM_ERR_SHAPE
+ * (negative sizes, ld < cols), OSM_ERR_HIP.
+ */
+osm_status osm_softmax_rows(const float *x, float *y, int64_t rows, int64_t cols,
+                            int64_t ld_x, int64_t ld_y, float *row_max, float *row_sum,
+                            osm_stream stream);
+
+/*
+ * osm_attn_fwd -- fused exact attention forward, O = softmax(scale * Q K^T) V,
+ * plus the per-query log-sum-exp.
+ *
+ * [P3] "Blocks, the bridge to FlashAttention" (the block step with matrices
+ * m, l, O~: S_j = Q K_j^T scaled, m_new = max(m, rowmax S_j),
+ * P~ = exp(S_j - m_new), l = exp(m - m_new) l + rowsum P~,
+ * O~ = diag(exp(m - m_new)) O~ + P~ V_j), one division at the end
+ * ([P3] "From weights to outputs"), LSE = m + log l ([P3] same section);
+ * masks applied inside the tile loop ([P2] "Walking through it", the mask
+ * paragraph).  The N x N score matrix is never written to memory ([P1] "Why
+ * does removing the N x N matrix matter if the FLOPs are the same?").
+ *
+ *   q     [batch][heads_q][seqlen_q][head_dim]  (dtype)
+ *   k, v  [batch][heads_kv][seqlen_k][head_dim] (dtype)
+ *   o     [batch][heads_q][seqlen_q][head_dim]  (dtype, written)
+ *   lse   fp32 [batch][heads_q][seqlen_q] (written; may be NULL)
+ *   heads_q % heads_kv == 0; query head h reads key/value head
+ *         h / (heads_q / heads_kv).
+ *   seqlens_q, seqlens_k  optional DEVICE int32 [batch]: valid prefix
+ *         lengths (right padding).  NULL = full length.  Key j is visible to
+ *         query i iff i < Lq_b and j < Lk_b and (causal == 0 or j <= i).
+ *         Positions past the valid length are never read into a sum; they
+ *         may hold any bits (NaN included).  Query rows i >= Lq_b are
+ *         written as O = 0, LSE = -inf.
+ *   scale multiplies Q K^T (for example 1/sqrt(head_dim)); must be finite and > 0.
+ *   causal 0 or 1 (top-left aligned: j <= i).
+ * Supported: dtype OSM_BF16, head_dim 128; fp32 accumulation of both
+ * products, fp32 running state, O rounded to bf16 once at the end.
+ * Errors: OSM_ERR_NULL, OSM_ERR_SHAPE (non-positive batch/heads/head_dim,
+ * negative seqlens, heads_q % heads_kv != 0, scale not finite or <= 0),
+ * OSM_ERR_UNSUPPORTED (other dtype or head_dim), OSM_ERR_HIP.
+ */
+osm_status osm_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                        osm_dtype dtype, int32_t batch, int32_t heads_q, int32_t heads_kv,
+                        int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                        const int32_t *seqlens_q, const int32_t *seqlens_k, float scale,
+                        int32_t causal, osm_stream stream);
+
+/*
+ * osm_decode_workspace_bytes -- bytes of device workspace that
+ * osm_attn_decode_splitkv needs for these sizes: fp32 partial triples
+ * m [batch][heads_q][C], l [batch][heads_q][C], O~ [batch][heads_q][C][head_dim]
+ * with C = ceil(max_seqlen_k / split_size), each array 256-byte aligned.
+ * Returns 0 for invalid sizes.
+ */
+size_t osm_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t max_seqlen_k,
+                                  int32_t head_dim, int32_t split_size);
+
+/*
+ * osm_attn_decode_splitkv -- attention of one new query token per
+ * (batch, query head) against a KV cache, with the keys split into pieces
+ * of `split_size` that are summarized independently and then merged.
+ *
+ * [P1] "How does this connect to KV-cache decoding?": the cache holds raw
+ * K and V.  [P3] "Merging partial results": each piece c of a row's keys is
+ * summarized by (m_c, l_c, O~_c) relative to its own maximum, and the
+ * pieces are combined with the merge (associative and commutative, identity
+ * (-inf, 0, 0)); [P3] "The same merge, in log-sum-exp form" names this split
+ * of one query's keys across many thread blocks.
+ *
+ *   q        [batch][heads_q][head_dim]                 (dtype)
+ *   k_cache, v_cache  [batch][heads_kv][max_seqlen_k][head_dim] (dtype)
+ *   o        [batch][heads_q][head_dim]                 (dtype, written)
+ *   lse      fp32 [batch][heads_q] (written; may be NULL)
+ *   seqlens_k  DEVICE int32 [batch], required: keys j < L_b are visible;
+ *            cache rows past L_b are never read into a sum (may hold NaN).
+ *            L_b == 0 gives O = 0, LSE = -inf.
+ *   scale    multiplies q . k; finite, > 0.
+ *   split_size  keys per piece, a multiple of 64 in [64, 8192]; piece c
+ *            covers keys [c*split, min((c+1)*split, L_b)).
+ *   workspace  DEVICE memory of at least osm_decode_workspace_bytes() bytes
+ *            (caller-owned, 256-byte aligned, contents on entry ignored).
+ * Two kernels are enqueued on `stream`: the per-piece summaries, then the
+ * merge (same as osm_merge_partials) reading the workspace.
+ * Supported: dtype OSM_F32 or OSM_BF16; head_dim 64 or 128.
+ * Errors: OSM_ERR_NULL, OSM_ERR_SHAPE, OSM_ERR_UNSUPPORTED,
+ * OSM_ERR_WORKSPACE, OSM_ERR_HIP.
+ */
+osm_status osm_attn_decode_splitkv(const void *q, const void *k_cache, const void *v_cache,
+                                   void *o, float *lse, osm_dtype dtype, int32_t batch,
+                                   int32_t heads_q, int32_t heads_kv, int32_t max_seqlen_k,
+                                   int32_t head_dim, const int32_t *seqlens_k, float scale,
+                                   int32_t split_size, void *workspace, size_t workspace_bytes,
+                                   osm_stream stream);
+
+/*
+ * osm_merge_partials -- merge per-piece summaries of each row into the
+ * row's output and log-sum-exp.
+ *
+ * [P3] "Merging partial results": with m = max(m_A, m_B),
+ * l = l_A exp(m_A - m) + l_B exp(m_B - m) and O~ likewise; the empty set
+ * (-inf, 0, 0) is the identity and is skipped (its l and O~ are not read,
+ * so they may hold any bits).  Then o = O~ / l and LSE = m + log l
+ * ([P3] "From weights to outputs").
+ *
+ *   part_m  fp32 [rows][num_splits]  piece maxima (natural-log units of the
+ *           scaled scores); -inf marks an empty piece
+ *   part_l  fp32 [rows][num_splits]  piece sums, relative to part_m
+ *   part_o  fp32 [rows][num_splits][head_dim]  unnormalized piece outputs
+ *   o       [rows][head_dim] (out_dtype, written)
+ *   lse     fp32 [rows] (written; may be NULL)
+ * A row whose pieces are all empty gives o = 0, LSE = -inf.
+ * Supported: out_dtype OSM_F32 or OSM_BF16; head_dim 1..512;
+ * num_splits >= 1.
+ * Errors: OSM_ERR_NULL, OSM_ERR_SHAPE, OSM_ERR_UNSUPPORTED, OSM_ERR_HIP.
+ */
+osm_status osm_merge_partials(const float *part_m, const float *part_l, const float *part_o,
+                              int64_t rows, int32_t num_splits, int32_t head_dim, void *o,
+                              osm_dtype out_dtype, float *lse, osm_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSM_H */

@@ -1,0 +1,137 @@
+"""The C ABI library without a GPU: it loads, exports every symbol the
+header declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_online_softmax_amd as osm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "osm.h")
+
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+no_gpu_only = pytest.mark.skipif(_has_gpu(), reason="fake-pointer checks run only without a GPU")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return osm.load_library()
+
+
+def test_header_symbols_exported(lib):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"\b(osm_[a-z_]+)\s*\(", text))
+    assert declared == set(osm.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, name in osm.STATUS.items():
+        assert osm.status_str(code).startswith(name)
+    assert osm.status_str(99) == "OSM_ERR_UNKNOWN"
+
+
+def test_workspace_bytes(lib):
+    # m, l: rows * C floats each; O~: rows * C * d floats; each 256-byte aligned
+    rows, C, d = 16 * 32, 128, 128
+    al = lambda n: (n + 255) // 256 * 256
+    assert osm.decode_workspace_bytes(16, 32, 32768, 128, 256) == 2 * al(rows * C * 4) + al(rows * C * d * 4)
+    assert osm.decode_workspace_bytes(1, 1, 4096, 64, 64) == 2 * al(64 * 4) + al(64 * 64 * 4)
+    assert osm.decode_workspace_bytes(1, 1, 4097, 64, 64) == 2 * al(65 * 4) + al(65 * 64 * 4)
+    assert osm.decode_workspace_bytes(0, 1, 1, 64, 64) == 0
+    assert osm.decode_workspace_bytes(1, 1, 1, 64, 0) == 0
+
+
+@no_gpu_only
+def test_softmax_validation(lib):
+    s = None
+    assert lib.osm_softmax_rows(FAKE, FAKE, -1, 4, 4, 4, None, None, s) == 2
+    assert lib.osm_softmax_rows(FAKE, FAKE, 2, 4, 3, 4, None, None, s) == 2     # ld_x < cols
+    assert lib.osm_softmax_rows(FAKE, FAKE, 2, 4, 4, 3, None, None, s) == 2
+    assert lib.osm_softmax_rows(None, FAKE, 2, 4, 4, 4, None, None, s) == 1
+    assert lib.osm_softmax_rows(FAKE, None, 2, 4, 4, 4, None, None, s) == 1
+    assert lib.osm_softmax_rows(None, None, 0, 4, 4, 4, None, None, s) == 0     # nothing to do
+
+
+@no_gpu_only
+def test_attn_fwd_validation(lib):
+    def call(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dtype=osm.OSM_BF16, B=1, Hq=2, Hkv=1, Nq=8, Nk=8,
+             d=128, scale=0.1, causal=0):
+        return lib.osm_attn_fwd(q, k, v, o, None, dtype, B, Hq, Hkv, Nq, Nk, d, None, None,
+                                scale, causal, None)
+    assert call(B=0) == 2
+    assert call(Hq=3, Hkv=2) == 2
+    assert call(Nq=-1) == 2
+    assert call(scale=0.0) == 2
+    assert call(scale=float("inf")) == 2
+    assert call(scale=float("nan")) == 2
+    assert call(causal=2) == 2
+    assert call(dtype=osm.OSM_F32) == 3
+    assert call(d=64) == 3
+    assert call(q=None) == 1
+    assert call(o=None) == 1
+    assert call(k=None) == 1
+    assert call(k=None, v=None, Nk=0) != 1          # no keys: k/v may be NULL
+    assert call(q=None, Nq=0) == 0                  # nothing to compute
+
+
+@no_gpu_only
+def test_decode_validation(lib):
+    ws_ok = osm.decode_workspace_bytes(2, 8, 1000, 128, 256)
+
+    def call(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, dtype=osm.OSM_BF16, B=2, Hq=8, Hkv=2, L=1000,
+             d=128, sk=FAKE, scale=0.1, split=256, ws=FAKE, wsb=ws_ok):
+        return lib.osm_attn_decode_splitkv(q, kc, vc, o, None, dtype, B, Hq, Hkv, L, d, sk, scale,
+                                           split, ws, wsb, None)
+    assert call(B=0) == 2
+    assert call(Hq=6, Hkv=4) == 2
+    assert call(split=0) == 2
+    assert call(scale=-1.0) == 2
+    assert call(d=96) == 3
+    assert call(Hq=6, Hkv=2) == 3                   # group of 3
+    assert call(split=100) == 3                     # not a multiple of 64
+    assert call(split=8192 + 64) == 3
+    assert call(Hq=16, Hkv=2, split=4096) == 3      # 8 * 4096 scores exceed the LDS budget
+    assert call(dtype=7) == 3
+    assert call(sk=None) == 1
+    assert call(q=None) == 1
+    assert call(ws=None) == 4
+    assert call(wsb=ws_ok - 1) == 4
+    assert call(ws=ctypes.c_void_p(0x10010)) == 4   # not 256-byte aligned
+
+
+@no_gpu_only
+def test_merge_validation(lib):
+    def call(pm=FAKE, pl=FAKE, po=FAKE, rows=4, C=3, d=64, o=FAKE, dt=osm.OSM_F32):
+        return lib.osm_merge_partials(pm, pl, po, rows, C, d, o, dt, None, None)
+    assert call(rows=-1) == 2
+    assert call(C=0) == 2
+    assert call(d=0) == 2
+    assert call(d=513) == 3
+    assert call(dt=9) == 3
+    assert call(pm=None) == 1
+    assert call(o=None) == 1
+    assert call(pm=None, rows=0) == 0
+
+
+@no_gpu_only
+def test_no_device_reports_hip_error(lib):
+    """A fully valid request in a process without a GPU fails cleanly with
+    OSM_ERR_HIP (the launch is refused by the runtime, nothing is read)."""
+    rc = lib.osm_merge_partials(FAKE, FAKE, FAKE, 4, 3, 64, FAKE, osm.OSM_F32, None, None)
+    assert rc == 5
+    rc = lib.osm_softmax_rows(FAKE, FAKE, 2, 4, 4, 4, None, None, None)
+    assert rc == 5

@@ -1,0 +1,141 @@
+"""osm_attn_fwd on the GPU against the oracle: element by element on small
+ragged shapes, sampled rows at the full benchmark sizes, and the bit-exact
+mask properties."""
+import numpy as np
+import pytest
+
+import exact_attention_online_softmax_amd as osm
+from exact_attention_online_softmax_amd import inputs
+from gpu_util import announce, check_attn, dev_bf16, dev_i32, host, host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def run(inp):
+    q, k, v = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v)
+    sq = None if inp.seqlens_q is None else dev_i32(inp.seqlens_q)
+    sk = None if inp.seqlens_k is None else dev_i32(inp.seqlens_k)
+    return osm.attn_fwd(q, k, v, scale=inp.scale, causal=inp.causal, seqlens_q=sq, seqlens_k=sk)
+
+
+def oracle(orc, inp, rows=None):
+    q, k, v = inp.widened()
+    return orc.attention(q, k, v, scale=inp.scale, causal=inp.causal, seqlens_q=inp.seqlens_q,
+                         seqlens_k=inp.seqlens_k, rows=rows)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,causal", [
+    (2, 4, 2, 300, 300, False),
+    (2, 4, 2, 300, 300, True),
+    (1, 2, 1, 129, 517, False),
+    (1, 2, 2, 1, 1, False),
+    (1, 1, 1, 1, 64, True),
+    (3, 8, 1, 64, 200, False),
+    (1, 2, 2, 640, 640, True),
+])
+def test_small(orc, B, Hq, Hkv, Nq, Nk, causal):
+    announce(f"fwd B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} causal={causal}")
+    inp = inputs.attention_inputs(B, Hq, Hkv, Nq, Nk, 128, seed=B * 1000 + Nq + Nk, causal=causal)
+    o, lse = run(inp)
+    o_ref, lse_ref = oracle(orc, inp)
+    check_attn(host(o), host(lse), o_ref, lse_ref, "bf16")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_poisoned(orc, causal):
+    announce(f"fwd varlen poisoned causal={causal}")
+    B, H, N = 4, 2, 400
+    lens = np.array([1, 130, 257, 400], np.int32)
+    inp = inputs.attention_inputs(B, H, H, N, N, 128, seed=31, causal=causal, seqlens_q=lens,
+                                  seqlens_k=lens, poison=True)
+    o, lse = run(inp)
+    o_ref, lse_ref = oracle(orc, inp)
+    oh, lh = host(o), host(lse)
+    check_attn(oh, lh, o_ref, lse_ref, "bf16")
+    for b, L in enumerate(lens):       # padded query rows: exactly 0 / -inf
+        assert np.all(oh[b, :, L:] == 0.0) and np.all(np.isneginf(lh[b, :, L:]))
+    # zero padding instead of NaN: bit-identical outputs
+    zq, zk, zv = (inputs.bf16_bits_to_f32(a).copy() for a in (inp.q, inp.k, inp.v))
+    for a in (zq, zk, zv):
+        a[np.isnan(a)] = 0.0
+    inp0 = inputs.AttnInputs(inputs.to_bf16_bits(zq), inputs.to_bf16_bits(zk), inputs.to_bf16_bits(zv),
+                             "bf16", lens, lens, inp.scale, causal)
+    o0, l0 = run(inp0)
+    assert np.array_equal(host_bits(o), host_bits(o0))
+    assert np.array_equal(host_bits(lse), host_bits(l0))
+
+
+def test_seqlens_q_null_keys_padded(orc):
+    """Only keys padded (seqlens_q NULL): every query row attends to the
+    valid keys; Lk = 0 gives 0 / -inf."""
+    announce("fwd key padding only, Lk=0 batch")
+    lens = np.array([0, 77, 300], np.int32)
+    inp = inputs.attention_inputs(3, 2, 2, 150, 300, 128, seed=41, seqlens_k=lens, poison=True)
+    o, lse = run(inp)
+    o_ref, lse_ref = oracle(orc, inp)
+    check_attn(host(o), host(lse), o_ref, lse_ref, "bf16")
+
+
+def test_causal_future_keys_do_not_matter(orc):
+    announce("fwd causal future-key perturbation")
+    inp = inputs.attention_inputs(1, 2, 2, 512, 512, 128, seed=51, causal=True)
+    o1, l1 = run(inp)
+    k2, v2 = inp.k.copy(), inp.v.copy()
+    k2[:, :, 200:] = inputs.to_bf16_bits(np.full(k2[:, :, 200:].shape, 3.0, np.float32))
+    v2[:, :, 200:] = inputs.to_bf16_bits(np.full(v2[:, :, 200:].shape, -5.0, np.float32))
+    inp2 = inputs.AttnInputs(inp.q, k2, v2, "bf16", None, None, inp.scale, True)
+    o2, l2 = run(inp2)
+    b1, b2 = host_bits(o1), host_bits(o2)
+    assert np.array_equal(b1[:, :, :200], b2[:, :, :200])
+    assert np.array_equal(host_bits(l1)[:, :, :200], host_bits(l2)[:, :, :200])
+    assert not np.array_equal(b1[:, :, 200:], b2[:, :, 200:])
+
+
+def _sample_rows(rng, B, H, N, n, lens=None):
+    rows = []
+    for _ in range(n):
+        b = int(rng.integers(0, B))
+        h = int(rng.integers(0, H))
+        top = N if lens is None else int(lens[b])
+        i = int(rng.integers(0, top))
+        rows.append((b * H + h) * N + i)
+    # the first and last rows of a few heads and tiles
+    for b in range(min(B, 2)):
+        top = N if lens is None else int(lens[b])
+        for i in (0, 63, 64, 127, 128, top - 1):
+            if 0 <= i < top:
+                rows.append((b * H) * N + i)
+    return np.array(sorted(set(rows)), np.int64)
+
+
+def test_config3_full_sampled(orc):
+    """B4 H32 N4096 d128 non-causal at full size: 600 sampled query rows
+    compared with the oracle one by one."""
+    announce("fwd config3 full size, sampled rows")
+    inp = inputs.config3()
+    o, lse = run(inp)
+    rows = _sample_rows(np.random.default_rng(3), 4, 32, 4096, 600)
+    o_ref, lse_ref = oracle(orc, inp, rows=rows)
+    oh = host(o).reshape(-1, 128)[rows]
+    lh = host(lse).reshape(-1)[rows]
+    check_attn(oh, lh, o_ref, lse_ref, "bf16")
+    assert np.isfinite(host(lse)).all()
+
+
+def test_config4_full_sampled(orc):
+    """B8 H16 N8192 causal with key padding, NaN-poisoned padding, at full
+    size: sampled rows vs the oracle, every padded row exactly 0 / -inf,
+    no NaN anywhere."""
+    announce("fwd config4 full size, sampled rows")
+    inp = inputs.config4()
+    o, lse = run(inp)
+    lens = inp.seqlens_q
+    rows = _sample_rows(np.random.default_rng(4), 8, 16, 8192, 400, lens)
+    o_ref, lse_ref = oracle(orc, inp, rows=rows)
+    oh_all = host(o)
+    lh_all = host(lse)
+    check_attn(oh_all.reshape(-1, 128)[rows], lh_all.reshape(-1)[rows], o_ref, lse_ref, "bf16")
+    assert not np.isnan(oh_all).any()
+    for b, L in enumerate(lens):
+        assert np.all(oh_all[b, :, L:] == 0.0) and np.all(np.isneginf(lh_all[b, :, L:]))
+        assert np.all(np.isfinite(lh_all[b, :, :L]))
