@@ -23,9 +23,16 @@ FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+# per-file extra flags.  The attention kernel never lets a NaN reach its
+# arithmetic (padding is zero-filled, masked scores are -inf), so it runs with
+# the IEEE mode bit off: max/min then need no NaN-quieting of their inputs.
+EXTRA = {"attn_fwd.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = ["hipcc", "-x", "hip", *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ["hipcc", "-x", "hip", *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

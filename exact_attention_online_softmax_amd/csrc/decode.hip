@@ -10,18 +10,21 @@
 // as identity.  [P3] "The same merge, in log-sum-exp form" names the split
 // of one query's keys over many thread blocks.
 //
-// decode_split: one workgroup per (piece, kv head, batch).  All query heads
-// that share the kv head (grouped-query attention) are served from one read
-// of the piece's K and V.  Lanes are grouped LPK = head_dim / 8 per key, each
-// lane owning 8 consecutive dims, so every wave load is a contiguous run of
-// whole cache rows.  Phase 1 computes the piece's scores into LDS; the
-// piece maximum and sum follow; phase 2 accumulates sum p_j v_j.
+// decode_split: one workgroup (8 waves) per (piece, kv head, batch).  All
+// query heads that share the kv head (grouped-query attention) are served
+// from one read of the piece's K and V.  Lanes are grouped LPK = head_dim/8
+// per key, each lane owning 8 consecutive dims, so every wave load is a
+// contiguous run of whole cache rows; the loads of up to 256 keys of K and V
+// are issued together before any is used.  Phase 1 computes the piece's
+// scores (bf16 dot products with v_dot2_f32_bf16, 16-lane sums with DPP row
+// shifts) into LDS; the piece maximum and sum follow; phase 2 accumulates
+// sum p_j v_j in fp32.
 // Pieces wholly past the valid length write the identity (m = -inf, l = 0).
 //
-// merge_partials: one workgroup per row; pieces are merged in groups of up
-// to blockDim with the running-maximum rescale between groups, empty pieces
-// skipped (their l and O~ are never read).  Then o = O~ / l once and
-// LSE = m + log l ([P3] "From weights to outputs").
+// merge_partials: one workgroup per row; the row's largest piece maximum is
+// the common reference, every piece is weighted by exp(m_c - m) and added,
+// empty pieces skipped (their l and O~ are never read).  Then o = O~ / l
+// once and LSE = m + log l ([P3] "From weights to outputs").
 #include "osm_device.h"
 #include "osm_internal.h"
 
@@ -29,28 +32,66 @@ namespace osm {
 
 namespace {
 
-constexpr int DEC_THREADS = 256;
+constexpr int DEC_THREADS = 512;
 constexpr int DEC_WAVES = DEC_THREADS / 64;
+constexpr int DEC_ROUND = 256;      // keys whose loads are issued together
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-// 8 consecutive elements of a row as fp32
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Eight consecutive elements of a cache or query row, kept as loaded.
 template <typename T> struct Row8;
+template <> struct Row8<uint16_t> {        // bf16: four packed pairs
+    uint4 w;
+    __device__ __forceinline__ void load(const uint16_t *p) { w = *reinterpret_cast<const uint4 *>(p); }
+    // sum_e q_e x_e with q, x both bf16 rows (v_dot2_f32_bf16, fp32 accumulate)
+    __device__ __forceinline__ float dot(const Row8 &q) const {
+        float a = 0.0f;
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w.x), __builtin_bit_cast(bf16x2_t, w.x), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w.y), __builtin_bit_cast(bf16x2_t, w.y), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w.z), __builtin_bit_cast(bf16x2_t, w.z), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w.w), __builtin_bit_cast(bf16x2_t, w.w), a, false);
+        return a;
+    }
+    __device__ __forceinline__ void axpy(float p, float (&acc)[8]) const {
+        acc[0] = fmaf(p, bf16_lo(w.x), acc[0]); acc[1] = fmaf(p, bf16_hi(w.x), acc[1]);
+        acc[2] = fmaf(p, bf16_lo(w.y), acc[2]); acc[3] = fmaf(p, bf16_hi(w.y), acc[3]);
+        acc[4] = fmaf(p, bf16_lo(w.z), acc[4]); acc[5] = fmaf(p, bf16_hi(w.z), acc[5]);
+        acc[6] = fmaf(p, bf16_lo(w.w), acc[6]); acc[7] = fmaf(p, bf16_hi(w.w), acc[7]);
+    }
+};
 template <> struct Row8<float> {
-    static __device__ __forceinline__ void load(const float *p, float (&v)[8]) {
-        const float4 a = *reinterpret_cast<const float4 *>(p);
-        const float4 b = *reinterpret_cast<const float4 *>(p + 4);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    float4 a, b;
+    __device__ __forceinline__ void load(const float *p) {
+        a = *reinterpret_cast<const float4 *>(p);
+        b = *reinterpret_cast<const float4 *>(p + 4);
+    }
+    __device__ __forceinline__ float dot(const Row8 &q) const {
+        float r = q.a.x * a.x;
+        r = fmaf(q.a.y, a.y, r); r = fmaf(q.a.z, a.z, r); r = fmaf(q.a.w, a.w, r);
+        r = fmaf(q.b.x, b.x, r); r = fmaf(q.b.y, b.y, r); r = fmaf(q.b.z, b.z, r);
+        return fmaf(q.b.w, b.w, r);
+    }
+    __device__ __forceinline__ void axpy(float p, float (&acc)[8]) const {
+        acc[0] = fmaf(p, a.x, acc[0]); acc[1] = fmaf(p, a.y, acc[1]);
+        acc[2] = fmaf(p, a.z, acc[2]); acc[3] = fmaf(p, a.w, acc[3]);
+        acc[4] = fmaf(p, b.x, acc[4]); acc[5] = fmaf(p, b.y, acc[5]);
+        acc[6] = fmaf(p, b.z, acc[6]); acc[7] = fmaf(p, b.w, acc[7]);
     }
 };
-template <> struct Row8<uint16_t> {
-    static __device__ __forceinline__ void load(const uint16_t *p, float (&v)[8]) {
-        const uint4 a = *reinterpret_cast<const uint4 *>(p);
-        v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
-        v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
-    }
-};
+
+// Sum over each group of LPK consecutive lanes (LPK = 8 or 16) with DPP
+// row shifts; the total lands in the group's last lane.
+template <int LPK>
+__device__ __forceinline__ float group_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, true));
+    if (LPK == 16)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, true));
+    return x;
+}
 
 template <typename T, int HD, int G>
 __global__ void __launch_bounds__(DEC_THREADS)
@@ -61,15 +102,16 @@ decode_split(const T *__restrict__ Q, const T *__restrict__ K, const T *__restri
     constexpr int LPK = HD / 8;                 // lanes per key
     constexpr int KPW = 64 / LPK;               // keys per wave step
     constexpr int KPB = KPW * DEC_WAVES;        // keys per workgroup step
-    constexpr int U = 4;                        // key steps in flight per lane
+    constexpr int R = DEC_ROUND / KPB;          // steps per round
     extern __shared__ float sc[];               // scores, then weights: [G][split]
     __shared__ float red_o[DEC_WAVES][G][HD];   // cross-wave partial outputs
     __shared__ float stat_m[G], stat_l[G];
 
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int L = clampi(seqlens_k[b], 0, Lmax);
+    const int L = __builtin_amdgcn_readfirstlane(clampi(seqlens_k[b], 0, Lmax));
     const int start = c * split;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const size_t row0 = (size_t)(b * Hq + g * G);   // first query row of this group
 
     if (start >= L) {          // empty piece: the identity
@@ -82,43 +124,37 @@ decode_split(const T *__restrict__ Q, const T *__restrict__ K, const T *__restri
     const int n = min(split, L - start);
     const int kslot = lane / LPK;               // key slot within the wave step
     const int d0 = (lane % LPK) * 8;            // this lane's 8 dims
+    const int kbase = wave * KPW + kslot;       // key of step 0 (round-relative)
 
-    // the G query vectors, this lane's 8 dims
-    float q[G][8];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) Row8<T>::load(Q + (row0 + hh) * HD + d0, q[hh]);
+    const T *Kp = K + ((size_t)(b * Hkv + g) * Lmax + start) * HD + d0;
+    const T *Vp = V + ((size_t)(b * Hkv + g) * Lmax + start) * HD + d0;
 
-    const T *Kp = K + ((size_t)(b * Hkv + g) * Lmax + start) * HD;
-    const T *Vp = V + ((size_t)(b * Hkv + g) * Lmax + start) * HD;
+    Row8<T> q[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) q[hh].load(Q + (row0 + hh) * HD + d0);
 
-    // ---- phase 1: scores (base-2 scaled units) --------------------------
-    // U key steps per iteration: all loads are issued before any use.
-    for (int k0 = 0; k0 < n; k0 += KPB * U) {
-        float kv[U][8];
+    // Every load of a round is issued before any is used.  Keys past n are
+    // clamped to the last valid key (in bounds, finite) and never used.
+    Row8<T> kr[R], vr[R];
+    const bool one_round = (n <= DEC_ROUND);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int kk = k0 + u * KPB + wave * KPW + kslot;
-            if (kk < n) Row8<T>::load(Kp + (size_t)kk * HD + d0, kv[u]);
-            else
+    for (int u = 0; u < R; ++u) kr[u].load(Kp + (size_t)min(kbase + u * KPB, n - 1) * HD);
+    if (one_round)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) kv[u][e] = 0.0f;
-        }
+        for (int u = 0; u < R; ++u) vr[u].load(Vp + (size_t)min(kbase + u * KPB, n - 1) * HD);
+
+    // ---- phase 1: scores (base-2 scaled units) into LDS ------------------
+    for (int r0 = 0; r0 < n; r0 += DEC_ROUND) {
+        if (r0 > 0)
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int kk = k0 + u * KPB + wave * KPW + kslot;
+            for (int u = 0; u < R; ++u) kr[u].load(Kp + (size_t)min(r0 + kbase + u * KPB, n - 1) * HD);
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const int kk = r0 + kbase + u * KPB;
             float dot[G];
 #pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
-                float acc = 0.0f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc = fmaf(q[hh][e], kv[u][e], acc);
-                dot[hh] = acc;
-            }
-#pragma unroll
-            for (int off = LPK / 2; off >= 1; off >>= 1)
-#pragma unroll
-                for (int hh = 0; hh < G; ++hh) dot[hh] += __shfl_xor(dot[hh], off, 64);
-            if ((lane % LPK) == 0 && kk < n)
+            for (int hh = 0; hh < G; ++hh) dot[hh] = group_sum<LPK>(kr[u].dot(q[hh]));
+            if ((lane % LPK) == LPK - 1 && kk < n)
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh) sc[hh * split + kk] = dot[hh] * scale_log2;
         }
@@ -152,26 +188,16 @@ decode_split(const T *__restrict__ Q, const T *__restrict__ K, const T *__restri
     for (int hh = 0; hh < G; ++hh)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[hh][e] = 0.0f;
-    for (int k0 = 0; k0 < n; k0 += KPB * U) {
-        float vv[U][8];
+    for (int r0 = 0; r0 < n; r0 += DEC_ROUND) {
+        if (!one_round)
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int kk = k0 + u * KPB + wave * KPW + kslot;
-            if (kk < n) Row8<T>::load(Vp + (size_t)kk * HD + d0, vv[u]);
-            else
+            for (int u = 0; u < R; ++u) vr[u].load(Vp + (size_t)min(r0 + kbase + u * KPB, n - 1) * HD);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) vv[u][e] = 0.0f;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int kk = k0 + u * KPB + wave * KPW + kslot;
+        for (int u = 0; u < R; ++u) {
+            const int kk = r0 + kbase + u * KPB;
             if (kk < n) {
 #pragma unroll
-                for (int hh = 0; hh < G; ++hh) {
-                    const float p = sc[hh * split + kk];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(p, vv[u][e], acc[hh][e]);
-                }
+                for (int hh = 0; hh < G; ++hh) vr[u].axpy(sc[hh * split + kk], acc[hh]);
             }
         }
     }
@@ -202,60 +228,89 @@ decode_split(const T *__restrict__ Q, const T *__restrict__ K, const T *__restri
 }
 
 // ---- merge ----------------------------------------------------------------
-__global__ void __launch_bounds__(512)
+// One workgroup (4 waves) per row.  The row maximum m over the pieces is
+// found first, so every piece's weight exp(m_c - m) is final and the pieces
+// can be accumulated in any order with no rescaling; waves take pieces
+// c = wave, wave + 4, ..., lanes own NDL dims each, and the four partial sums
+// are added through LDS.  Empty pieces (m_c = -inf) are skipped without
+// reading their l or O~.
+constexpr int MRG_THREADS = 256;
+constexpr int MRG_WAVES = MRG_THREADS / 64;
+
+template <int NDL>
+__global__ void __launch_bounds__(MRG_THREADS)
 merge_partials_kernel(const float *__restrict__ pm, const float *__restrict__ pl,
                       const float *__restrict__ po, int64_t rows, int C, int HD,
                       void *__restrict__ out, int out_bf16, float *__restrict__ lse) {
-    __shared__ float w_s[512];
-    __shared__ float red[16];
-    const int tid = threadIdx.x, nt = blockDim.x;
-    const int lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
+    __shared__ float red_acc[MRG_WAVES][NDL * 64];
+    __shared__ float red_s[MRG_WAVES];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-        float m = kNegInf, l = 0.0f, acc = 0.0f;
-        for (int c0 = 0; c0 < C; c0 += nt) {
-            const int cn = min(nt, C - c0);
-            // group maximum
-            const float mc = (tid < cn) ? pm[r * C + c0 + tid] : kNegInf;
-            float mx = mc;
+        const float *pmr = pm + r * C;
+        // row maximum
+        float mx = kNegInf;
+        for (int c = tid; c < C; c += MRG_THREADS) mx = fmaxf(mx, pmr[c]);
 #pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-            if (lane == 0) red[wave] = mx;
-            __syncthreads();
-            mx = kNegInf;
-            for (int w = 0; w < nw; ++w) mx = fmaxf(mx, red[w]);
-            __syncthreads();
-            const float mn = fmaxf(m, mx);
-            if (mn == kNegInf) continue;                      // only empty pieces so far
-            // weights of this group's pieces against the new reference
-            const float wc = (mc == kNegInf) ? 0.0f : exp_acc(mc - mn);
-            w_s[tid] = wc;
-            float lw = (wc != 0.0f) ? wc * pl[r * C + c0 + tid] : 0.0f;
+        for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        if (lane == 0) red_s[wave] = mx;
+        __syncthreads();
+        mx = kNegInf;
 #pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) lw += __shfl_xor(lw, off, 64);
-            if (lane == 0) red[wave] = lw;
-            __syncthreads();
-            float lsum = 0.0f;
-            for (int w = 0; w < nw; ++w) lsum += red[w];
-            const float alpha = (m == kNegInf) ? 0.0f : exp_acc(m - mn);
-            l = fmaf(l, alpha, lsum);
-            if (tid < HD) {
-                float a = acc * alpha;
-                for (int j = 0; j < cn; ++j) {
-                    const float wj = w_s[j];
-                    if (wj != 0.0f) a = fmaf(wj, po[(r * C + c0 + j) * HD + tid], a);
+        for (int w = 0; w < MRG_WAVES; ++w) mx = fmaxf(mx, red_s[w]);
+        __syncthreads();
+        const float m = mx;
+        float acc[NDL];
+#pragma unroll
+        for (int k = 0; k < NDL; ++k) acc[k] = 0.0f;
+        float lsum = 0.0f;
+        if (m != kNegInf) {
+            constexpr int U = 4;
+            for (int c0 = wave; c0 < C; c0 += MRG_WAVES * U) {
+                float w[U], lv[U], ov[U][NDL];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + u * MRG_WAVES;
+                    const float mc = (c < C) ? pmr[c] : kNegInf;
+                    w[u] = (mc == kNegInf) ? 0.0f : exp_acc(mc - m);
+                    lv[u] = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < NDL; ++k) ov[u][k] = 0.0f;
+                    if (w[u] != 0.0f) {
+                        lv[u] = pl[r * C + c];
+                        const float *oc = po + (r * C + c) * HD;
+#pragma unroll
+                        for (int k = 0; k < NDL; ++k)
+                            if (lane + 64 * k < HD) ov[u][k] = oc[lane + 64 * k];
+                    }
                 }
-                acc = a;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    lsum = fmaf(w[u], lv[u], lsum);
+#pragma unroll
+                    for (int k = 0; k < NDL; ++k) acc[k] = fmaf(w[u], ov[u][k], acc[k]);
+                }
             }
-            m = mn;
-            __syncthreads();
         }
+#pragma unroll
+        for (int k = 0; k < NDL; ++k) red_acc[wave][lane + 64 * k] = acc[k];
+        if (lane == 0) red_s[wave] = lsum;
+        __syncthreads();
+        float l = 0.0f;
+#pragma unroll
+        for (int w = 0; w < MRG_WAVES; ++w) l += red_s[w];
         const bool valid = (m != kNegInf) && (l > 0.0f);
-        if (tid < HD) {
-            const float o = valid ? acc / l : 0.0f;
-            if (out_bf16) static_cast<uint16_t *>(out)[r * HD + tid] = f32_to_bf16(o);
-            else static_cast<float *>(out)[r * HD + tid] = o;
+        const float inv = valid ? 1.0f / l : 0.0f;
+        for (int d = tid; d < HD; d += MRG_THREADS) {
+            float o = 0.0f;
+#pragma unroll
+            for (int w = 0; w < MRG_WAVES; ++w) o += red_acc[w][d];
+            o *= inv;
+            if (out_bf16) static_cast<uint16_t *>(out)[r * HD + d] = f32_to_bf16(o);
+            else static_cast<float *>(out)[r * HD + d] = o;
         }
         if (lse && tid == 0) lse[r] = valid ? m + logf(l) : kNegInf;
+        __syncthreads();   // red_acc / red_s are reused by the next row
     }
 }
 
@@ -310,11 +365,17 @@ hipError_t launch_decode_split(const DecodeArgs &a, const DecodeLayout &lay, hip
 
 hipError_t launch_merge_partials(const MergeArgs &a, hipStream_t s) {
     if (a.rows == 0) return hipSuccess;
-    int threads = ((a.head_dim + 63) / 64) * 64;
-    if (threads < 128) threads = 128;
     const int grid = (int)(a.rows < 1048576 ? a.rows : 1048576);
-    hipLaunchKernelGGL(merge_partials_kernel, dim3(grid), dim3(threads), 0, s, a.part_m, a.part_l,
-                       a.part_o, a.rows, a.num_splits, a.head_dim, a.o, a.out_dtype, a.lse);
+    const int ndl = (a.head_dim + 63) / 64;
+#define OSM_MERGE_LAUNCH(N)                                                                     \
+    hipLaunchKernelGGL(merge_partials_kernel<N>, dim3(grid), dim3(MRG_THREADS), 0, s, a.part_m, \
+                       a.part_l, a.part_o, a.rows, a.num_splits, a.head_dim, a.o, a.out_dtype,  \
+                       a.lse)
+    if (ndl <= 1) OSM_MERGE_LAUNCH(1);
+    else if (ndl <= 2) OSM_MERGE_LAUNCH(2);
+    else if (ndl <= 4) OSM_MERGE_LAUNCH(4);
+    else OSM_MERGE_LAUNCH(8);
+#undef OSM_MERGE_LAUNCH
     return hipGetLastError();
 }
 
