@@ -107,11 +107,12 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     int head, qrev;
     if (xcd_heads) {
         // hardware places block L on XCD L % 8; give every XCD whole heads
-        // (head % 8 == XCD) and walk its heads' blocks heaviest-first.
+        // (head % 8 == XCD) and run one head's query blocks back to back
+        // (heaviest first), so the blocks resident on an XCD share a few
+        // heads' K and V in its L2.
         const int xcd = L & 7, slot = L >> 3;
-        const int nh = xcd_heads;           // heads per XCD
-        qrev = slot / nh;
-        head = (slot % nh) * 8 + xcd;
+        qrev = slot % nqb;
+        head = (slot / nqb) * 8 + xcd;
     } else {
         head = L / nqb;
         qrev = L % nqb;
