@@ -44,18 +44,36 @@ def bf16_dev(bits, torch):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
 
 
-def traffic_from_profile(path):
-    """HBM bytes per launch recorded with the last rocprofv3 counter runs of
-    the headline forward, or None when absent or stale."""
+KERNEL_SOURCES = {"fwd": "attn_fwd.hip", "fwd_causal": "attn_fwd.hip", "softmax": "softmax_rows.hip",
+                  "decode": "decode.hip"}
+
+
+def source_hash(name):
+    """sha256 (first 16 hex digits) of the kernel source a workload runs."""
+    import hashlib
+    path = os.path.join(ROOT, "exact_attention_online_softmax_amd", "csrc", KERNEL_SOURCES[name])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(path, name):
+    """HBM bytes per launch recorded by the rocprofv3 counter runs summarized
+    in `path`, or None when absent or taken on a different kernel source."""
+    vals = {}
     try:
         with open(path) as f:
             for line in f:
-                if line.startswith("traffic_bytes_per_launch:"):
-                    v = line.split(":", 1)[1].strip()
-                    return None if v in ("", "null", "stale") else float(v)
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    vals[k.strip()] = v.strip()
     except OSError:
         return None
-    return None
+    if vals.get("kernel_source_sha256_16") != source_hash(name):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(inp, seconds):
@@ -81,6 +99,83 @@ def cpu_baseline(inp, seconds):
                       f"non-causal forward, fp64, {dt:.1f} s"}
 
 
+def summarize(name, trace_dir, out):
+    """Summary of rocprofv3 output for one workload's kernel: average kernel
+    duration (--kernel-trace --stats), FETCH_SIZE / WRITE_SIZE per dispatch
+    (--pmc runs) scaled by the same counters read on a plain copy of known
+    size (the torch copy kernel run with --copy-calibration)."""
+    import csv
+    import glob
+    kern = {"fwd": "attn_fwd", "fwd_causal": "attn_fwd", "softmax": "softmax_rows",
+            "decode": "decode_split"}[name]
+    lines = [f"# rocprofv3 summary: {name}", ""]
+    trace = os.path.join(trace_dir, "trace", "run_kernel_trace.csv")
+    avg_ns = None
+    if os.path.exists(trace):
+        # per (kernel, grid size): the attention kernel runs with different
+        # grids for the non-causal and the causal workload
+        groups = {}
+        for r in csv.DictReader(open(trace)):
+            short = r["Kernel_Name"].replace("osm::(anonymous namespace)::", "").replace("void ", "")
+            short = short.split("(")[0]
+            key = (short, int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])))
+            groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        lines += ["## kernel trace (--kernel-trace --stats): per kernel and grid", "",
+                  "| kernel | workgroups | calls | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+        for (short, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            lines.append(f"| {short} | {wg} | {len(d)} | {sum(d) / len(d) / 1e3:.1f} | "
+                         f"{min(d) / 1e3:.1f} | {max(d) / 1e3:.1f} |")
+        want = {"fwd": ("attn_fwd", 2048), "fwd_causal": ("attn_fwd", 4096),
+                "softmax": ("softmax_rows", None), "decode": ("decode_split", None)}[name]
+        for (short, wg), d in groups.items():
+            if want[0] in short and (want[1] is None or wg == want[1]):
+                avg_ns = sum(d) / len(d)
+        lines.append("")
+    counters = {}
+    for f in sorted(glob.glob(os.path.join(trace_dir, "pmc_*", "run_counter_collection.csv"))):
+        per = {}
+        for r in csv.DictReader(open(f)):
+            # the calibration copy is torch's device-to-device copy_, which
+            # runs the HIP runtime's buffer-copy kernel
+            key = ("copy" if "copyBuffer" in r["Kernel_Name"]
+                   else ("kernel" if kern in r["Kernel_Name"] else None))
+            if key is None:
+                continue
+            per.setdefault((key, r["Counter_Name"]), {}).setdefault(r["Dispatch_Id"], 0.0)
+            per[(key, r["Counter_Name"])][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        for k, d in per.items():
+            # the calibration copy is the largest buffer copy of the run
+            # (small ones upload lengths); the kernel is averaged
+            counters[k] = max(d.values()) if k[0] == "copy" else sum(d.values()) / len(d)
+    cal = None
+    if counters:
+        lines += ["## counters per dispatch (--pmc), KiB", "", "| kernel | counter | KiB |", "|---|---|---|"]
+        for (k, c), v in sorted(counters.items()):
+            lines.append(f"| {k} | {c} | {v:.0f} |")
+        lines.append("")
+    copy_bytes = None
+    for f in glob.glob(os.path.join(trace_dir, "copy_bytes.txt")):
+        copy_bytes = float(open(f).read().strip())
+    traffic = None
+    if copy_bytes and ("copy", "FETCH_SIZE") in counters and ("kernel", "FETCH_SIZE") in counters:
+        f_scale = copy_bytes / (counters[("copy", "FETCH_SIZE")] * 1024)
+        w_scale = copy_bytes / (counters[("copy", "WRITE_SIZE")] * 1024) if ("copy", "WRITE_SIZE") in counters else f_scale
+        traffic = (counters[("kernel", "FETCH_SIZE")] * 1024 * f_scale
+                   + counters.get(("kernel", "WRITE_SIZE"), 0.0) * 1024 * w_scale)
+        lines += [f"copy calibration: {copy_bytes:.0f} bytes read and written by the copy; "
+                  f"FETCH_SIZE scale {f_scale:.4f}, WRITE_SIZE scale {w_scale:.4f}", ""]
+    lines += [f"kernel_source_sha256_16: {source_hash(name)}",
+              f"avg_kernel_us: {avg_ns / 1e3:.2f}" if avg_ns else "avg_kernel_us: null",
+              f"traffic_bytes_per_launch: {traffic:.0f}" if traffic else "traffic_bytes_per_launch: null", ""]
+    cmdf = os.path.join(trace_dir, "commands.txt")
+    if os.path.exists(cmdf):
+        lines += ["## commands", "", "```", open(cmdf).read().strip(), "```", ""]
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -90,7 +185,15 @@ def main():
                     help="run one operation only (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB per step (scales rocprof "
+                         "FETCH_SIZE/WRITE_SIZE to bytes)")
+    ap.add_argument("--summarize", nargs=3, metavar=("NAME", "TRACE_DIR", "OUT"), default=None,
+                    help="write a profile summary from rocprofv3 CSV output: NAME is a workload "
+                         "name, TRACE_DIR holds run_kernel_stats.csv and pmc_*/ counter dirs")
     args = ap.parse_args()
+    if args.summarize:
+        return summarize(*args.summarize)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by batch/head with no exchange; see DESIGN.md)", file=sys.stderr)
@@ -158,6 +261,14 @@ def main():
         work["decode"] = ("hbm", kv + io + partials, "B16 Hq32 Hkv8 d128, L_b U[4096,32768], split 256")
         del inp5
 
+    if args.copy_calibration:
+        n = args.copy_calibration * 1024 * 1024 // 4
+        csrc = torch.ones(n, dtype=torch.float32, device="cuda")
+        cdst = torch.empty_like(csrc)
+        names.append("copy")
+        calls["copy"] = lambda: cdst.copy_(csrc)
+        work["copy"] = ("hbm", 8.0 * n, f"device copy {args.copy_calibration} MiB")
+
     # ---- warmup, then K timed steps --------------------------------------
     for _ in range(args.warmup):
         for n in names:
@@ -193,7 +304,7 @@ def main():
     hc = comps[head]
     roofline = {"bound": hc["bound"], "achieved": hc["achieved"], "peak": hc["peak"],
                 "unit": hc["unit"], "frac": hc["frac"],
-                "traffic": traffic_from_profile(PROFILE_FWD) if head == "fwd" else None}
+                "traffic": traffic_from_profile(PROFILE_FWD, "fwd") if head == "fwd" else None}
     out = {"metric": METRIC, "value": hc["achieved"], "unit": hc["unit"], "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
