@@ -24,9 +24,12 @@ FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-
 
 
 # per-file extra flags.  The attention kernel never lets a NaN reach its
-# arithmetic (padding is zero-filled, masked scores are -inf), so it runs with
-# the IEEE mode bit off: max/min then need no NaN-quieting of their inputs.
-EXTRA = {"attn_fwd.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+# arithmetic (padding rows are never loaded, masked scores are -inf), so it
+# runs with the IEEE mode bit off: max/min then need no NaN-quieting of their
+# inputs.  Its score MFMAs must write VGPRs (the softmax reads them), so the
+# compiler is told to select the VGPR form of the MFMA builtins; the output
+# accumulators stay in AGPRs through inline assembly.
+EXTRA = {"attn_fwd.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 def _compile(src: str) -> str:

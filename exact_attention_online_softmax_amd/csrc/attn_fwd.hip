@@ -12,31 +12,33 @@
 // scaled units, log2(e) folded into the scale (same section).
 //
 // Mapping to CDNA4:
-//  * workgroup = 8 wavefronts = 256 queries (two waves per SIMD, one
-//    workgroup per CU); each wave owns 32 queries.  A K/V tile loaded into
-//    LDS serves all 256 queries.
+//  * workgroup = 4 wavefronts = 256 queries, one wavefront per SIMD and one
+//    workgroup per CU; each wave owns 64 queries as two 32-query blocks, so
+//    every K or V operand read from LDS feeds two MFMAs (half the LDS traffic
+//    per flop of a 32-query wave).  With one wave per SIMD each wave has 512
+//    registers: the output accumulators live in the AGPRs.
 //  * both products run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
-//    The score tile is computed transposed, S^T = K Q^T, so lane l of a wave
-//    holds the scores of ONE query (l % 32) against 32 of the 64 keys of the
-//    tile; its partner lane l ^ 32 holds the other 32.  Row max and row sum
-//    are therefore in-lane plus one cross-half exchange.
-//  * the output is accumulated transposed, O~^T = V^T P~^T: P~^T is exactly
-//    the fp32 score accumulator converted in place to bf16 (no data
-//    movement), and lane l holds 64 of the 128 output dims of its query, so
-//    the rescale by exp2(m_old - m_new) is a per-lane multiply.
-//  * K and V tiles (64 keys x 128 dims) go from HBM straight into LDS with
-//    global_load_lds_dwordx4 (no VGPR staging; lane i of a load writes
-//    bytes 16 i .. 16 i + 15 of a 1 KiB LDS block).  Rows are unpadded and
-//    XOR-swizzled at 16-byte granularity (K: slot = chunk ^ (row % 16); V:
-//    slot = chunk ^ 4 (row % 4)) so that the K operand reads and the
-//    transposing V reads are free of bank conflicts.
-//  * ping-pong: the two waves of each SIMD belong to groups A (waves 0-3)
-//    and B (waves 4-7) that run half a tile apart, separated by barriers.
-//    Each wave alternates a softmax phase (vector ALU: masks, maximum,
-//    exponentials, bf16 P~) and an MFMA phase (P~V of this tile, then the
-//    scores of the next tile), so on every SIMD the matrix cores work for one
-//    wave while the other exponentiates.  K and V are double-buffered; each
-//    tile's loads are issued two phases before first use.
+//    The score tile is computed transposed, S^T = K Q^T, so lane l holds the
+//    scores of one query (l % 32) of each block against 16 of the 32 keys of
+//    the tile; lane l ^ 32 holds the other 16.  Row max and row sum are
+//    in-lane plus one cross-half exchange.
+//  * the output is accumulated transposed, O~^T = V^T P~^T: P~^T is the fp32
+//    score accumulator converted in place to bf16, and the rescale by
+//    exp2(m_old - m_new) is a per-lane multiply.
+//  * software pipeline inside each wave: iteration j exponentiates the
+//    scores of tile j and multiplies them into O~ while the matrix cores
+//    already compute the scores of tile j+1; the vector ALU work of one tile
+//    and the MFMAs of the next interleave in one instruction stream.
+//  * K and V tiles (32 keys x 128 dims, 8 KiB each) go from HBM straight
+//    into LDS with global_load_lds_dwordx4 (no VGPR staging; lane i of a load
+//    writes bytes 16 i .. 16 i + 15 of a 1 KiB LDS block) through a ring of
+//    four slots, loaded three tiles ahead.  Each slot is its own LDS object
+//    and the loop is unrolled by four, so every access names its slot
+//    statically: operand reads use immediate offsets, and the compiler can
+//    tell that the loads in flight never alias the slots being read.
+//  * rows are unpadded and XOR-swizzled at 16-byte granularity (K: slot =
+//    chunk ^ (row % 16); V: slot = chunk ^ 4 (row % 4)) so that the K operand
+//    reads and the transposing V reads are free of bank conflicts.
 //  * the V^T operand is read with the gfx950 transposing LDS read
 //    (ds_read_b64_tr_b16): in each 16-lane group, lane i points at
 //    V[k0 + i/4][d0 + 4 (i%4) .. +3] and lane j receives V[k0 + e][d0 + j],
@@ -50,6 +52,9 @@
 //    still go wrong": any reference that keeps the weights bounded works;
 //    the running maximum is the tightest one), so after the first tiles the
 //    rescale is skipped by a wave-uniform branch.
+//  * tiles that need a mask (the causal diagonal, the ragged end) are the
+//    last ones each wave visits; they run in a separate, branchy loop so the
+//    main loop carries no mask code.
 //  * blocks are ordered heaviest-first for causal masks, and each
 //    (batch, head)'s query blocks are kept on one XCD (shared L2 for K/V)
 //    when the head count divides evenly by 8.
@@ -64,19 +69,63 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
-
-constexpr int D = 128;           // head dim
-constexpr int NW = 8;            // wavefronts per workgroup (two per SIMD)
-constexpr int BQ = 32 * NW;      // queries per workgroup
-constexpr int BK = 64;           // keys per tile
-constexpr int NT = 64 * NW;      // threads per workgroup
-constexpr int ROWB = D * 2;      // bytes per K/V row in LDS (unpadded)
-constexpr int TILEB = BK * ROWB; // bytes per K or V tile (16 KiB)
-
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+constexpr int D = 128;            // head dim
+constexpr int NW = 4;             // wavefronts per workgroup (one per SIMD)
+constexpr int QW = 64;            // queries per wavefront (two 32-query blocks)
+constexpr int BQ = QW * NW;       // queries per workgroup
+constexpr int BK = 32;            // keys per tile
+constexpr int NT = 64 * NW;       // threads per workgroup
+constexpr int ROWB = D * 2;       // bytes per K/V row in LDS (unpadded)
+constexpr int TILEB = BK * ROWB;  // bytes per K or V tile (8 KiB)
+constexpr int LPW = TILEB / 1024 / NW;  // 1 KiB loads per wave per K (or V) tile
+constexpr int AHEAD = 3;          // tiles loaded ahead of the one being computed
+
+template <int N> struct Slot { static constexpr int value = N; };
+
+// f(Slot<I>{}) for I = B .. E-1, each with its index as a compile-time constant
+template <int B, int E, typename F> __device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(Slot<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// The 32 exponential items of a tile (n = 0..31: query block (n/8) % 2,
+// element (n%8) + 8 (n/16) of that block's scores) in the order the P~V
+// steps consume them, in groups g = -1 .. kGroups-1: items
+// [item_lo(g), item_lo(g+1)), four in the first group, then one or two.
+constexpr int kGroups = 22;
+constexpr int item_lo(int g) { return g < 0 ? 0 : 4 + (g * 28) / kGroups; }
+constexpr int item_qb(int n) { return (n >> 3) & 1; }
+constexpr int item_i(int n) { return (n & 7) + 8 * (n >> 4); }
+
+// O~^T accumulation MFMA with its accumulator pinned to AGPRs.  Written as
+// inline assembly because the compiler picks one register form for every
+// MFMA of a kernel, and the score MFMAs must write VGPRs (the softmax reads
+// them) while the 128 output registers per lane only fit in the AGPRs.  The
+// hazard recognizer does not look inside inline assembly, so the two wait
+// states a VALU write needs before an MFMA reads it are spelled out here;
+// back-to-back accumulation into the same registers needs none.
+__device__ __forceinline__ void mfma_acc(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+__device__ __forceinline__ void acc_zero(f32x16 &acc, const bf16x8 &z) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(z));
+}
+
+// Before ordinary code reads accumulators written by mfma_acc: wait out the
+// MFMA result latency (the compiler model asks for 12 wait states; 24 here).
+__device__ __forceinline__ void acc_settle(f32x16 (&o)[2][4]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]),
+                   "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
+}
+
 // transposing LDS read: see the header comment for the lane layout
-__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p) {
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t *p) {
     const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (s16x4 __attribute__((address_space(3))) *)(p));
     return __builtin_bit_cast(bf16x4, r);
@@ -93,14 +142,21 @@ __device__ __forceinline__ void tile_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// s_waitcnt encodings (gfx9): vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8; a field at its maximum does not wait.
+constexpr int kWaitVm0 = 0x0F70;   // vmcnt(0)
+constexpr int kWaitVm4 = 0x0F74;   // vmcnt(4): one tile's loads of this wave may stay in flight
+static_assert(2 * LPW == 4, "kWaitVm4 assumes four loads per wave per tile");
+
 __global__ void __launch_bounds__(NT, 1)
 attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                    const uint16_t *__restrict__ V, uint16_t *__restrict__ O,
                    float *__restrict__ LSE, int B, int Hq, int Hkv, int Nq, int Nk,
                    const int32_t *__restrict__ seqlens_q, const int32_t *__restrict__ seqlens_k,
                    float scale_log2, int causal, int nqb, int xcd_heads) {
-    // K buffers 0, 1 and V buffers 0, 1, 16 KiB each
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * TILEB];
+    // ring of four K slots and four V slots, 8 KiB each
+    __shared__ __attribute__((aligned(1024))) uint8_t k0[TILEB], k1[TILEB], k2[TILEB], k3[TILEB];
+    __shared__ __attribute__((aligned(1024))) uint8_t v0[TILEB], v1[TILEB], v2[TILEB], v3[TILEB];
 
     // ---- which (batch, head, query block) ------------------------------
     const int L = blockIdx.x;
@@ -121,7 +177,7 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     // uniform, so move them back to scalar registers
     head = __builtin_amdgcn_readfirstlane(head);
     qrev = __builtin_amdgcn_readfirstlane(qrev);
-    const int qb = causal ? (nqb - 1 - qrev) : qrev;
+    const int qb0 = causal ? (nqb - 1 - qrev) : qrev;
     const int b = head / Hq, h = head % Hq;
     const int kvh = h / (Hq / Hkv);
     // lengths and the wave index are uniform: keep them in scalar registers
@@ -132,12 +188,9 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, c = lane & 31;
-    // ping-pong groups: waves 0-3 (A) and 4-7 (B), one of each per SIMD.  The
-    // two waves of a SIMD take adjacent 32-query blocks.
-    const bool grpB = wave >= 4;
-    const int q0 = qb * BQ;
-    const int qw0 = q0 + 64 * (wave & 3) + (grpB ? 32 : 0);
-    const int qi = qw0 + c;
+    const int q0 = qb0 * BQ;
+    const int qw0 = q0 + QW * wave;         // first query of this wave
+    // this lane's queries: qw0 + c (block 0) and qw0 + 32 + c (block 1)
 
     const size_t qhead = (size_t)(b * Hq + h) * Nq;
     const uint16_t *Kh = K + (size_t)(b * Hkv + kvh) * Nk * D;
@@ -162,274 +215,439 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     // tiles this wave computes: none if all its queries are padding; with a
     // causal mask only tiles starting at or below its last query
     int wtiles = (qw0 >= Lq) ? 0 : ntiles;
-    if (causal) wtiles = min(wtiles, (qw0 + 31) / BK + 1);
+    if (causal) wtiles = min(wtiles, (qw0 + QW - 1) / BK + 1);
+    // first tile that needs a mask: the causal diagonal starts at the tile
+    // holding key qw0, the ragged end at the tile holding key Lk - 1
+    int wfirst_mask = wtiles;
+    if (causal) wfirst_mask = min(wfirst_mask, qw0 / BK);
+    if (Lk % BK) wfirst_mask = min(wfirst_mask, Lk / BK);
+    // iterations j whose next tile j + 1 is computed without a mask
+    const int nfast = max(0, wfirst_mask - 1);
 
-    // ---- Q fragment (B operand of S^T = K Q^T), kept in registers -------
-    // lane l holds Q[qi][64 g + 8 ks + 0..7] for ks = 0..7
-    bf16x8 qf[8];
+    // ---- Q fragments (B operands of S^T = K Q^T), kept in registers -----
+    // lane l holds Q[qw0 + 32 qb + c][64 g + 8 ks + 0..7] for ks = 0..7
+    bf16x8 qf[2][8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (qi < Lq) w = *reinterpret_cast<const uint4 *>(Q + (qhead + qi) * D + 64 * g + 8 * ks);
-        qf[ks] = __builtin_bit_cast(bf16x8, w);
+    for (int qb = 0; qb < 2; ++qb) {
+        const int qi = qw0 + 32 * qb + c;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            uint4 w = make_uint4(0, 0, 0, 0);
+            if (qi < Lq) w = *reinterpret_cast<const uint4 *>(Q + (qhead + qi) * D + 64 * g + 8 * ks);
+            qf[qb][ks] = __builtin_bit_cast(bf16x8, w);
+        }
     }
 
-    f32x16 oacc[4];
+    // O~^T accumulators, zeroed in the AGPRs by an MFMA of zeros (so they
+    // never pass through VGPRs)
+    f32x16 oacc[2][4];
+    {
+        const bf16x8 z8 = {};
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.0f;
-    f32x16 sacc[2];                     // S^T of the current tile
-    bf16x8 pb[2][2];                    // P~^T of the current tile (bf16)
-    float m = kNegInf;   // reference maximum of raw scores q.k for query qi
-    float msub = 0.0f;   // m * scale * log2(e) (0 while m = -inf)
-    float l = 0.0f;      // this lane's half of the running sum (same reference m)
+            for (int dt = 0; dt < 4; ++dt) acc_zero(oacc[qb][dt], z8);
+    }
+    f32x16 sacc[2];          // S^T of the tile whose softmax is next
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[qb][i] = kNegInf;
+    float m[2], msub[2], l[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        m[qb] = kNegInf;     // reference maximum of raw scores q.k
+        msub[qb] = 0.0f;     // m * scale * log2(e) (0 while m = -inf)
+        l[qb] = 0.0f;        // this lane's half of the running sum
+    }
     constexpr float kLazy = 8.0f;                 // allowed growth, base-2 units
     const float lazy_raw = kLazy / scale_log2;    // the same in raw score units
 
     // ---- direct HBM -> LDS tile loads -----------------------------------
-    // K tiles are loaded by group B, V tiles by group A.  Load j (0..15) of a
-    // tile writes LDS rows 4j .. 4j+3; wave w issues j = 4 i + (w % 4).  Lane
-    // l fills row 4j + l/16, slot l%16, which holds global 16-byte chunk
-    // (slot ^ swizzle(row)).  Rows past Lk are clamped.
-    constexpr int LPT = 4;            // 1 KiB loads per wave per tile
-    const int gw = wave & 3;          // wave index within its group
-    int loff[LPT], lrow[LPT];
+    // Load i of wave w fills LDS block 2 w + i (rows 4 (2 w + i) .. +3) of a
+    // slot; lane l fills row 4 (2 w + i) + l/16, slot l%16, which holds global
+    // 16-byte chunk (slot ^ swizzle(row)).  Offsets are in bytes within a tile.
+    uint32_t kld[LPW], vld[LPW];
+    int lrow[LPW];
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-        const int j = 4 * i + gw;
-        const int row = 4 * j + (lane >> 4);
-        const int slot = lane & 15;
+    for (int i = 0; i < LPW; ++i) {
+        const int blk = LPW * wave + i;
+        const int row = 4 * blk + (lane >> 4);
+        const int s = lane & 15;
         lrow[i] = row;
-        loff[i] = row * D + (grpB ? (slot ^ (row & 15)) : (slot ^ ((row & 3) << 2))) * 8;
+        kld[i] = row * ROWB + ((s ^ (row & 15)) << 4);
+        vld[i] = row * ROWB + ((s ^ ((row & 3) << 2)) << 4);
     }
-    auto load_tile = [&](const uint16_t *src, uint8_t *dst, int j0) __attribute__((always_inline)) {
-        const uint16_t *tb = src + (size_t)j0 * D;
-        const bool tail = (j0 + BK > Lk);
+    auto issue = [&](uint8_t *kd, uint8_t *vd, int t) __attribute__((always_inline)) {
+        const int j0 = t * BK;
+        const uint8_t *kt = reinterpret_cast<const uint8_t *>(Kh + (size_t)j0 * D);
+        const uint8_t *vt = reinterpret_cast<const uint8_t *>(Vh + (size_t)j0 * D);
+        uint32_t ko[LPW], vo[LPW];
 #pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            const int j = 4 * i + gw;
-            int off = loff[i];
-            if (tail) off += (min(j0 + lrow[i], Lk - 1) - (j0 + lrow[i])) * D;
-            __builtin_amdgcn_global_load_lds(
-                (const void __attribute__((address_space(1))) *)(tb + off),
-                (void __attribute__((address_space(3))) *)(dst + j * 1024), 16, 0, 0);
+        for (int i = 0; i < LPW; ++i) { ko[i] = kld[i]; vo[i] = vld[i]; }
+        if (j0 + BK > Lk) {
+            // rows past Lk re-read row Lk - 1 (finite data, masked later)
+#pragma unroll
+            for (int i = 0; i < LPW; ++i) {
+                const int back = (j0 + lrow[i] - min(j0 + lrow[i], Lk - 1)) * ROWB;
+                ko[i] -= back;
+                vo[i] -= back;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            const int blk = LPW * wave + i;
+            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(kt + ko[i]),
+                                             (void __attribute__((address_space(3))) *)(kd + blk * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(vt + vo[i]),
+                                             (void __attribute__((address_space(3))) *)(vd + blk * 1024), 16, 0, 0);
         }
     };
 
-    // per-lane LDS byte offsets (within a tile) of the QK A operand: row
-    // 32 mt + c, chunk 8 g + ks -> slot (8 g + ks) ^ (c % 16)
-    const int ka_row = c * ROWB;
-    const int ka_sb = (8 * g) ^ (c & 15);
+    // per-lane LDS byte offsets (within a tile) of the QK A operand: row c,
+    // chunk 8 g + ks -> slot (8 g + ks) ^ (c % 16)
+    uint32_t koff[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) koff[ks] = c * ROWB + ((((8 * g) ^ (c & 15)) ^ ks) << 4);
     // transposing V read: 16-lane group q = lane/16, index i = lane%16:
     // row kb + i/4 (kb a multiple of 4), dims 32 dt + 16 (q%2) + 4 (i%4) ..+3
     const int trq = lane >> 4, tri = lane & 15;
     const int tr_row = 4 * (trq >> 1) + (tri >> 2);
     const int tr_sw = (tri >> 2) << 2;                  // 4 * (row % 4)
     const int tr_half = (tri & 1) * 8;
+    uint32_t voff[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        const int chunk = 4 * dt + 2 * (trq & 1) + ((tri & 3) >> 1);
+        voff[dt] = tr_row * ROWB + ((chunk ^ tr_sw) << 4) + tr_half;
+    }
 
-    // S^T = K Q^T (raw scores): lane holds key 32 mt + 8 r + 4 g + u of the
-    // tile in sacc[mt][4 r + u], query qi
-    auto qk = [&](const uint8_t *Kb) __attribute__((always_inline)) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[mt][i] = 0.0f;
+    // S^T = K Q^T (raw scores) of one tile: lane holds key 8 r + 4 g + u of
+    // the tile in s[qb][4 r + u], query qw0 + 32 qb + c
+    auto qk = [&](const uint8_t *kb, f32x16 (&s)[2]) __attribute__((always_inline)) {
+        const f32x16 zero = {};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb + koff[ks]);
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                    Kb + mt * 32 * ROWB + ka_row + ((ka_sb ^ ks) << 4));
-                sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[mt], 0, 0, 0);
-            }
+            for (int qb = 0; qb < 2; ++qb)
+                s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], ks ? s[qb] : zero, 0, 0, 0);
         }
-        // one operand read per MFMA, one ahead: bounded register footprint
-        // (the other wave of the SIMD covers the LDS latency)
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int i = 0; i < 14; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     };
 
     // O~^T += V^T P~^T.  A operand, lane l, dim row 32 dt + c: keys
-    // 32 mt + 16 hh + 4 g + 0..3 and + 8, the same keys in the same order as
-    // the B operand's elements
-    auto pv = [&](const uint8_t *Vb) __attribute__((always_inline)) {
+    // 16 hh + 4 g + 0..3 and + 8, the same keys in the same order as the B
+    // operand's elements
+    auto pv = [&](const uint8_t *vb, const bf16x8 (&p)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-            // chunk of dims 32 dt + 16 (q%2) + 4 (i%4): 4 dt + 2 (q%2) + (i%4)/2
-            const int chunk = 4 * dt + 2 * (trq & 1) + ((tri & 3) >> 1);
-            const int cofs = ((chunk ^ tr_sw) << 4) + tr_half;
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int dt = 0; dt < 4; ++dt) {
+                const uint8_t *base = vb + 16 * hh * ROWB + voff[dt];
+                const bf16x4 lo = lds_read_tr(base);
+                const bf16x4 hi = lds_read_tr(base + 8 * ROWB);
+                const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const uint8_t *base = Vb + (32 * mt + 16 * hh + tr_row) * ROWB + cofs;
-                    const bf16x4 lo = lds_read_tr(reinterpret_cast<const uint16_t *>(base));
-                    const bf16x4 hi = lds_read_tr(reinterpret_cast<const uint16_t *>(base + 8 * ROWB));
-                    const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[mt][hh], oacc[dt], 0, 0, 0);
-                }
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int i = 0; i < 14; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                for (int qb = 0; qb < 2; ++qb) mfma_acc(oacc[qb][dt], a, p[qb][hh]);
+            }
     };
 
-    // softmax of tile t: masks, reference maximum, P~ = exp2(S - m), l
-    auto softmax = [&](int t) __attribute__((always_inline)) {
-        const int j0 = t * BK;
-        const bool need_mask = (j0 + BK > Lk) || (causal && j0 + BK - 1 > qw0);
-        if (need_mask) {
-            // key j0 + 32 mt + 8 r + 4 g + u is visible iff it is <= lim
-            const int lim = (causal ? min(Lk - 1, qi) : Lk - 1) - j0 - 4 * g;
+    // P~ = exp2(S scale log2e - m scale log2e) as bf16 B operands, l += row sums
+    auto expo = [&](const f32x16 (&s)[2], bf16x8 (&p)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if (32 * mt + 8 * r + u > lim) sacc[mt][4 * r + u] = kNegInf;
-        }
-        float tmax;
-        {
-            float mx[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int mt = k >> 1, o = (k & 1) * 8;
-                mx[k] = fmaxf(fmaxf(fmaxf(sacc[mt][o + 0], sacc[mt][o + 1]), fmaxf(sacc[mt][o + 2], sacc[mt][o + 3])),
-                              fmaxf(fmaxf(sacc[mt][o + 4], sacc[mt][o + 5]), fmaxf(sacc[mt][o + 6], sacc[mt][o + 7])));
-            }
-            tmax = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
-            // the other 32 keys of this query sit in lane l ^ 32
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax),
-                                                             __float_as_uint(tmax), false, false);
-            tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        // The reference m only moves when some lane's tile maximum exceeds it
-        // by more than kLazy (base-2 units): every weight is then at most
-        // 2^kLazy, far from fp32/bf16 overflow, and the final O~/l and LSE do
-        // not depend on which common reference was used.  When it moves, O~
-        // and l are rescaled by exp2(m_old - m_new) (0 when m_old is -inf:
-        // nothing accumulated yet).
-        if (!__all(tmax <= m + lazy_raw)) {
-            const float mn = fmaxf(m, tmax);
-            const float alpha = (mn == kNegInf || m == mn) ? 1.0f
-                              : (m == kNegInf ? 0.0f : fast_exp2((m - mn) * scale_log2));
-            l *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-            m = mn;
-            msub = (mn == kNegInf) ? 0.0f : mn * scale_log2;
-        }
-        float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int qb = 0; qb < 2; ++qb) {
+            float e[16];
+            float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float p = fast_exp2(fmaf(sacc[mt][i], scale_log2, -msub));
-                sacc[mt][i] = p;
-                rs[i & 3] += p;
+                e[i] = fast_exp2(fmaf(s[qb][i], scale_log2, -msub[qb]));
+                rs[i & 3] += e[i];
             }
-        l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-        // P~^T as bf16 B operands: k-step (mt, hh) = s[mt][8 hh .. 8 hh + 7]
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+            l[qb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 f32x8 f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) f[e] = sacc[mt][8 * hh + e];
-                pb[mt][hh] = __builtin_convertvector(f, bf16x8);
+                for (int k = 0; k < 8; ++k) f[k] = e[8 * hh + k];
+                p[qb][hh] = __builtin_convertvector(f, bf16x8);
             }
+        }
     };
 
-    // ---- schedule --------------------------------------------------------
-    // Phases p = 0 .. 2 ntiles, separated by barriers.  Group A runs the
-    // softmax of tile t in phase 2t and the MFMAs of tile t (P~V(t), then
-    // S(t+1) = K(t+1) Q^T) in phase 2t+1; group B runs one phase later.  On
-    // each SIMD one wave is in its MFMA phase while the other exponentiates.
-    // K(j) lives in K buffer j%2 and is read in phases 2j-1 and 2j; V(j)
-    // lives in V buffer j%2 and is read in phases 2j+1 and 2j+2.
-    //  * group B loads K(t+2) at the start of its softmax phase 2t+1 (the
-    //    buffer's previous tile was last read in phase 2t) and waits for it
-    //    at the end of that phase;
-    //  * group A loads V(t+1) at the end of its MFMA phase 2t+1 (the buffer's
-    //    previous tile was last read in phase 2t) and waits for it at the end
-    //    of its softmax phase 2t+2.
-    // No wave reads LDS while its own loads are in flight.
-    uint8_t *Kbuf0 = lds, *Kbuf1 = lds + TILEB, *Vbuf0 = lds + 2 * TILEB, *Vbuf1 = lds + 3 * TILEB;
-
-    // prologue: K(0), K(1), V(0) resident; group A computes S(0)
-    if (ntiles > 0) {
-        if (grpB) {
-            load_tile(Kh, Kbuf0, 0);
-            if (ntiles > 1) load_tile(Kh, Kbuf1, BK);
-        } else {
-            load_tile(Vh, Vbuf0, 0);
+    // key 32 t + 8 r + 4 g + u is visible to query q iff it is <= min(Lk-1, q)
+    // (causal) or <= Lk - 1
+    auto mask = [&](f32x16 (&s)[2], int t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int qi = qw0 + 32 * qb + c;
+            const int lim = (causal ? min(Lk - 1, qi) : Lk - 1) - t * BK - 4 * g;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (8 * r + u > lim) s[qb][4 * r + u] = kNegInf;
         }
+    };
+
+    // tile maximum of each query (both halves of the tile)
+    auto tile_max = [&](const f32x16 (&s)[2], float (&tm)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float t = fmaxf(fmaxf(s[qb][0], s[qb][1]), s[qb][2]);
+#pragma unroll
+            for (int i = 3; i < 15; i += 2) t = fmaxf(fmaxf(t, s[qb][i]), s[qb][i + 1]);
+            t = fmaxf(t, s[qb][15]);
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+            tm[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+    };
+
+    // The reference m only moves when some lane's tile maximum exceeds it by
+    // more than kLazy (base-2 units): every weight is then at most 2^kLazy,
+    // far from fp32/bf16 overflow, and the final O~/l and LSE do not depend
+    // on which common reference was used.  When it moves, O~ and l are
+    // rescaled by exp2(m_old - m_new) (0 when m_old is -inf: nothing
+    // accumulated yet).
+    auto update_ref = [&](const float (&tm)[2]) __attribute__((always_inline)) {
+        if (!__all((tm[0] <= m[0] + lazy_raw) && (tm[1] <= m[1] + lazy_raw))) {
+            acc_settle(oacc);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const float mn = fmaxf(m[qb], tm[qb]);
+                const float alpha = (mn == kNegInf || m[qb] == mn) ? 1.0f
+                                  : (m[qb] == kNegInf ? 0.0f : fast_exp2((m[qb] - mn) * scale_log2));
+                l[qb] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[qb][dt][i] *= alpha;
+                m[qb] = mn;
+                msub[qb] = (mn == kNegInf) ? 0.0f : mn * scale_log2;
+            }
+        }
+    };
+
+    // slot buffers by (compile-time) index
+    auto kslot = [&](auto S) __attribute__((always_inline)) -> uint8_t * {
+        constexpr int s = decltype(S)::value & 3;
+        return s == 0 ? k0 : s == 1 ? k1 : s == 2 ? k2 : k3;
+    };
+    auto vslot = [&](auto S) __attribute__((always_inline)) -> uint8_t * {
+        constexpr int s = decltype(S)::value & 3;
+        return s == 0 ? v0 : s == 1 ? v1 : s == 2 ? v2 : v3;
+    };
+
+    // top of iteration j: tile j + 1 resident for every wave, and every wave
+    // done with iteration j - 1, whose slot (j + 3) % 4 is refilled here
+    auto enter = [&](auto S, int j) __attribute__((always_inline)) {
+        if (j + 2 < ntiles) __builtin_amdgcn_s_waitcnt(kWaitVm4);
+        else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        tile_barrier();
+        if (j + AHEAD < ntiles) issue(kslot(Slot<decltype(S)::value + 3>{}), vslot(Slot<decltype(S)::value + 3>{}), j + AHEAD);
+    };
+
+    // Iteration j, laid out as 32 MFMA steps: steps 0-15 compute
+    // S(j+1) = K(j+1) Q^T, steps 16-31 add P~(j) V(j) to O~.  The vector
+    // work rides between them, software-pipelined so that no step waits on
+    // a result produced in the same step: the 32 exponential items of tile j
+    // go through three stages (fma, exp2, sum/convert) in consecutive steps,
+    // each bf16 P~ operand ready before its P~V step; then the maximum of
+    // tile j+1 as a shallow tree.  Operand reads run four or five steps
+    // ahead of their MFMA.  sched_barrier keeps the compiler from regrouping
+    // the steps.  With MASKED, the scores of tile j+1 are masked first.
+    auto body = [&](auto S, auto MASKED, int j) __attribute__((always_inline)) {
+        constexpr bool masked = decltype(MASKED)::value != 0;
+        enter(S, j);
+        const uint8_t *kb = kslot(Slot<decltype(S)::value + 1>{});
+        const uint8_t *vb = vslot(S);
+        const f32x16 zero = {};
+        float e[2][16];
+        float rs[2][4] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+        bf16x8 pb[2][2];
+        f32x16 sn[2];
+        bf16x8 ka[8];
+        bf16x8 va[2][4];
+        float px[2][6];
+
+        // stage 0 (fma), 1 (exp2) or 2 (sum, and the bf16 operand after the
+        // eighth item of an operand) of the items of group G
+        auto stage = [&](auto STAGE, auto G) __attribute__((always_inline)) {
+            constexpr int stg = decltype(STAGE)::value, grp = decltype(G)::value - 1;
+            static_for<item_lo(grp), item_lo(grp + 1)>([&](auto N) __attribute__((always_inline)) {
+                constexpr int n = decltype(N)::value, qb = item_qb(n), i = item_i(n);
+                if constexpr (stg == 0) {
+                    e[qb][i] = fmaf(sacc[qb][i], scale_log2, -msub[qb]);
+                } else if constexpr (stg == 1) {
+                    e[qb][i] = fast_exp2(e[qb][i]);
+                } else {
+                    rs[qb][i & 3] += e[qb][i];
+                    if constexpr ((n & 7) == 7) {
+                        constexpr int hh = n >> 4;
+                        f32x8 f;
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) f[k] = e[qb][8 * hh + k];
+                        pb[qb][hh] = __builtin_convertvector(f, bf16x8);
+                    }
+                }
+            });
+        };
+        auto rk = [&](int ks) __attribute__((always_inline)) {
+            ka[ks] = *reinterpret_cast<const bf16x8 *>(kb + koff[ks]);
+        };
+        auto rv = [&](int hh, int dt) __attribute__((always_inline)) {
+            const uint8_t *base = vb + 16 * hh * ROWB + voff[dt];
+            const bf16x4 lo4 = lds_read_tr(base);
+            const bf16x4 hi4 = lds_read_tr(base + 8 * ROWB);
+            va[hh][dt] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+
+        rk(0);
+        rk(1);
+        stage(Slot<0>{}, Slot<0>{});          // fma of group -1
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, 32>([&](auto ST) __attribute__((always_inline)) {
+            constexpr int st = decltype(ST)::value;
+            if constexpr (st < 16) {
+                constexpr int ks = st >> 1, qb = st & 1;
+                sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[qb][ks], ks ? sn[qb] : zero, 0, 0, 0);
+            } else {
+                constexpr int t = st - 16, hh = t >> 3, dt = (t >> 1) & 3, qb = t & 1;
+                mfma_acc(oacc[qb][dt], va[hh][dt], pb[qb][hh]);
+            }
+            // K operand of step 2 ks is read at step 2 ks - 4
+            if constexpr (st < 12 && !(st & 1)) rk((st + 4) >> 1);
+            // V operand of step 16 + 8 hh + 2 dt is read five steps earlier
+            if constexpr (st >= 11 && st < 27 && (st & 1)) rv((st - 11) >> 3, ((st - 11) >> 1) & 3);
+            // exponential pipeline: fma of group st, exp2 of st-1, sum of st-2
+            // (Slot<g + 1> names group g)
+            if constexpr (st < kGroups) stage(Slot<0>{}, Slot<st + 1>{});
+            if constexpr (st <= kGroups) stage(Slot<1>{}, Slot<st>{});
+            if constexpr (st >= 1 && st <= kGroups + 1) stage(Slot<2>{}, Slot<st - 1>{});
+            // masked iterations: mask S(j+1) once its MFMAs are done
+            if constexpr (masked && st >= 17 && st < 25) {
+                constexpr int qb = (st - 17) >> 2, r = (st - 17) & 3;
+                const int qi = qw0 + 32 * qb + c;
+                const int lim = (causal ? min(Lk - 1, qi) : Lk - 1) - (j + 1) * BK - 4 * g;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (8 * r + u > lim) sn[qb][4 * r + u] = kNegInf;
+            }
+            // maximum of tile j+1: five independent max3 per block, then two
+            if constexpr (st >= 25 && st < 30) {
+                constexpr int k = st - 25;
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+                    px[qb][k] = fmaxf(fmaxf(sn[qb][3 * k], sn[qb][3 * k + 1]), sn[qb][3 * k + 2]);
+            }
+            if constexpr (st == 30) {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    px[qb][0] = fmaxf(fmaxf(px[qb][0], px[qb][1]), px[qb][2]);
+                    px[qb][3] = fmaxf(fmaxf(px[qb][3], px[qb][4]), sn[qb][15]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            l[qb] += (rs[qb][0] + rs[qb][1]) + (rs[qb][2] + rs[qb][3]);
+            sacc[qb] = sn[qb];
+        }
+        float tm[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const float t = fmaxf(px[qb][0], px[qb][3]);
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+            tm[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            // past the last tile the scores are of stale LDS data: unused
+            if (masked && j + 1 >= wtiles) tm[qb] = kNegInf;
+        }
+        update_ref(tm);
+    };
+
+    // ---- prologue: tiles 0 .. AHEAD-1 in flight, S(0) and its maximum ----
+    if (ntiles < 4) {
+        // slots no tile will fill: zero them (the masked loop reads them)
+        auto zero_slot = [&](uint8_t *kd, uint8_t *vd) __attribute__((always_inline)) {
+            for (int o = tid * 16; o < TILEB; o += NT * 16) {
+                *reinterpret_cast<uint4 *>(kd + o) = make_uint4(0, 0, 0, 0);
+                *reinterpret_cast<uint4 *>(vd + o) = make_uint4(0, 0, 0, 0);
+            }
+        };
+        if (ntiles < 1) zero_slot(k0, v0);
+        if (ntiles < 2) zero_slot(k1, v1);
+        if (ntiles < 3) zero_slot(k2, v2);
+        zero_slot(k3, v3);
     }
+    if (ntiles > 0) issue(k0, v0, 0);
+    if (ntiles > 1) issue(k1, v1, 1);
+    if (ntiles > 2) issue(k2, v2, 2);
     __builtin_amdgcn_s_waitcnt(0);   // nothing in flight (Q included)
     __syncthreads();
-    if (!grpB && wtiles > 0) qk(Kbuf0);
+    if (wtiles > 0) {
+        qk(k0, sacc);
+        if (wfirst_mask == 0) mask(sacc, 0);
+        float tm[2];
+        tile_max(sacc, tm);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            // nothing accumulated yet: take the tile maximum as reference
+            m[qb] = tm[qb];
+            msub[qb] = (tm[qb] == kNegInf) ? 0.0f : tm[qb] * scale_log2;
+        }
+    }
 
-    // Each iteration k covers phases 2k and 2k+1: group A runs softmax(k)
-    // then the MFMAs of tile k; group B runs the MFMAs of tile k-1 then
-    // softmax(k).  The two groups run separate loops that pass the same
-    // barriers (two per iteration, ntiles + 1 iterations).
-    if (!grpB) {
-        for (int k = 0; k <= ntiles; ++k) {
-            if (k < wtiles) softmax(k);
-            __builtin_amdgcn_s_waitcnt(0x0070);      // vmcnt(0) lgkmcnt(0): own V loads landed
-            tile_barrier();
-            if (k < wtiles) pv((k & 1) ? Vbuf1 : Vbuf0);
-            if (k + 1 < wtiles) qk(((k + 1) & 1) ? Kbuf1 : Kbuf0);
-            __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this wave's LDS reads done
-            if (k + 1 < ntiles) load_tile(Vh, ((k + 1) & 1) ? Vbuf1 : Vbuf0, (k + 1) * BK);
-            tile_barrier();
-        }
-    } else {
-        for (int k = 0; k <= ntiles; ++k) {
-            const int t = k - 1;
-            if (t >= 0 && t < wtiles) pv((t & 1) ? Vbuf1 : Vbuf0);
-            if (t + 1 < wtiles) qk(((t + 1) & 1) ? Kbuf1 : Kbuf0);
-            __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
-            tile_barrier();
-            if (k + 2 < ntiles) load_tile(Kh, (k & 1) ? Kbuf1 : Kbuf0, (k + 2) * BK);
-            if (k < wtiles) softmax(k);
-            __builtin_amdgcn_s_waitcnt(0x0070);      // vmcnt(0) lgkmcnt(0): own K loads landed
-            tile_barrier();
-        }
+    // ---- main loop (unrolled by the ring size), then the masked tail -----
+    // Control flow never joins two versions of the accumulators (the
+    // compiler would copy all 128 of them through VGPRs): the masked loop also
+    // runs in whole groups of four.  Its iterations past wtiles are exact
+    // no-ops: every score of those tiles is masked, so P~ = 0, and every V
+    // slot holds finite data.  Every wave passes the same barriers.
+    const int wend = (wtiles + 3) & ~3, nend = (ntiles + 3) & ~3;
+    int j = 0;
+    for (; j + 4 <= nfast; j += 4) {
+        body(Slot<0>{}, Slot<0>{}, j);
+        body(Slot<1>{}, Slot<0>{}, j + 1);
+        body(Slot<2>{}, Slot<0>{}, j + 2);
+        body(Slot<3>{}, Slot<0>{}, j + 3);
+    }
+    for (; j < wend; j += 4) {
+        body(Slot<0>{}, Slot<1>{}, j);
+        body(Slot<1>{}, Slot<1>{}, j + 1);
+        body(Slot<2>{}, Slot<1>{}, j + 2);
+        body(Slot<3>{}, Slot<1>{}, j + 3);
+    }
+    // this wave is done; keep loading and passing barriers with the others
+    for (; j < nend; j += 4) {
+        enter(Slot<0>{}, j);
+        enter(Slot<1>{}, j + 1);
+        enter(Slot<2>{}, j + 2);
+        enter(Slot<3>{}, j + 3);
     }
 
     // ---- epilogue: O = O~ / l once, LSE = m + log l ------------------------
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
-    const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const bool valid = (qi < Lq) && (lt > 0.0f);
-    const float inv = valid ? 1.0f / lt : 0.0f;
-    if (qi < Nq) {
-        uint16_t *orow = O + (qhead + qi) * D;
+    acc_settle(oacc);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+    for (int qb = 0; qb < 2; ++qb) {
+        const int qi = qw0 + 32 * qb + c;
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l[qb]), __float_as_uint(l[qb]), false, false);
+        const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const bool valid = (qi < Lq) && (lt > 0.0f);
+        const float inv = valid ? 1.0f / lt : 0.0f;
+        if (qi < Nq) {
+            uint16_t *orow = O + (qhead + qi) * D;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                uint2 w;
-                w.x = pack_bf16x2(oacc[dt][4 * r + 0] * inv, oacc[dt][4 * r + 1] * inv);
-                w.y = pack_bf16x2(oacc[dt][4 * r + 2] * inv, oacc[dt][4 * r + 3] * inv);
-                *reinterpret_cast<uint2 *>(orow + 32 * dt + 8 * r + 4 * g) = w;
-            }
-        if (LSE && g == 0)
-            LSE[qhead + qi] = valid ? (m * scale_log2 + __log2f(lt)) * kLn2 : kNegInf;
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    uint2 w;
+                    w.x = valid ? pack_bf16x2(oacc[qb][dt][4 * r + 0] * inv, oacc[qb][dt][4 * r + 1] * inv) : 0u;
+                    w.y = valid ? pack_bf16x2(oacc[qb][dt][4 * r + 2] * inv, oacc[qb][dt][4 * r + 3] * inv) : 0u;
+                    *reinterpret_cast<uint2 *>(orow + 32 * dt + 8 * r + 4 * g) = w;
+                }
+            if (LSE && g == 0)
+                LSE[qhead + qi] = valid ? (m[qb] * scale_log2 + __log2f(lt)) * kLn2 : kNegInf;
+        }
     }
 }
 
