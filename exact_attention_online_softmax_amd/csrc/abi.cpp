@@ -52,6 +52,8 @@ osm_status osm_attn_fwd(const void *q, const void *k, const void *v, void *o, fl
         heads_q % heads_kv != 0 || !(scale > 0.0f) || !isfinite(scale) || (causal != 0 && causal != 1))
         return OSM_ERR_SHAPE;
     if (dtype != OSM_BF16 || head_dim != 128) return OSM_ERR_UNSUPPORTED;
+    // one head's K (or V) rows are addressed with 32-bit byte offsets
+    if ((int64_t)seqlen_k * head_dim * 2 >= ((int64_t)1 << 31)) return OSM_ERR_UNSUPPORTED;
     if (seqlen_q == 0) return OSM_OK;
     if (!q || !o || (seqlen_k > 0 && (!k || !v))) return OSM_ERR_NULL;
     osm::AttnFwdArgs a{q, k, v, o, lse, batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim,

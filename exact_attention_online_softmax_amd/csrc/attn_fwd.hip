@@ -142,6 +142,10 @@ __device__ __forceinline__ void tile_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Buffer resource word 3 for raw (unformatted, unswizzled) dword access:
+// DATA_FORMAT = 32 bits, everything else zero.
+constexpr int kRsrcWord3 = 0x00020000;
+
 // s_waitcnt encodings (gfx9): vmcnt in bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8; a field at its maximum does not wait.
 constexpr int kWaitVm0 = 0x0F70;   // vmcnt(0)
@@ -267,41 +271,46 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     // Load i of wave w fills LDS block 2 w + i (rows 4 (2 w + i) .. +3) of a
     // slot; lane l fills row 4 (2 w + i) + l/16, slot l%16, which holds global
     // 16-byte chunk (slot ^ swizzle(row)).  Offsets are in bytes within a tile.
+    // The loads go through a buffer resource that starts at the tile and
+    // spans its rows below Lk: the range check turns rows past Lk (and every
+    // row of a tile at or past Lk) into zeros without touching memory, so
+    // LDS only ever holds finite data, and a load needs no branch.  The
+    // buffer (MUBUF) form of the LDS DMA is used because with the global
+    // (FLAT) form in flight the compiler turns every LDS operand wait into a
+    // wait for all LDS reads.
     uint32_t kld[LPW], vld[LPW];
-    int lrow[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
         const int blk = LPW * wave + i;
         const int row = 4 * blk + (lane >> 4);
         const int s = lane & 15;
-        lrow[i] = row;
         kld[i] = row * ROWB + ((s ^ (row & 15)) << 4);
         vld[i] = row * ROWB + ((s ^ ((row & 3) << 2)) << 4);
     }
-    auto issue = [&](uint8_t *kd, uint8_t *vd, int t) __attribute__((always_inline)) {
+    struct TileRsrc {
+        __amdgpu_buffer_rsrc_t k, v;
+    };
+    auto tile_rsrc = [&](int t) __attribute__((always_inline)) -> TileRsrc {
         const int j0 = t * BK;
-        const uint8_t *kt = reinterpret_cast<const uint8_t *>(Kh + (size_t)j0 * D);
-        const uint8_t *vt = reinterpret_cast<const uint8_t *>(Vh + (size_t)j0 * D);
-        uint32_t ko[LPW], vo[LPW];
+        const int bytes = max(0, Lk - j0) * ROWB;   // < 2^31: the ABI bounds Nk * 256
+        return {__builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(Kh) + (size_t)j0 * D, 0, bytes, kRsrcWord3),
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(Vh) + (size_t)j0 * D, 0, bytes, kRsrcWord3)};
+    };
+    // one of the four loads (K block 0, V block 0, K block 1, V block 1) of
+    // this wave's share of a tile
+    auto load1 = [&](const TileRsrc &r, uint8_t *kd, uint8_t *vd, int which) __attribute__((always_inline)) {
+        const int i = which >> 1, blk = LPW * wave + i;
+        if (which & 1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r.v, (void __attribute__((address_space(3))) *)(vd + blk * 1024), 16,
+                                                     vld[i], 0, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r.k, (void __attribute__((address_space(3))) *)(kd + blk * 1024), 16,
+                                                     kld[i], 0, 0, 0);
+    };
+    auto issue = [&](uint8_t *kd, uint8_t *vd, int t) __attribute__((always_inline)) {
+        const TileRsrc r = tile_rsrc(t);
 #pragma unroll
-        for (int i = 0; i < LPW; ++i) { ko[i] = kld[i]; vo[i] = vld[i]; }
-        if (j0 + BK > Lk) {
-            // rows past Lk re-read row Lk - 1 (finite data, masked later)
-#pragma unroll
-            for (int i = 0; i < LPW; ++i) {
-                const int back = (j0 + lrow[i] - min(j0 + lrow[i], Lk - 1)) * ROWB;
-                ko[i] -= back;
-                vo[i] -= back;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-            const int blk = LPW * wave + i;
-            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(kt + ko[i]),
-                                             (void __attribute__((address_space(3))) *)(kd + blk * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(vt + vo[i]),
-                                             (void __attribute__((address_space(3))) *)(vd + blk * 1024), 16, 0, 0);
-        }
+        for (int w = 0; w < 2 * LPW; ++w) load1(r, kd, vd, w);
     };
 
     // per-lane LDS byte offsets (within a tile) of the QK A operand: row c,
@@ -439,11 +448,17 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 
     // top of iteration j: tile j + 1 resident for every wave, and every wave
     // done with iteration j - 1, whose slot (j + 3) % 4 is refilled here
-    auto enter = [&](auto S, int j) __attribute__((always_inline)) {
-        if (j + 2 < ntiles) __builtin_amdgcn_s_waitcnt(kWaitVm4);
-        else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    // Every iteration issues exactly four loads per wave (tiles past the end
+    // are zero fills of consumed slots), so at the top of iteration j the
+    // loads of tiles j+1 and j+2 are the ones in flight.
+    auto enter = [&](int j) __attribute__((always_inline)) {
+        (void)j;
+        __builtin_amdgcn_s_waitcnt(kWaitVm4);
         tile_barrier();
-        if (j + AHEAD < ntiles) issue(kslot(Slot<decltype(S)::value + 3>{}), vslot(Slot<decltype(S)::value + 3>{}), j + AHEAD);
+    };
+    auto idle = [&](auto S, int j) __attribute__((always_inline)) {
+        enter(j);
+        issue(kslot(Slot<decltype(S)::value + 3>{}), vslot(Slot<decltype(S)::value + 3>{}), j + AHEAD);
     };
 
     // Iteration j, laid out as 32 MFMA steps: steps 0-15 compute
@@ -457,9 +472,12 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     // the steps.  With MASKED, the scores of tile j+1 are masked first.
     auto body = [&](auto S, auto MASKED, int j) __attribute__((always_inline)) {
         constexpr bool masked = decltype(MASKED)::value != 0;
-        enter(S, j);
+        enter(j);
         const uint8_t *kb = kslot(Slot<decltype(S)::value + 1>{});
         const uint8_t *vb = vslot(S);
+        uint8_t *kd = kslot(Slot<decltype(S)::value + 3>{});
+        uint8_t *vd = vslot(Slot<decltype(S)::value + 3>{});
+        const TileRsrc lr = tile_rsrc(j + AHEAD);
         const f32x16 zero = {};
         float e[2][16];
         float rs[2][4] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
@@ -514,6 +532,8 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
                 constexpr int t = st - 16, hh = t >> 3, dt = (t >> 1) & 3, qb = t & 1;
                 mfma_acc(oacc[qb][dt], va[hh][dt], pb[qb][hh]);
             }
+            // this wave's loads of tile j+3, one every eight steps
+            if constexpr ((st & 7) == 3) load1(lr, kd, vd, st >> 3);
             // K operand of step 2 ks is read at step 2 ks - 4
             if constexpr (st < 12 && !(st & 1)) rk((st + 4) >> 1);
             // V operand of step 16 + 8 hh + 2 dt is read five steps earlier
@@ -566,22 +586,10 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     };
 
     // ---- prologue: tiles 0 .. AHEAD-1 in flight, S(0) and its maximum ----
-    if (ntiles < 4) {
-        // slots no tile will fill: zero them (the masked loop reads them)
-        auto zero_slot = [&](uint8_t *kd, uint8_t *vd) __attribute__((always_inline)) {
-            for (int o = tid * 16; o < TILEB; o += NT * 16) {
-                *reinterpret_cast<uint4 *>(kd + o) = make_uint4(0, 0, 0, 0);
-                *reinterpret_cast<uint4 *>(vd + o) = make_uint4(0, 0, 0, 0);
-            }
-        };
-        if (ntiles < 1) zero_slot(k0, v0);
-        if (ntiles < 2) zero_slot(k1, v1);
-        if (ntiles < 3) zero_slot(k2, v2);
-        zero_slot(k3, v3);
-    }
-    if (ntiles > 0) issue(k0, v0, 0);
-    if (ntiles > 1) issue(k1, v1, 1);
-    if (ntiles > 2) issue(k2, v2, 2);
+    // tiles 0..2 (zero fills past the end); iteration 0 fills slot 3
+    issue(k0, v0, 0);
+    issue(k1, v1, 1);
+    issue(k2, v2, 2);
     __builtin_amdgcn_s_waitcnt(0);   // nothing in flight (Q included)
     __syncthreads();
     if (wtiles > 0) {
@@ -619,11 +627,12 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     }
     // this wave is done; keep loading and passing barriers with the others
     for (; j < nend; j += 4) {
-        enter(Slot<0>{}, j);
-        enter(Slot<1>{}, j + 1);
-        enter(Slot<2>{}, j + 2);
-        enter(Slot<3>{}, j + 3);
+        idle(Slot<0>{}, j);
+        idle(Slot<1>{}, j + 1);
+        idle(Slot<2>{}, j + 2);
+        idle(Slot<3>{}, j + 3);
     }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // no load outlives the loop
 
     // ---- epilogue: O = O~ / l once, LSE = m + log l ------------------------
     acc_settle(oacc);

@@ -120,7 +120,8 @@ osm_status osm_softmax_rows(const float *x, float *y, int64_t rows, int64_t cols
  * products, fp32 running state, O rounded to bf16 once at the end.
  * Errors: OSM_ERR_NULL, OSM_ERR_SHAPE (non-positive batch/heads/head_dim,
  * negative seqlens, heads_q % heads_kv != 0, scale not finite or <= 0),
- * OSM_ERR_UNSUPPORTED (other dtype or head_dim), OSM_ERR_HIP.
+ * OSM_ERR_UNSUPPORTED (other dtype or head_dim, or one head's K rows
+ * spanning 2 GiB or more: seqlen_k >= 2^23 at head_dim 128), OSM_ERR_HIP.
  */
 osm_status osm_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                         osm_dtype dtype, int32_t batch, int32_t heads_q, int32_t heads_kv,

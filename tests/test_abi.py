@@ -81,6 +81,7 @@ def test_attn_fwd_validation(lib):
     assert call(causal=2) == 2
     assert call(dtype=osm.OSM_F32) == 3
     assert call(d=64) == 3
+    assert call(Nk=1 << 23) == 3                    # one head's K rows would span 2 GiB
     assert call(q=None) == 1
     assert call(o=None) == 1
     assert call(k=None) == 1
