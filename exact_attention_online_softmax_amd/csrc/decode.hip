@@ -10,12 +10,15 @@
 // as identity.  [P3] "The same merge, in log-sum-exp form" names the split
 // of one query's keys over many thread blocks.
 //
-// decode_split: one workgroup (8 waves) per (piece, kv head, batch).  All
+// decode_split: one workgroup (4 waves) per (piece, kv head, batch).  All
 // query heads that share the kv head (grouped-query attention) are served
 // from one read of the piece's K and V.  Lanes are grouped LPK = head_dim/8
 // per key, each lane owning 8 consecutive dims, so every wave load is a
-// contiguous run of whole cache rows; the loads of up to 256 keys of K and V
-// are issued together before any is used.  Phase 1 computes the piece's
+// contiguous run of whole cache rows; the loads of a round of 64 keys are
+// issued together before any is used.  Small workgroups with few registers
+// keep six of them on a CU, so the loads of some overlap the arithmetic of
+// others (the piece's keys are streamed in rounds rather than all held at
+// once).  Phase 1 computes the piece's
 // scores (bf16 dot products with v_dot2_f32_bf16, 16-lane sums with DPP row
 // shifts) into LDS; the piece maximum and sum follow; phase 2 accumulates
 // sum p_j v_j in fp32.
@@ -32,9 +35,9 @@ namespace osm {
 
 namespace {
 
-constexpr int DEC_THREADS = 512;
+constexpr int DEC_THREADS = 256;
 constexpr int DEC_WAVES = DEC_THREADS / 64;
-constexpr int DEC_ROUND = 256;      // keys whose loads are issued together
+constexpr int DEC_ROUND = 64;       // keys whose loads are issued together
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
