@@ -606,11 +606,11 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     }
 
     // ---- main loop (unrolled by the ring size), then the masked tail -----
-    // Control flow never joins two versions of the accumulators (the
-    // compiler would copy all 128 of them through VGPRs): the masked loop also
-    // runs in whole groups of four.  Its iterations past wtiles are exact
-    // no-ops: every score of those tiles is masked, so P~ = 0, and every V
-    // slot holds finite data.  Every wave passes the same barriers.
+    // Control flow never joins two versions of the accumulators that both
+    // came out of MFMAs (the compiler would copy all 128 of them through
+    // VGPRs): the masked loop also runs in whole groups of four, and its
+    // iterations past wtiles only load and pass the barrier.  Every wave
+    // passes the same barriers.
     const int wend = (wtiles + 3) & ~3, nend = (ntiles + 3) & ~3;
     int j = 0;
     for (; j + 4 <= nfast; j += 4) {
@@ -621,9 +621,9 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     }
     for (; j < wend; j += 4) {
         body(Slot<0>{}, Slot<1>{}, j);
-        body(Slot<1>{}, Slot<1>{}, j + 1);
-        body(Slot<2>{}, Slot<1>{}, j + 2);
-        body(Slot<3>{}, Slot<1>{}, j + 3);
+        if (j + 1 < wtiles) body(Slot<1>{}, Slot<1>{}, j + 1); else idle(Slot<1>{}, j + 1);
+        if (j + 2 < wtiles) body(Slot<2>{}, Slot<1>{}, j + 2); else idle(Slot<2>{}, j + 2);
+        if (j + 3 < wtiles) body(Slot<3>{}, Slot<1>{}, j + 3); else idle(Slot<3>{}, j + 3);
     }
     // this wave is done; keep loading and passing barriers with the others
     for (; j < nend; j += 4) {
