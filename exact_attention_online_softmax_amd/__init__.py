@@ -28,7 +28,7 @@ OSM_BF16 = 1
 STATUS = {0: "OSM_OK", 1: "OSM_ERR_NULL", 2: "OSM_ERR_SHAPE", 3: "OSM_ERR_UNSUPPORTED",
           4: "OSM_ERR_WORKSPACE", 5: "OSM_ERR_HIP"}
 EXPORTS = ("osm_status_str", "osm_softmax_rows", "osm_attn_fwd", "osm_decode_workspace_bytes",
-           "osm_attn_decode_splitkv", "osm_merge_partials")
+           "osm_attn_decode_splitkv", "osm_merge_partials", "osm_merge_lse")
 
 
 class OsmError(RuntimeError):
@@ -60,8 +60,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.osm_attn_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i32, i32, i32, i32,
                                             i32, vp, f32, i32, vp, ctypes.c_size_t, vp]
     lib.osm_merge_partials.argtypes = [vp, vp, vp, i64, i32, i32, vp, ctypes.c_int, vp, vp]
+    lib.osm_merge_lse.argtypes = [vp, vp, i64, i32, i32, ctypes.c_int, vp, ctypes.c_int, vp, vp]
     for name in ("osm_softmax_rows", "osm_attn_fwd", "osm_attn_decode_splitkv",
-                 "osm_merge_partials"):
+                 "osm_merge_partials", "osm_merge_lse"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -223,3 +224,24 @@ def merge_partials(part_m, part_l, part_o, out_dtype=None):
     _check(lib.osm_merge_partials(_ptr(part_m), _ptr(part_l), _ptr(part_o), rows, C, d, _ptr(o),
                                   _dtype_code(out_dtype), _ptr(lse), _stream()))
     return o, lse
+
+
+def merge_lse(o_parts, lse_parts, out_dtype=None, out=None, lse=None):
+    """Combine normalized results of disjoint key sets in log-sum-exp form:
+    o_parts [S, rows, d] (fp32 or bf16), lse_parts [S, rows] fp32.  Returns
+    (o [rows, d], lse [rows])."""
+    torch = _torch()
+    lib = load_library()
+    _device_tensor(o_parts, "o_parts", (torch.float32, torch.bfloat16))
+    _device_tensor(lse_parts, "lse_parts", (torch.float32,))
+    if o_parts.dim() != 3 or lse_parts.dim() != 2:
+        raise ValueError("o_parts must be [S, rows, d] and lse_parts [S, rows]")
+    S, rows, d = o_parts.shape
+    if tuple(lse_parts.shape) != (S, rows):
+        raise ValueError("lse_parts shape does not match o_parts")
+    out_dtype = o_parts.dtype if out_dtype is None else out_dtype
+    o = torch.empty((rows, d), dtype=out_dtype, device=o_parts.device) if out is None else out
+    lse_t = torch.empty(rows, dtype=torch.float32, device=o_parts.device) if lse is None else lse
+    _check(lib.osm_merge_lse(_ptr(o_parts), _ptr(lse_parts), rows, S, d, _dtype_code(o_parts.dtype),
+                             _ptr(o), _dtype_code(out_dtype), _ptr(lse_t), _stream()))
+    return o, lse_t

@@ -110,4 +110,18 @@ osm_status osm_merge_partials(const float *part_m, const float *part_l, const fl
     return hip_status(osm::launch_merge_partials(m, static_cast<hipStream_t>(stream)));
 }
 
+osm_status osm_merge_lse(const void *o_parts, const float *lse_parts, int64_t rows,
+                         int32_t num_parts, int32_t head_dim, osm_dtype in_dtype, void *o,
+                         osm_dtype out_dtype, float *lse, osm_stream stream) {
+    if (rows < 0 || num_parts < 1 || head_dim < 1) return OSM_ERR_SHAPE;
+    if ((in_dtype != OSM_F32 && in_dtype != OSM_BF16) || (out_dtype != OSM_F32 && out_dtype != OSM_BF16) ||
+        head_dim > 1024 || (head_dim % 2 != 0 && head_dim > 512))
+        return OSM_ERR_UNSUPPORTED;
+    if (rows == 0) return OSM_OK;
+    if (!o_parts || !lse_parts || !o) return OSM_ERR_NULL;
+    osm::MergeLseArgs m{o_parts, lse_parts, rows, num_parts, head_dim,
+                        in_dtype == OSM_BF16 ? 1 : 0, out_dtype == OSM_BF16 ? 1 : 0, o, lse};
+    return hip_status(osm::launch_merge_lse(m, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -68,4 +68,16 @@ struct MergeArgs {
 };
 hipError_t launch_merge_partials(const MergeArgs &a, hipStream_t s);
 
+// ---- log-sum-exp merge of normalized results -------------------------------
+struct MergeLseArgs {
+    const void *o_parts;       // [num_parts][rows][head_dim]
+    const float *lse_parts;    // [num_parts][rows]
+    int64_t rows;
+    int num_parts, head_dim;
+    int in_bf16, out_bf16;     // element types of o_parts and o
+    void *o;                   // [rows][head_dim]
+    float *lse;                // [rows] or null
+};
+hipError_t launch_merge_lse(const MergeLseArgs &a, hipStream_t s);
+
 }  // namespace osm

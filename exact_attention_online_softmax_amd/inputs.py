@@ -193,3 +193,21 @@ def random_partials(rows: int, splits: int, d: int, seed: int, empty_frac: float
     l[empty] = 0.0
     o[empty] = 0.0
     return m, l, o.astype(np.float32)
+
+
+def lse_parts(parts: int, rows: int, d: int, seed: int, *, dtype: str = "f32",
+              empty_frac: float = 0.0, poison: bool = False):
+    """Normalized results of `parts` disjoint key sets for the log-sum-exp
+    merge: o_s ~ N(0, 1) [parts, rows, d] (bf16 bits for dtype "bf16", else
+    fp32), lse_s ~ U[-8, 8] fp32 [parts, rows]; a fraction of the pieces are
+    the empty set (lse = -inf), whose o is NaN when `poison` (it must never
+    be read) and 0 otherwise."""
+    g = rng(seed)
+    o = normal_f32(g, (parts, rows, d))
+    lse = g.uniform(-8.0, 8.0, size=(parts, rows)).astype(np.float32)
+    empty = g.random((parts, rows)) < empty_frac
+    lse[empty] = -np.inf
+    o[empty] = np.nan if poison else 0.0
+    if dtype == "bf16":
+        o = to_bf16_bits(o)
+    return o, lse

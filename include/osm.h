@@ -201,6 +201,32 @@ osm_status osm_merge_partials(const float *part_m, const float *part_l, const fl
                               int64_t rows, int32_t num_splits, int32_t head_dim, void *o,
                               osm_dtype out_dtype, float *lse, osm_stream stream);
 
+/*
+ * osm_merge_lse -- combine normalized attention results of disjoint key
+ * sets (for example separate osm_attn_fwd calls over chunks of the keys)
+ * into the result over their union.
+ *
+ * [P3] "The same merge, in log-sum-exp form": each piece s carries its
+ * normalized output o_s and its log-sum-exp lse_s; the union has
+ * lse = log sum_s e^lse_s (computed as M + log sum_s e^(lse_s - M),
+ * M = max_s lse_s) and o = sum_s e^(lse_s - lse) o_s.  A piece with
+ * lse_s = -inf is the empty set: it drops out and its o_s is never read
+ * (it may hold any bits).
+ *
+ *   o_parts    [num_parts][rows][head_dim] (in_dtype)
+ *   lse_parts  fp32 [num_parts][rows], natural log; each entry finite or -inf
+ *   o          [rows][head_dim] (out_dtype, written)
+ *   lse        fp32 [rows] (written; may be NULL)
+ * A row whose pieces are all empty gives o = 0, LSE = -inf.
+ * Supported: in_dtype and out_dtype OSM_F32 or OSM_BF16; head_dim 1..1024
+ * (even) or 1..511 (odd); num_parts >= 1.  fp32 accumulation.
+ * Errors: OSM_ERR_NULL, OSM_ERR_SHAPE (rows < 0, num_parts < 1,
+ * head_dim < 1), OSM_ERR_UNSUPPORTED, OSM_ERR_HIP.
+ */
+osm_status osm_merge_lse(const void *o_parts, const float *lse_parts, int64_t rows,
+                         int32_t num_parts, int32_t head_dim, osm_dtype in_dtype, void *o,
+                         osm_dtype out_dtype, float *lse, osm_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

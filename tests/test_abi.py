@@ -129,10 +129,29 @@ def test_merge_validation(lib):
 
 
 @no_gpu_only
+def test_merge_lse_validation(lib):
+    def call(op=FAKE, lp=FAKE, rows=4, S=3, d=128, it=osm.OSM_BF16, o=FAKE, ot=osm.OSM_BF16):
+        return lib.osm_merge_lse(op, lp, rows, S, d, it, o, ot, None, None)
+    assert call(rows=-1) == 2
+    assert call(S=0) == 2
+    assert call(d=0) == 2
+    assert call(d=1026) == 3
+    assert call(d=513) == 3                         # odd head_dim is limited to 511
+    assert call(it=9) == 3
+    assert call(ot=9) == 3
+    assert call(op=None) == 1
+    assert call(lp=None) == 1
+    assert call(o=None) == 1
+    assert call(op=None, rows=0) == 0
+
+
+@no_gpu_only
 def test_no_device_reports_hip_error(lib):
     """A fully valid request in a process without a GPU fails cleanly with
     OSM_ERR_HIP (the launch is refused by the runtime, nothing is read)."""
     rc = lib.osm_merge_partials(FAKE, FAKE, FAKE, 4, 3, 64, FAKE, osm.OSM_F32, None, None)
     assert rc == 5
     rc = lib.osm_softmax_rows(FAKE, FAKE, 2, 4, 4, 4, None, None, None)
+    assert rc == 5
+    rc = lib.osm_merge_lse(FAKE, FAKE, 4, 3, 128, osm.OSM_BF16, FAKE, osm.OSM_BF16, None, None)
     assert rc == 5
