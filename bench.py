@@ -9,6 +9,8 @@ inputs already resident in HBM:
   fwd_causal osm_attn_fwd           bf16 B=8 H=16 N=8192 d=128, causal, lengths U[1024,8192]
   decode    osm_attn_decode_splitkv bf16 B=16 Hq=32 Hkv=8 d=128, L U[4096,32768], 256-key pieces
                                     (piece summaries + merge)
+  merge_lse osm_merge_lse           8 normalized pieces of a 524288-row d=128 bf16 output
+                                    (log-sum-exp merge of results over disjoint key sets)
 
 Each call is timed with HIP events on the stream it runs on (torch's current
 stream); ``value`` is the headline forward's TFLOP/s.  The CPU oracle is timed
@@ -45,7 +47,7 @@ def bf16_dev(bits, torch):
 
 
 KERNEL_SOURCES = {"fwd": "attn_fwd.hip", "fwd_causal": "attn_fwd.hip", "softmax": "softmax_rows.hip",
-                  "decode": "decode.hip"}
+                  "decode": "decode.hip", "merge_lse": "merge_lse.hip"}
 
 
 def source_hash(name):
@@ -107,7 +109,7 @@ def summarize(name, trace_dir, out):
     import csv
     import glob
     kern = {"fwd": "attn_fwd", "fwd_causal": "attn_fwd", "softmax": "softmax_rows",
-            "decode": "decode_split"}[name]
+            "decode": "decode_split", "merge_lse": "merge_lse_kernel"}[name]
     lines = [f"# rocprofv3 summary: {name}", ""]
     trace = os.path.join(trace_dir, "trace", "run_kernel_trace.csv")
     avg_ns = None
@@ -126,7 +128,8 @@ def summarize(name, trace_dir, out):
             lines.append(f"| {short} | {wg} | {len(d)} | {sum(d) / len(d) / 1e3:.1f} | "
                          f"{min(d) / 1e3:.1f} | {max(d) / 1e3:.1f} |")
         want = {"fwd": ("attn_fwd", 2048), "fwd_causal": ("attn_fwd", 4096),
-                "softmax": ("softmax_rows", None), "decode": ("decode_split", None)}[name]
+                "softmax": ("softmax_rows", None), "decode": ("decode_split", None),
+                "merge_lse": ("merge_lse_kernel", None)}[name]
         for (short, wg), d in groups.items():
             if want[0] in short and (want[1] is None or wg == want[1]):
                 avg_ns = sum(d) / len(d)
@@ -181,7 +184,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", choices=["softmax", "fwd", "fwd_causal", "decode"], default=None,
+    ap.add_argument("--only", choices=["softmax", "fwd", "fwd_causal", "decode", "merge_lse"], default=None,
                     help="run one operation only (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -196,7 +199,7 @@ def main():
         return summarize(*args.summarize)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by batch/head with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(attention shards by batch and head with no exchange between GPUs)", file=sys.stderr)
         return 2
 
     import torch
@@ -205,7 +208,7 @@ def main():
 
     osm.load_library()
     torch.cuda.set_device(0)
-    names = ["softmax", "fwd", "fwd_causal", "decode"] if args.only is None else [args.only]
+    names = ["softmax", "fwd", "fwd_causal", "decode", "merge_lse"] if args.only is None else [args.only]
     calls, work = {}, {}
 
     if "softmax" in names:
@@ -261,6 +264,19 @@ def main():
         work["decode"] = ("hbm", kv + io + partials, "B16 Hq32 Hkv8 d128, L_b U[4096,32768], split 256")
         del inp5
 
+    if "merge_lse" in names:
+        log("inputs: merge_lse 8 pieces x 524288 rows x d128 bf16")
+        S6, R6, D6 = 8, 4 * 32 * 4096, 128
+        o6, l6 = inputs.lse_parts(S6, R6, D6, inputs.SEED_BASE + 6, dtype="bf16")
+        op6 = bf16_dev(o6, torch)
+        lp6 = torch.from_numpy(l6).to("cuda")
+        del o6, l6
+        out6 = torch.empty((R6, D6), dtype=torch.bfloat16, device="cuda")
+        lse6 = torch.empty(R6, dtype=torch.float32, device="cuda")
+        calls["merge_lse"] = lambda: osm.merge_lse(op6, lp6, out=out6, lse=lse6)
+        work["merge_lse"] = ("hbm", float(S6 * R6 * (D6 * 2 + 4) + R6 * (D6 * 2 + 4)),
+                             "8 pieces of the B4 H32 N4096 d128 output (524288 rows), bf16")
+
     if args.copy_calibration:
         n = args.copy_calibration * 1024 * 1024 // 4
         csrc = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -311,7 +327,7 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": f"attn_fwd {hc['workload']}" if head == "fwd" else hc["workload"],
                       "step": "softmax_rows + attn_fwd (non-causal) + attn_fwd (causal varlen) "
-                              "+ attn_decode_splitkv" if args.only is None else args.only,
+                              "+ attn_decode_splitkv + merge_lse" if args.only is None else args.only,
                       "global_batch": 4, "seq_len": 4096, "parallelism": "none (1 GPU)"},
            "roofline": roofline, "components": comps}
     if not args.no_cpu_baseline and args.only is None:

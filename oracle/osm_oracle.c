@@ -16,7 +16,7 @@
  *   [P2] "Online softmax" (guide.dupenodi.dev, inference guide)
  *   [P3] "Online softmax" (zerotofrontier.app, efficient-attention chapter)
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - A row with no unmasked score (all -inf, or zero length) gives output 0,
  *     maximum -inf and sum 0; for attention, O = 0 and LSE = -inf.
  *     ([P3] "Precision, and what can still go wrong": a fully masked row ends
