@@ -9,13 +9,15 @@
 // already divided by its own sum.  The merge is associative, so S pieces
 // combine at once: lse = M + log sum_s e^(lse_s - M) with M = max_s lse_s,
 // o = sum_s e^(lse_s - lse) o_s.  A piece with lse = -inf is the empty set:
-// it drops out and its o is never read (it may hold any bits).
+// it drops out whatever its o holds (any bits, NaN included).
 //
-// One wavefront per row.  Pass 1 spreads the pieces over the lanes for the
-// maximum and the sum of exponentials (wave reductions); pass 2 walks the
-// pieces with the row's weights, each lane owning VEC consecutive dims per
-// 64 * VEC-dim chunk, so every load of a piece row is one contiguous run.
-// fp32 accumulation; exponentials with the accurate exp_acc.
+// Rows of a power-of-two number of 16-byte vectors (head_dim 128 in bf16,
+// for example) take merge_lse_rows: a row per group of lanes, several rows
+// per wave, the loads of eight pieces in flight together.  Other head_dims
+// take merge_lse_kernel: one wavefront per row, the pieces spread over the
+// lanes for the maximum and the sum (wave reductions), then walked with the
+// row's weights, each lane owning VEC consecutive dims per 64 * VEC-dim
+// chunk.  fp32 accumulation; exponentials with the accurate exp_acc.
 #include "osm_device.h"
 #include "osm_internal.h"
 
@@ -105,7 +107,7 @@ merge_lse_kernel(const TI *__restrict__ op, const float *__restrict__ lp, int64_
         const TI *base = op + r * hd;
         for (int s = 0; s < S; ++s) {
             const float l = lp[(int64_t)s * rows + r];   // the same for every lane
-            if (l == kNegInf) continue;                  // empty piece: o_s unread
+            if (l == kNegInf) continue;                  // empty piece: o_s not read
             const float w = exp_acc(l - L);
             const TI *prow = base + (int64_t)s * part_stride;
 #pragma unroll
@@ -135,6 +137,95 @@ merge_lse_kernel(const TI *__restrict__ op, const float *__restrict__ lp, int64_
     }
 }
 
+// Fast path: each row is LPR lanes x 16 bytes of o (VE elements per lane),
+// 64 / LPR rows per wave.  Pieces go in batches of 8: their lse values are
+// read by every lane of the row (one cache line), their o vectors are all
+// requested before any is used.  An empty piece gets weight 0 through a
+// select, so whatever its o holds (NaN included) never reaches the sum.
+template <typename TI, typename TO, int LPR>
+__global__ void __launch_bounds__(MLSE_THREADS)
+merge_lse_rows(const TI *__restrict__ op, const float *__restrict__ lp, int64_t rows, int S,
+               TO *__restrict__ o, float *__restrict__ lse) {
+    constexpr int VE = 16 / sizeof(TI);          // elements per lane
+    constexpr int HD = LPR * VE;                 // head_dim
+    constexpr int RPW = 64 / LPR;                // rows per wave
+    constexpr int BATCH = 8;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int sub = lane / LPR, part = lane % LPR;
+    const int64_t part_stride = rows * HD;
+    const int64_t step = (int64_t)gridDim.x * MLSE_WAVES * RPW;
+    for (int64_t r0 = ((int64_t)blockIdx.x * MLSE_WAVES + wave) * RPW; r0 < rows; r0 += step) {
+        const int64_t r = r0 + sub;
+        const bool live = r < rows;
+        const int64_t rc = live ? r : rows - 1;  // rows past the end read the last row, write nothing
+        // ---- pass 1: M = max lse_s, then L = M + log sum_s e^(lse_s - M) ----
+        float mx = kNegInf;
+        for (int s0 = 0; s0 < S; s0 += BATCH) {
+            float l[BATCH];
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k) l[k] = (s0 + k < S) ? lp[(int64_t)(s0 + k) * rows + rc] : kNegInf;
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k) mx = fmaxf(mx, l[k]);
+        }
+        float sum = 0.0f;
+        if (mx != kNegInf)
+            for (int s0 = 0; s0 < S; s0 += BATCH) {
+                float l[BATCH];
+#pragma unroll
+                for (int k = 0; k < BATCH; ++k) l[k] = (s0 + k < S) ? lp[(int64_t)(s0 + k) * rows + rc] : kNegInf;
+#pragma unroll
+                for (int k = 0; k < BATCH; ++k) sum += (l[k] == kNegInf) ? 0.0f : exp_acc(l[k] - mx);
+            }
+        const float L = (mx == kNegInf) ? kNegInf : mx + logf(sum);
+        // ---- pass 2: o = sum_s e^(lse_s - L) o_s ----------------------------
+        float acc[VE];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[e] = 0.0f;
+        const TI *base = op + rc * HD + part * VE;
+        if (mx != kNegInf)
+            for (int s0 = 0; s0 < S; s0 += BATCH) {
+                float w[BATCH];
+                uint4 x[BATCH];
+#pragma unroll
+                for (int k = 0; k < BATCH; ++k) {
+                    const int sk = (s0 + k < S) ? s0 + k : S - 1;
+                    x[k] = *reinterpret_cast<const uint4 *>(base + (int64_t)sk * part_stride);
+                }
+#pragma unroll
+                for (int k = 0; k < BATCH; ++k) {
+                    const float l = (s0 + k < S) ? lp[(int64_t)(s0 + k) * rows + rc] : kNegInf;
+                    w[k] = (l == kNegInf) ? 0.0f : exp_acc(l - L);
+                }
+#pragma unroll
+                for (int k = 0; k < BATCH; ++k) {
+                    float v[VE];
+                    if constexpr (sizeof(TI) == 2) {
+                        const uint32_t q[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            v[2 * e] = bf16_lo(q[e]);
+                            v[2 * e + 1] = bf16_hi(q[e]);
+                        }
+                    } else {
+                        v[0] = __uint_as_float(x[k].x);
+                        v[1] = __uint_as_float(x[k].y);
+                        v[2] = __uint_as_float(x[k].z);
+                        v[3] = __uint_as_float(x[k].w);
+                    }
+#pragma unroll
+                    for (int e = 0; e < VE; ++e) acc[e] = (w[k] == 0.0f) ? acc[e] : fmaf(w[k], v[e], acc[e]);
+                }
+            }
+        if (live) {
+            TO *orow = o + r * HD + part * VE;
+#pragma unroll
+            for (int e = 0; e < VE; e += 2) Elem<TO>::put2(orow + e, acc[e], acc[e + 1]);
+            if (lse && part == 0) lse[r] = L;
+        }
+    }
+}
+
 template <typename TI, typename TO, int VEC>
 hipError_t launch_typed(const MergeLseArgs &a, hipStream_t s, int grid) {
     const int nk = (a.head_dim + 64 * VEC - 1) / (64 * VEC);
@@ -153,6 +244,30 @@ hipError_t launch_typed(const MergeLseArgs &a, hipStream_t s, int grid) {
 
 template <typename TI, typename TO>
 hipError_t launch_vec(const MergeLseArgs &a, hipStream_t s, int grid) {
+    // fast path when a row is a power-of-two number (<= 64) of 16-byte vectors
+    constexpr int VE = 16 / sizeof(TI);
+    const int lpr = a.head_dim / VE;
+    if (a.head_dim % VE == 0 && lpr <= 64 && (lpr & (lpr - 1)) == 0) {
+        const int rpw = 64 / lpr;
+        const int64_t want = (a.rows + (int64_t)MLSE_WAVES * rpw - 1) / ((int64_t)MLSE_WAVES * rpw);
+        const int g = (int)(want < 65536 ? want : 65536);
+        const TI *op = static_cast<const TI *>(a.o_parts);
+        TO *o = static_cast<TO *>(a.o);
+#define OSM_MLSE_ROWS(N)                                                                              \
+    hipLaunchKernelGGL((merge_lse_rows<TI, TO, N>), dim3(g), dim3(MLSE_THREADS), 0, s, op, a.lse_parts, \
+                       a.rows, a.num_parts, o, a.lse)
+        switch (lpr) {
+        case 1: OSM_MLSE_ROWS(1); break;
+        case 2: OSM_MLSE_ROWS(2); break;
+        case 4: OSM_MLSE_ROWS(4); break;
+        case 8: OSM_MLSE_ROWS(8); break;
+        case 16: OSM_MLSE_ROWS(16); break;
+        case 32: OSM_MLSE_ROWS(32); break;
+        default: OSM_MLSE_ROWS(64); break;
+        }
+#undef OSM_MLSE_ROWS
+        return hipGetLastError();
+    }
     return (a.head_dim % 2 == 0) ? launch_typed<TI, TO, 2>(a, s, grid) : launch_typed<TI, TO, 1>(a, s, grid);
 }
 

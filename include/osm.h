@@ -210,8 +210,8 @@ osm_status osm_merge_partials(const float *part_m, const float *part_l, const fl
  * normalized output o_s and its log-sum-exp lse_s; the union has
  * lse = log sum_s e^lse_s (computed as M + log sum_s e^(lse_s - M),
  * M = max_s lse_s) and o = sum_s e^(lse_s - lse) o_s.  A piece with
- * lse_s = -inf is the empty set: it drops out and its o_s is never read
- * (it may hold any bits).
+ * lse_s = -inf is the empty set: it drops out whatever its o_s holds (any
+ * bits, NaN included; the memory must still be valid).
  *
  *   o_parts    [num_parts][rows][head_dim] (in_dtype)
  *   lse_parts  fp32 [num_parts][rows], natural log; each entry finite or -inf

@@ -35,7 +35,8 @@ def run(o_parts, lse_parts, in_dtype, out_dtype):
 @pytest.mark.parametrize("S,rows,d,it,ot", [
     (1, 7, 128, "f32", "f32"), (3, 100, 64, "f32", "f32"), (8, 513, 128, "bf16", "bf16"),
     (70, 33, 96, "f32", "f32"), (5, 40, 37, "f32", "bf16"), (4, 10, 1024, "bf16", "f32"),
-    (2, 9, 511, "f32", "f32"), (6, 300, 128, "bf16", "f32")])
+    (2, 9, 511, "f32", "f32"), (6, 300, 128, "bf16", "f32"), (11, 77, 128, "bf16", "bf16"),
+    (19, 5, 64, "f32", "f32")])
 def test_fold(orc, S, rows, d, it, ot):
     announce(f"merge_lse S{S} rows{rows} d{d} {it}->{ot}")
     o_parts, lse_parts = inputs.lse_parts(S, rows, d, 4000 + S * 7 + d, dtype=it, empty_frac=0.2,
