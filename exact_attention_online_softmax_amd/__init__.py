@@ -28,7 +28,7 @@ OSM_BF16 = 1
 STATUS = {0: "OSM_OK", 1: "OSM_ERR_NULL", 2: "OSM_ERR_SHAPE", 3: "OSM_ERR_UNSUPPORTED",
           4: "OSM_ERR_WORKSPACE", 5: "OSM_ERR_HIP"}
 EXPORTS = ("osm_status_str", "osm_softmax_rows", "osm_attn_fwd", "osm_decode_workspace_bytes",
-           "osm_attn_decode_splitkv", "osm_merge_partials", "osm_merge_lse")
+           "osm_attn_decode_splitkv", "osm_merge_partials", "osm_merge_lse", "osm_attn_extend")
 
 
 class OsmError(RuntimeError):
@@ -61,8 +61,10 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
                                             i32, vp, f32, i32, vp, ctypes.c_size_t, vp]
     lib.osm_merge_partials.argtypes = [vp, vp, vp, i64, i32, i32, vp, ctypes.c_int, vp, vp]
     lib.osm_merge_lse.argtypes = [vp, vp, i64, i32, i32, ctypes.c_int, vp, ctypes.c_int, vp, vp]
+    lib.osm_attn_extend.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32, f32, vp, vp, vp,
+                                    i32, vp, ctypes.c_size_t, vp]
     for name in ("osm_softmax_rows", "osm_attn_fwd", "osm_attn_decode_splitkv",
-                 "osm_merge_partials", "osm_merge_lse"):
+                 "osm_merge_partials", "osm_merge_lse", "osm_attn_extend"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -245,3 +247,45 @@ def merge_lse(o_parts, lse_parts, out_dtype=None, out=None, lse=None):
     _check(lib.osm_merge_lse(_ptr(o_parts), _ptr(lse_parts), rows, S, d, _dtype_code(o_parts.dtype),
                              _ptr(o), _dtype_code(out_dtype), _ptr(lse_t), _stream()))
     return o, lse_t
+
+
+def attn_state(batch, heads_q, head_dim, device="cuda"):
+    """A fresh streaming summary (the empty set): m = -inf, l = 0, O~ = 0,
+    shaped [batch * heads_q], [batch * heads_q], [batch * heads_q, head_dim]."""
+    torch = _torch()
+    rows = batch * heads_q
+    return (torch.full((rows,), float("-inf"), dtype=torch.float32, device=device),
+            torch.zeros(rows, dtype=torch.float32, device=device),
+            torch.zeros((rows, head_dim), dtype=torch.float32, device=device))
+
+
+def attn_extend(q, k_new, v_new, state, *, scale=None, split_size=256, workspace=None):
+    """Fold new keys k_new, v_new [B, Hkv, n, d] into the streaming summary
+    `state` = (m, l, O~) of the queries q [B, Hq, d], in place."""
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new)):
+        _device_tensor(t, name, (torch.float32, torch.bfloat16))
+    sm, sl, so = state
+    for name, t in (("state_m", sm), ("state_l", sl), ("state_o", so)):
+        _device_tensor(t, name, (torch.float32,))
+    B, Hq, d = q.shape
+    _, Hkv, n, _ = k_new.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nbytes = decode_workspace_bytes(B, Hq, max(n, 1), d, split_size)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.osm_attn_extend(_ptr(q), _ptr(k_new), _ptr(v_new), _dtype_code(q.dtype), B, Hq, Hkv, n, d,
+                               float(scale), _ptr(sm), _ptr(sl), _ptr(so), int(split_size),
+                               _ptr(workspace), workspace.numel(), _stream()))
+    return state
+
+
+def attn_state_finalize(state, out_dtype=None):
+    """o = O~ / l and LSE = m + log l of a streaming summary (the state is
+    not modified)."""
+    torch = _torch()
+    sm, sl, so = state
+    rows, d = so.shape
+    return merge_partials(sm.reshape(rows, 1), sl.reshape(rows, 1), so.reshape(rows, 1, d), out_dtype=out_dtype)

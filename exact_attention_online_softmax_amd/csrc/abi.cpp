@@ -110,6 +110,43 @@ osm_status osm_merge_partials(const float *part_m, const float *part_l, const fl
     return hip_status(osm::launch_merge_partials(m, static_cast<hipStream_t>(stream)));
 }
 
+osm_status osm_attn_extend(const void *q, const void *k_new, const void *v_new, osm_dtype dtype,
+                           int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t n_new,
+                           int32_t head_dim, float scale, float *state_m, float *state_l,
+                           float *state_o, int32_t split_size, void *workspace,
+                           size_t workspace_bytes, osm_stream stream) {
+    if (batch < 1 || heads_q < 1 || heads_kv < 1 || n_new < 0 || head_dim < 1 ||
+        heads_q % heads_kv != 0 || !(scale > 0.0f) || !isfinite(scale) || split_size < 1)
+        return OSM_ERR_SHAPE;
+    const int group = heads_q / heads_kv;
+    if ((dtype != OSM_F32 && dtype != OSM_BF16) || (head_dim != 64 && head_dim != 128) ||
+        (group != 1 && group != 2 && group != 4 && group != 8) || split_size % 64 != 0 ||
+        split_size > 8192 || (int64_t)group * split_size > kMaxDecodeScores)
+        return OSM_ERR_UNSUPPORTED;
+    if (!state_m || !state_l || !state_o) return OSM_ERR_NULL;
+    if (n_new == 0) return OSM_OK;                 // no new keys: the state is already the answer
+    if (!q || !k_new || !v_new) return OSM_ERR_NULL;
+    const osm::DecodeLayout lay = osm::decode_layout(batch, heads_q, n_new, head_dim, split_size);
+    if (!workspace || workspace_bytes < lay.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
+        return OSM_ERR_WORKSPACE;
+    // the new keys' pieces, summarized as in the split decode (every key valid)
+    osm::DecodeArgs a{q, k_new, v_new, nullptr, nullptr, dtype == OSM_BF16 ? 1 : 0, batch, heads_q,
+                      heads_kv, n_new, head_dim, nullptr, scale, split_size, workspace};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = osm::launch_decode_split(a, lay, s);
+    if (e != hipSuccess) return OSM_ERR_HIP;
+    // merged with the persisted summary, back into it
+    const char *ws = static_cast<const char *>(workspace);
+    osm::MergeArgs m{reinterpret_cast<const float *>(ws + lay.off_m),
+                     reinterpret_cast<const float *>(ws + lay.off_l),
+                     reinterpret_cast<const float *>(ws + lay.off_o),
+                     lay.rows, lay.chunks, head_dim, nullptr, 0, nullptr};
+    m.state_m = state_m;
+    m.state_l = state_l;
+    m.state_o = state_o;
+    return hip_status(osm::launch_merge_partials(m, s));
+}
+
 osm_status osm_merge_lse(const void *o_parts, const float *lse_parts, int64_t rows,
                          int32_t num_parts, int32_t head_dim, osm_dtype in_dtype, void *o,
                          osm_dtype out_dtype, float *lse, osm_stream stream) {

@@ -111,7 +111,7 @@ decode_split(const T *__restrict__ Q, const T *__restrict__ K, const T *__restri
     __shared__ float stat_m[G], stat_l[G];
 
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int L = __builtin_amdgcn_readfirstlane(clampi(seqlens_k[b], 0, Lmax));
+    const int L = __builtin_amdgcn_readfirstlane(seqlens_k ? clampi(seqlens_k[b], 0, Lmax) : Lmax);
     const int start = c * split;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -240,11 +240,15 @@ decode_split(const T *__restrict__ Q, const T *__restrict__ K, const T *__restri
 constexpr int MRG_THREADS = 256;
 constexpr int MRG_WAVES = MRG_THREADS / 64;
 
-template <int NDL>
+// STATE: the row's persisted summary (state_m, state_l, state_o) is one more
+// piece of the merge, and the merged summary is written back to it
+// unnormalized (the streaming extend) instead of o and LSE.
+template <int NDL, bool STATE>
 __global__ void __launch_bounds__(MRG_THREADS)
 merge_partials_kernel(const float *__restrict__ pm, const float *__restrict__ pl,
                       const float *__restrict__ po, int64_t rows, int C, int HD,
-                      void *__restrict__ out, int out_bf16, float *__restrict__ lse) {
+                      void *__restrict__ out, int out_bf16, float *__restrict__ lse,
+                      float *state_m, float *state_l, float *state_o) {
     __shared__ float red_acc[MRG_WAVES][NDL * 64];
     __shared__ float red_s[MRG_WAVES];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -262,7 +266,8 @@ merge_partials_kernel(const float *__restrict__ pm, const float *__restrict__ pl
 #pragma unroll
         for (int w = 0; w < MRG_WAVES; ++w) mx = fmaxf(mx, red_s[w]);
         __syncthreads();
-        const float m = mx;
+        const float ms = STATE ? state_m[r] : kNegInf;
+        const float m = fmaxf(mx, ms);
         float acc[NDL];
 #pragma unroll
         for (int k = 0; k < NDL; ++k) acc[k] = 0.0f;
@@ -295,6 +300,14 @@ merge_partials_kernel(const float *__restrict__ pm, const float *__restrict__ pl
                 }
             }
         }
+        if (STATE && wave == 0 && ms != kNegInf) {
+            // the persisted summary, weighted like any other piece
+            const float w = exp_acc(ms - m);
+            lsum = fmaf(w, state_l[r], lsum);
+#pragma unroll
+            for (int k = 0; k < NDL; ++k)
+                if (lane + 64 * k < HD) acc[k] = fmaf(w, state_o[r * HD + lane + 64 * k], acc[k]);
+        }
 #pragma unroll
         for (int k = 0; k < NDL; ++k) red_acc[wave][lane + 64 * k] = acc[k];
         if (lane == 0) red_s[wave] = lsum;
@@ -302,6 +315,22 @@ merge_partials_kernel(const float *__restrict__ pm, const float *__restrict__ pl
         float l = 0.0f;
 #pragma unroll
         for (int w = 0; w < MRG_WAVES; ++w) l += red_s[w];
+        if (STATE) {
+            // write the merged (m, l, O~) back; every read of this row's
+            // state happened before the barrier above
+            for (int d = tid; d < HD; d += MRG_THREADS) {
+                float o = 0.0f;
+#pragma unroll
+                for (int w = 0; w < MRG_WAVES; ++w) o += red_acc[w][d];
+                state_o[r * HD + d] = (m == kNegInf) ? 0.0f : o;
+            }
+            if (tid == 0) {
+                state_m[r] = m;
+                state_l[r] = (m == kNegInf) ? 0.0f : l;
+            }
+            __syncthreads();   // red_acc / red_s are reused by the next row
+            continue;
+        }
         const bool valid = (m != kNegInf) && (l > 0.0f);
         const float inv = valid ? 1.0f / l : 0.0f;
         for (int d = tid; d < HD; d += MRG_THREADS) {
@@ -370,14 +399,18 @@ hipError_t launch_merge_partials(const MergeArgs &a, hipStream_t s) {
     if (a.rows == 0) return hipSuccess;
     const int grid = (int)(a.rows < 1048576 ? a.rows : 1048576);
     const int ndl = (a.head_dim + 63) / 64;
-#define OSM_MERGE_LAUNCH(N)                                                                     \
-    hipLaunchKernelGGL(merge_partials_kernel<N>, dim3(grid), dim3(MRG_THREADS), 0, s, a.part_m, \
-                       a.part_l, a.part_o, a.rows, a.num_splits, a.head_dim, a.o, a.out_dtype,  \
-                       a.lse)
-    if (ndl <= 1) OSM_MERGE_LAUNCH(1);
-    else if (ndl <= 2) OSM_MERGE_LAUNCH(2);
-    else if (ndl <= 4) OSM_MERGE_LAUNCH(4);
-    else OSM_MERGE_LAUNCH(8);
+    const bool st = a.state_m != nullptr;
+#define OSM_MERGE_LAUNCH(N, ST)                                                                        \
+    hipLaunchKernelGGL((merge_partials_kernel<N, ST>), dim3(grid), dim3(MRG_THREADS), 0, s, a.part_m,  \
+                       a.part_l, a.part_o, a.rows, a.num_splits, a.head_dim, a.o, a.out_dtype, a.lse, \
+                       a.state_m, a.state_l, a.state_o)
+    if (st) {
+        if (ndl <= 1) OSM_MERGE_LAUNCH(1, true);
+        else OSM_MERGE_LAUNCH(2, true);
+    } else if (ndl <= 1) OSM_MERGE_LAUNCH(1, false);
+    else if (ndl <= 2) OSM_MERGE_LAUNCH(2, false);
+    else if (ndl <= 4) OSM_MERGE_LAUNCH(4, false);
+    else OSM_MERGE_LAUNCH(8, false);
 #undef OSM_MERGE_LAUNCH
     return hipGetLastError();
 }

@@ -65,6 +65,9 @@ struct MergeArgs {
     void *o;
     int out_dtype;       // 0 f32, 1 bf16
     float *lse;
+    // streaming extend: when set, the persisted summary [rows], [rows],
+    // [rows][head_dim] joins the merge and receives the result (o, lse unused)
+    float *state_m = nullptr, *state_l = nullptr, *state_o = nullptr;
 };
 hipError_t launch_merge_partials(const MergeArgs &a, hipStream_t s);
 

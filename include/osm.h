@@ -202,6 +202,45 @@ osm_status osm_merge_partials(const float *part_m, const float *part_l, const fl
                               osm_dtype out_dtype, float *lse, osm_stream stream);
 
 /*
+ * osm_attn_extend -- streaming attention: fold a chunk of newly arrived keys
+ * into a persisted per-row online-softmax summary.
+ *
+ * [P1] "How does this connect to KV-cache decoding?": as keys arrive, the
+ * running state of one query is carried forward instead of recomputing over
+ * the whole cache.  [P3] "Merging partial results": a row's summary
+ * (m, l, O~) -- maximum of the scaled scores seen so far, sum of
+ * e^(s - m), and sum of e^(s - m) v -- merges with the summary of the new
+ * keys exactly (the recurrence over one more block is this merge); the
+ * empty set (-inf, 0, 0) is the identity, so a fresh stream starts there.
+ * The new keys are split into pieces of split_size, summarized as in
+ * osm_attn_decode_splitkv, and merged with the state in place.  To read the
+ * result, call osm_merge_partials(state_m, state_l, state_o, rows, 1, ...)
+ * (o = O~ / l, LSE = m + log l), which leaves the state untouched.
+ *
+ *   q        [batch][heads_q][head_dim]            (dtype)
+ *   k_new, v_new  [batch][heads_kv][n_new][head_dim] (dtype), all keys valid
+ *   state_m  fp32 [batch * heads_q]  (read and written; natural-log units
+ *            of the scaled scores; -inf for an empty stream)
+ *   state_l  fp32 [batch * heads_q]  (read and written; 0 for an empty stream)
+ *   state_o  fp32 [batch * heads_q][head_dim]  (read and written; unnormalized)
+ *   scale    multiplies q . k; finite, > 0.
+ *   split_size, workspace  as for osm_attn_decode_splitkv, with
+ *            osm_decode_workspace_bytes(batch, heads_q, n_new, head_dim, split_size).
+ * n_new == 0 leaves the state as it is (and q, k_new, v_new may be NULL).
+ * Two kernels are enqueued on `stream`; calls that update the same state
+ * must be ordered on one stream.
+ * Supported: dtype OSM_F32 or OSM_BF16; head_dim 64 or 128;
+ * heads_q / heads_kv in {1, 2, 4, 8}.
+ * Errors: OSM_ERR_NULL, OSM_ERR_SHAPE, OSM_ERR_UNSUPPORTED,
+ * OSM_ERR_WORKSPACE, OSM_ERR_HIP.
+ */
+osm_status osm_attn_extend(const void *q, const void *k_new, const void *v_new, osm_dtype dtype,
+                           int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t n_new,
+                           int32_t head_dim, float scale, float *state_m, float *state_l,
+                           float *state_o, int32_t split_size, void *workspace,
+                           size_t workspace_bytes, osm_stream stream);
+
+/*
  * osm_merge_lse -- combine normalized attention results of disjoint key
  * sets (for example separate osm_attn_fwd calls over chunks of the keys)
  * into the result over their union.

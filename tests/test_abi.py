@@ -146,6 +146,28 @@ def test_merge_lse_validation(lib):
 
 
 @no_gpu_only
+def test_extend_validation(lib):
+    ws_ok = lib.osm_decode_workspace_bytes(1, 2, 100, 128, 64)
+    def call(q=FAKE, k=FAKE, v=FAKE, dt=osm.OSM_BF16, B=1, Hq=2, Hkv=1, n=100, d=128, scale=0.1,
+             sm=FAKE, sl=FAKE, so=FAKE, split=64, ws=FAKE, wsb=ws_ok):
+        return lib.osm_attn_extend(q, k, v, dt, B, Hq, Hkv, n, d, scale, sm, sl, so, split, ws, wsb, None)
+    assert call(B=0) == 2
+    assert call(n=-1) == 2
+    assert call(Hq=3, Hkv=2) == 2
+    assert call(scale=float("nan")) == 2
+    assert call(d=96) == 3
+    assert call(dt=9) == 3
+    assert call(split=100) == 3
+    assert call(Hq=16, Hkv=1) == 3                  # group 16
+    assert call(sm=None) == 1
+    assert call(so=None) == 1
+    assert call(n=0, q=None, k=None, v=None) == 0   # no new keys: nothing to do
+    assert call(q=None) == 1
+    assert call(wsb=ws_ok - 1) == 4
+    assert call(ws=ctypes.c_void_p(0x10004)) == 4    # not 256-byte aligned
+
+
+@no_gpu_only
 def test_no_device_reports_hip_error(lib):
     """A fully valid request in a process without a GPU fails cleanly with
     OSM_ERR_HIP (the launch is refused by the runtime, nothing is read)."""
