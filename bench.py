@@ -11,6 +11,8 @@ inputs already resident in HBM:
                                     (piece summaries + merge)
   merge_lse osm_merge_lse           8 normalized pieces of a 524288-row d=128 bf16 output
                                     (log-sum-exp merge of results over disjoint key sets)
+  extend    osm_attn_extend         bf16 B=16 Hq=32 Hkv=8 d=128, 4096 new keys per call folded
+                                    into a persisted (m, l, O~) state (streaming attention)
 
 Each call is timed with HIP events on the stream it runs on (torch's current
 stream); ``value`` is the headline forward's TFLOP/s.  The CPU oracle is timed
@@ -47,7 +49,7 @@ def bf16_dev(bits, torch):
 
 
 KERNEL_SOURCES = {"fwd": "attn_fwd.hip", "fwd_causal": "attn_fwd.hip", "softmax": "softmax_rows.hip",
-                  "decode": "decode.hip", "merge_lse": "merge_lse.hip"}
+                  "decode": "decode.hip", "merge_lse": "merge_lse.hip", "extend": "decode.hip"}
 
 
 def source_hash(name):
@@ -109,7 +111,7 @@ def summarize(name, trace_dir, out):
     import csv
     import glob
     kern = {"fwd": "attn_fwd", "fwd_causal": "attn_fwd", "softmax": "softmax_rows",
-            "decode": "decode_split", "merge_lse": "merge_lse_kernel"}[name]
+            "decode": "decode_split", "merge_lse": "merge_lse_kernel", "extend": "decode_split"}[name]
     lines = [f"# rocprofv3 summary: {name}", ""]
     trace = os.path.join(trace_dir, "trace", "run_kernel_trace.csv")
     avg_ns = None
@@ -129,7 +131,7 @@ def summarize(name, trace_dir, out):
                          f"{min(d) / 1e3:.1f} | {max(d) / 1e3:.1f} |")
         want = {"fwd": ("attn_fwd", 2048), "fwd_causal": ("attn_fwd", 4096),
                 "softmax": ("softmax_rows", None), "decode": ("decode_split", None),
-                "merge_lse": ("merge_lse_kernel", None)}[name]
+                "merge_lse": ("merge_lse_kernel", None), "extend": ("decode_split", None)}[name]
         for (short, wg), d in groups.items():
             if want[0] in short and (want[1] is None or wg == want[1]):
                 avg_ns = sum(d) / len(d)
@@ -184,7 +186,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", choices=["softmax", "fwd", "fwd_causal", "decode", "merge_lse"], default=None,
+    ap.add_argument("--only", choices=["softmax", "fwd", "fwd_causal", "decode", "merge_lse", "extend"],
+                    default=None,
                     help="run one operation only (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -208,7 +211,8 @@ def main():
 
     osm.load_library()
     torch.cuda.set_device(0)
-    names = ["softmax", "fwd", "fwd_causal", "decode", "merge_lse"] if args.only is None else [args.only]
+    names = (["softmax", "fwd", "fwd_causal", "decode", "merge_lse", "extend"] if args.only is None
+             else [args.only])
     calls, work = {}, {}
 
     if "softmax" in names:
@@ -277,6 +281,23 @@ def main():
         work["merge_lse"] = ("hbm", float(S6 * R6 * (D6 * 2 + 4) + R6 * (D6 * 2 + 4)),
                              "8 pieces of the B4 H32 N4096 d128 output (524288 rows), bf16")
 
+    if "extend" in names:
+        log("inputs: extend B16 Hq32 Hkv8 d128 bf16, 4096 new keys per call")
+        B7, Hq7, Hkv7, N7, D7 = 16, 32, 8, 4096, 128
+        inp7 = inputs.attention_inputs(B7, Hq7, Hkv7, 1, N7, D7, inputs.SEED_BASE + 7)
+        q7 = bf16_dev(inp7.q[:, :, 0, :], torch)
+        k7, v7 = bf16_dev(inp7.k, torch), bf16_dev(inp7.v, torch)
+        state7 = osm.attn_state(B7, Hq7, D7)
+        ws7 = torch.empty(osm.decode_workspace_bytes(B7, Hq7, N7, D7, 256), dtype=torch.uint8, device="cuda")
+        scale7 = inp7.scale
+        del inp7
+        calls["extend"] = lambda: osm.attn_extend(q7, k7, v7, state7, scale=scale7, split_size=256,
+                                                  workspace=ws7)
+        pieces7 = N7 // 256
+        work["extend"] = ("hbm", float(B7 * Hkv7 * N7 * D7 * 2 * 2 + B7 * Hq7 * D7 * 2
+                                       + 2 * B7 * Hq7 * (D7 + 2) * 4 + 2 * B7 * Hq7 * pieces7 * (D7 + 2) * 4),
+                          "B16 Hq32 Hkv8 d128 bf16, 4096 new keys folded into a persisted state")
+
     if args.copy_calibration:
         n = args.copy_calibration * 1024 * 1024 // 4
         csrc = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -327,7 +348,8 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": f"attn_fwd {hc['workload']}" if head == "fwd" else hc["workload"],
                       "step": "softmax_rows + attn_fwd (non-causal) + attn_fwd (causal varlen) "
-                              "+ attn_decode_splitkv + merge_lse" if args.only is None else args.only,
+                              "+ attn_decode_splitkv + merge_lse + attn_extend" if args.only is None
+                              else args.only,
                       "global_batch": 4, "seq_len": 4096, "parallelism": "none (1 GPU)"},
            "roofline": roofline, "components": comps}
     if not args.no_cpu_baseline and args.only is None:
