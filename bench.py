@@ -111,7 +111,7 @@ def summarize(name, trace_dir, out):
     import csv
     import glob
     kern = {"fwd": "attn_fwd", "fwd_causal": "attn_fwd", "softmax": "softmax_rows",
-            "decode": "decode_split", "merge_lse": "merge_lse_kernel", "extend": "decode_split"}[name]
+            "decode": "decode_split", "merge_lse": "merge_lse", "extend": "decode_split"}[name]
     lines = [f"# rocprofv3 summary: {name}", ""]
     trace = os.path.join(trace_dir, "trace", "run_kernel_trace.csv")
     avg_ns = None
@@ -131,7 +131,7 @@ def summarize(name, trace_dir, out):
                          f"{min(d) / 1e3:.1f} | {max(d) / 1e3:.1f} |")
         want = {"fwd": ("attn_fwd", 2048), "fwd_causal": ("attn_fwd", 4096),
                 "softmax": ("softmax_rows", None), "decode": ("decode_split", None),
-                "merge_lse": ("merge_lse_kernel", None), "extend": ("decode_split", None)}[name]
+                "merge_lse": ("merge_lse", None), "extend": ("decode_split", None)}[name]
         for (short, wg), d in groups.items():
             if want[0] in short and (want[1] is None or wg == want[1]):
                 avg_ns = sum(d) / len(d)
