@@ -15,6 +15,8 @@ and brute force):
 * ``merge``              the merge of partial triples, then o = o~/l
 * ``attention``          naive attention materializing each score row
 * ``merge_lse``          the log-sum-exp form of the merge
+* ``attention_bwd``      gradients of naive attention (chain rule through the
+                         forward definition; the pages print no backward)
 """
 from __future__ import annotations
 
@@ -70,8 +72,12 @@ class Oracle:
                                          vp, vp, ctypes.c_double, ctypes.c_int, vp, i64,
                                          _f64p, _f64p]
         lib.oracle_merge_lse.argtypes = [_f64p, _f64p, _f64p, _f64p, i64, i64, _f64p, _f64p]
+        lib.oracle_attention_bwd.argtypes = [_f32p, _f32p, _f32p, _f32p, i64, i64, i64, i64, i64,
+                                             i64, vp, vp, ctypes.c_double, ctypes.c_int,
+                                             _f64p, _f64p, _f64p]
         for f in (lib.oracle_softmax_rows, lib.oracle_online_normalizer, lib.oracle_summary,
-                  lib.oracle_merge, lib.oracle_attention, lib.oracle_merge_lse):
+                  lib.oracle_merge, lib.oracle_attention, lib.oracle_merge_lse,
+                  lib.oracle_attention_bwd):
             f.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -170,6 +176,31 @@ class Oracle:
         if self.lib.oracle_merge_lse(o_a, lse_a, o_b, lse_b, rows, d, o, lse):
             raise RuntimeError("oracle_merge_lse failed")
         return o, lse
+
+
+    def attention_bwd(self, q, k, v, dout, *, scale, causal=False, seqlens_q=None,
+                      seqlens_k=None):
+        """Gradients (dq, dk, dv) in fp64 of attention(q, k, v) against the
+        output gradient ``dout`` [B, Hq, Nq, d]; shapes as ``attention``."""
+        q = np.ascontiguousarray(q, dtype=np.float32)
+        k = np.ascontiguousarray(k, dtype=np.float32)
+        v = np.ascontiguousarray(v, dtype=np.float32)
+        dout = np.ascontiguousarray(dout, dtype=np.float32)
+        B, Hq, Nq, d = q.shape
+        _, Hkv, Nk, _ = k.shape
+        if dout.shape != q.shape:
+            raise ValueError("dout must be shaped like q")
+        sq = _i32_or_null(seqlens_q)
+        sk = _i32_or_null(seqlens_k)
+        dq = np.empty((B, Hq, Nq, d), np.float64)
+        dk = np.empty((B, Hkv, Nk, d), np.float64)
+        dv = np.empty((B, Hkv, Nk, d), np.float64)
+        cv = lambda p: None if p is None else ctypes.cast(p[0], ctypes.c_void_p)
+        rc = self.lib.oracle_attention_bwd(q, k, v, dout, B, Hq, Hkv, Nq, Nk, d, cv(sq), cv(sk),
+                                           float(scale), int(bool(causal)), dq, dk, dv)
+        if rc:
+            raise RuntimeError(f"oracle_attention_bwd failed ({rc})")
+        return dq, dk, dv
 
 
 _default = None

@@ -339,3 +339,104 @@ int oracle_merge_lse(const double *o_a, const double *lse_a, const double *o_b,
     }
     return ORACLE_OK;
 }
+
+/*
+ * oracle_attention_bwd: gradients of naive attention with respect to Q, K
+ * and V, given the gradient dO of the output.  The pages define only the
+ * forward ([P3] "From weights to outputs"; the log-sum-exp paragraph there
+ * notes that lse is what a backward pass keeps to rebuild the weights, as
+ * y_j = exp(s_j - lse)); the gradient is the derivative of that definition,
+ * written out by the chain rule for one query row with visible keys j:
+ *   s_j  = scale * (q . k_j),   y = safe softmax of s,   o = sum_j y_j v_j
+ *   dv_j += y_j * dO                        (o is linear in v_j)
+ *   g_j   = dO . v_j                        (dL/dy_j)
+ *   ds_j  = y_j * (g_j - sum_k y_k g_k)     (the softmax Jacobian
+ *                                            dy_k/ds_j = y_k (delta_kj - y_j))
+ *   dq   += scale * sum_j ds_j k_j,   dk_j += scale * ds_j q
+ * The weights y are the safe softmax of the materialized scores, not rebuilt
+ * from an lse.  Masks, lengths and grouped heads are those of
+ * oracle_attention; a row with no visible key contributes nothing, and
+ * rows past the valid lengths get zero gradients.  dK and dV of a key/value
+ * head sum over the query heads that read it.
+ *
+ * Layouts as oracle_attention; dout [B][Hq][Nq][d] fp32; outputs double:
+ * dq [B][Hq][Nq][d], dk and dv [B][Hkv][Nk][d].
+ */
+int oracle_attention_bwd(const float *q, const float *k, const float *v,
+                         const float *dout, int64_t B, int64_t Hq, int64_t Hkv,
+                         int64_t Nq, int64_t Nk, int64_t d,
+                         const int32_t *seqlens_q, const int32_t *seqlens_k,
+                         double scale, int causal, double *dq, double *dk,
+                         double *dv) {
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || B < 0 || Hq < 1 || Hkv < 1 ||
+        Nq < 0 || Nk < 0 || d < 1 || Hq % Hkv != 0)
+        return ORACLE_ERR_ARG;
+    const int64_t group = Hq / Hkv;
+    int err = ORACLE_OK;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+        double *y = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+        double *gy = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+        if (!s || !y || !gy) {
+#pragma omp atomic write
+            err = ORACLE_ERR_NOMEM;
+        } else {
+            /* one (batch, key/value head) per iteration: it owns its dK, dV
+             * rows and the dQ rows of the query heads that read it */
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t bg = 0; bg < B * Hkv; ++bg) {
+                int64_t b = bg / Hkv, g = bg % Hkv;
+                int64_t Lq = clamp_len(seqlens_q, b, Nq);
+                int64_t Lk = clamp_len(seqlens_k, b, Nk);
+                const float *kh = k + (b * Hkv + g) * Nk * d;
+                const float *vh = v + (b * Hkv + g) * Nk * d;
+                double *dkh = dk + (b * Hkv + g) * Nk * d;
+                double *dvh = dv + (b * Hkv + g) * Nk * d;
+                for (int64_t c = 0; c < Nk * d; ++c) {
+                    dkh[c] = 0.0;
+                    dvh[c] = 0.0;
+                }
+                for (int64_t h = g * group; h < (g + 1) * group; ++h) {
+                    for (int64_t i = 0; i < Nq; ++i) {
+                        const float *qr = q + ((b * Hq + h) * Nq + i) * d;
+                        const float *dor = dout + ((b * Hq + h) * Nq + i) * d;
+                        double *dqr = dq + ((b * Hq + h) * Nq + i) * d;
+                        for (int64_t c = 0; c < d; ++c) dqr[c] = 0.0;
+                        int64_t n_vis = (i < Lq) ? Lk : 0;
+                        if (causal && n_vis > i + 1) n_vis = i + 1;
+                        if (n_vis == 0) continue;
+                        for (int64_t j = 0; j < n_vis; ++j) {   /* scores */
+                            double dot = 0.0;
+                            for (int64_t c = 0; c < d; ++c)
+                                dot += (double)qr[c] * (double)kh[j * d + c];
+                            s[j] = scale * dot;
+                        }
+                        double m, l;
+                        safe_softmax_row(s, n_vis, y, &m, &l);
+                        double yg = 0.0;                         /* sum_k y_k g_k */
+                        for (int64_t j = 0; j < n_vis; ++j) {
+                            double dot = 0.0;
+                            for (int64_t c = 0; c < d; ++c)
+                                dot += (double)dor[c] * (double)vh[j * d + c];
+                            gy[j] = dot;
+                            yg += y[j] * dot;
+                        }
+                        for (int64_t j = 0; j < n_vis; ++j) {
+                            double ds = y[j] * (gy[j] - yg);
+                            for (int64_t c = 0; c < d; ++c) {
+                                dvh[j * d + c] += y[j] * (double)dor[c];
+                                dqr[c] += scale * ds * (double)kh[j * d + c];
+                                dkh[j * d + c] += scale * ds * (double)qr[c];
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        free(s);
+        free(y);
+        free(gy);
+    }
+    return err;
+}

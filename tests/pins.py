@@ -514,4 +514,129 @@ def pin_merge_of_attention_pieces(orc):
     close(lse[0], lse_ref[0, 0, 0], 2e-7, what="pieces lse")
 
 
+# ---------------------------------------------------------------------------
+# backward: the derivative of the forward definition (the pages print none)
+# ---------------------------------------------------------------------------
+_BWD_MASKS = [  # (causal, seqlens_q, seqlens_k) for B = 2
+    (False, None, None),
+    (True, None, None),
+    (True, [5, 3], [7, 4]),
+    (False, [0, 4], [6, 0]),
+]
+
+
+def _dyadic(gen, shape, step=2.0 ** -6, bound=2.0):
+    """Values that are multiples of ``step`` in [-bound, bound): a nudge by a
+    power of two no larger than ``step`` stays exact in fp32."""
+    return (np.round(gen.uniform(-bound, bound, shape) / step) * step).astype(np.float32)
+
+
+def pin_attention_bwd_finite_differences(orc):
+    """Each gradient entry against central differences of the loss
+    L = sum(dO * O) computed by the forward oracle, Richardson-extrapolated
+    (error O(h^4)); inputs are dyadic so every nudged input is exact."""
+    gen = np.random.default_rng(50)
+    B, Hq, Hkv, Nq, Nk, d = 2, 4, 2, 5, 7, 3
+    q = _dyadic(gen, (B, Hq, Nq, d))
+    k = _dyadic(gen, (B, Hkv, Nk, d))
+    v = _dyadic(gen, (B, Hkv, Nk, d))
+    do = _dyadic(gen, (B, Hq, Nq, d))
+    scale = 0.625
+    h = 2.0 ** -9
+    for causal, lq, lk in _BWD_MASKS:
+        sq = None if lq is None else np.array(lq)
+        sk = None if lk is None else np.array(lk)
+
+        def loss(qq, kk, vv):
+            o, _ = orc.attention(qq, kk, vv, scale=scale, causal=causal, seqlens_q=sq,
+                                 seqlens_k=sk)
+            return math.fsum((o * do.astype(np.float64)).ravel())
+
+        dq, dk, dv = orc.attention_bwd(q, k, v, do, scale=scale, causal=causal,
+                                       seqlens_q=sq, seqlens_k=sk)
+        for name, x, g in (("dq", q, dq), ("dk", k, dk), ("dv", v, dv)):
+            fd = np.empty(x.shape)
+            for idx in np.ndindex(x.shape):
+                def central(step):
+                    xp, xm = x.copy(), x.copy()
+                    xp[idx] += step
+                    xm[idx] -= step
+                    args_p = [xp if name == n else y for n, y in (("dq", q), ("dk", k), ("dv", v))]
+                    args_m = [xm if name == n else y for n, y in (("dq", q), ("dk", k), ("dv", v))]
+                    return (loss(*args_p) - loss(*args_m)) / (2 * step)
+                fd[idx] = (4 * central(h / 2) - central(h)) / 3
+            close(g, fd, 1e-7, 1e-9, what=f"{name} causal={causal} lq={lq} lk={lk}")
+
+
+def pin_attention_bwd_autograd(orc):
+    """Against fp64 reverse-mode autodiff (torch, CPU) of a forward written
+    here row by row over the visible keys only."""
+    import torch
+    gen = np.random.default_rng(51)
+    B, Hq, Hkv, Nq, Nk, d = 2, 4, 2, 9, 11, 5
+    group = Hq // Hkv
+    q, k, v = (gen.standard_normal(s).astype(np.float32)
+               for s in ((B, Hq, Nq, d), (B, Hkv, Nk, d), (B, Hkv, Nk, d)))
+    do = gen.standard_normal((B, Hq, Nq, d)).astype(np.float32)
+    scale = 0.41
+    for causal, lq, lk in ((False, [9, 9], [11, 11]), (True, [9, 9], [11, 11]),
+                           (True, [7, 2], [9, 5]), (False, [9, 0], [3, 11])):
+        tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+        tdo = torch.tensor(do, dtype=torch.float64)
+        loss = torch.zeros((), dtype=torch.float64)
+        for b in range(B):
+            for hh in range(Hq):
+                g = hh // group
+                for i in range(min(lq[b], Nq)):
+                    n = min(lk[b], i + 1) if causal else lk[b]
+                    if n == 0:
+                        continue
+                    w = torch.softmax(scale * (tk[b, g, :n] @ tq[b, hh, i]), 0)
+                    loss = loss + torch.dot(w @ tv[b, g, :n], tdo[b, hh, i])
+        loss.backward()
+        dq, dk, dv = orc.attention_bwd(q, k, v, do, scale=scale, causal=causal,
+                                       seqlens_q=np.array(lq), seqlens_k=np.array(lk))
+        for name, got, ref in (("dq", dq, tq.grad), ("dk", dk, tk.grad), ("dv", dv, tv.grad)):
+            close(got, ref.numpy(), 1e-12, 1e-14, what=f"{name} causal={causal} lq={lq} lk={lk}")
+
+
+def pin_attention_bwd_invariants(orc):
+    """Each visible row's score gradients sum to zero (softmax is shift
+    invariant), so the key gradients of a head sum to zero; each visible row's
+    weights sum to one, so the value gradients of a head sum to the output
+    gradients of the rows that see any key; padded rows get exact zeros."""
+    gen = np.random.default_rng(52)
+    B, Hq, Hkv, Nq, Nk, d = 2, 6, 2, 13, 10, 4
+    q, k, v = (gen.standard_normal(s).astype(np.float32)
+               for s in ((B, Hq, Nq, d), (B, Hkv, Nk, d), (B, Hkv, Nk, d)))
+    do = gen.standard_normal((B, Hq, Nq, d)).astype(np.float32)
+    lq, lk = np.array([11, 13]), np.array([10, 6])
+    for causal in (False, True):
+        dq, dk, dv = orc.attention_bwd(q, k, v, do, scale=0.5, causal=causal, seqlens_q=lq,
+                                       seqlens_k=lk)
+        for b in range(B):
+            for g in range(Hkv):
+                close(dk[b, g].sum(0), np.zeros(d), 0, 1e-13, what="sum of dk")
+                seen = [(hh, i) for hh in range(3 * g, 3 * g + 3) for i in range(lq[b])
+                        if (min(lk[b], i + 1) if causal else lk[b]) > 0]
+                want = np.sum([do[b, hh, i].astype(np.float64) for hh, i in seen], 0)
+                close(dv[b, g].sum(0), want, 1e-13, 1e-13, what="sum of dv")
+            assert np.all(dq[b, :, lq[b]:] == 0.0)
+            assert np.all(dk[b, :, lk[b]:] == 0.0) and np.all(dv[b, :, lk[b]:] == 0.0)
+
+
+def pin_attention_bwd_one_key(orc):
+    """One visible key: the weight is 1 whatever the scores, so dq = dk = 0
+    and dv_0 is the sum of the output gradients of every row of the group."""
+    gen = np.random.default_rng(53)
+    q = gen.standard_normal((1, 2, 4, 6)).astype(np.float32)
+    k = gen.standard_normal((1, 1, 1, 6)).astype(np.float32)
+    v = gen.standard_normal((1, 1, 1, 6)).astype(np.float32)
+    do = gen.standard_normal((1, 2, 4, 6)).astype(np.float32)
+    dq, dk, dv = orc.attention_bwd(q, k, v, do, scale=0.9)
+    close(dq, np.zeros_like(dq), 0, 1e-15, what="dq")
+    close(dk, np.zeros_like(dk), 0, 1e-15, what="dk")
+    close(dv[0, 0, 0], do[0].reshape(-1, 6).astype(np.float64).sum(0), 1e-14, 1e-15, what="dv")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

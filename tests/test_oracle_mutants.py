@@ -70,6 +70,32 @@ MUTANTS = [
      "double wa = 0.5, wb = 0.5;"),
     ("lse merge plain max", "double L = mx + log(exp(la - mx) + exp(lb - mx));",
      "double L = mx;"),
+    # backward
+    ("bwd drops the row term", "double ds = y[j] * (gy[j] - yg);", "double ds = y[j] * gy[j];"),
+    ("bwd row term wrong sign", "double ds = y[j] * (gy[j] - yg);",
+     "double ds = y[j] * (gy[j] + yg);"),
+    ("bwd dk unscaled", "dkh[j * d + c] += scale * ds * (double)qr[c];",
+     "dkh[j * d + c] += ds * (double)qr[c];"),
+    ("bwd dq from values", "dqr[c] += scale * ds * (double)kh[j * d + c];",
+     "dqr[c] += scale * ds * (double)vh[j * d + c];"),
+    ("bwd dv weighted by score gradient", "dvh[j * d + c] += y[j] * (double)dor[c];",
+     "dvh[j * d + c] += ds * (double)dor[c];"),
+    ("bwd dL/dy from keys", "dot += (double)dor[c] * (double)vh[j * d + c];",
+     "dot += (double)dor[c] * (double)kh[j * d + c];"),
+    ("bwd causal ignored",
+     "                        if (causal && n_vis > i + 1) n_vis = i + 1;\n"
+     "                        if (n_vis == 0) continue;",
+     "                        if (n_vis == 0) continue;"),
+    ("bwd first head of the group only", "for (int64_t h = g * group; h < (g + 1) * group; ++h)",
+     "for (int64_t h = g * group; h < g * group + 1; ++h)"),
+    ("bwd padded keys enter",
+     "int64_t Lk = clamp_len(seqlens_k, b, Nk);\n                const float *kh",
+     "int64_t Lk = Nk;\n                const float *kh"),
+    ("bwd padded queries enter",
+     "                        int64_t n_vis = (i < Lq) ? Lk : 0;\n"
+     "                        if (causal",
+     "                        int64_t n_vis = Lk;\n"
+     "                        if (causal"),
 ]
 
 
