@@ -13,6 +13,8 @@ inputs already resident in HBM:
                                     (log-sum-exp merge of results over disjoint key sets)
   extend    osm_attn_extend         bf16 B=16 Hq=32 Hkv=8 d=128, 4096 new keys per call folded
                                     into a persisted (m, l, O~) state (streaming attention)
+  bwd       osm_attn_bwd            backward of the fwd workload (dQ, dK, dV from O, LSE, dO)
+  bwd_causal osm_attn_bwd           backward of the fwd_causal workload
 
 Each call is timed with HIP events on the stream it runs on (torch's current
 stream); ``value`` is the headline forward's TFLOP/s.  The CPU oracle is timed
@@ -49,7 +51,9 @@ def bf16_dev(bits, torch):
 
 
 KERNEL_SOURCES = {"fwd": "attn_fwd.hip", "fwd_causal": "attn_fwd.hip", "softmax": "softmax_rows.hip",
-                  "decode": "decode.hip", "merge_lse": "merge_lse.hip", "extend": "decode.hip"}
+                  "decode": "decode.hip", "merge_lse": "merge_lse.hip", "extend": "decode.hip",
+                  "bwd": "attn_bwd.hip", "bwd_causal": "attn_bwd.hip"}
+WORKLOADS = ["softmax", "fwd", "fwd_causal", "decode", "merge_lse", "extend", "bwd", "bwd_causal"]
 
 
 def source_hash(name):
@@ -111,7 +115,8 @@ def summarize(name, trace_dir, out):
     import csv
     import glob
     kern = {"fwd": "attn_fwd", "fwd_causal": "attn_fwd", "softmax": "softmax_rows",
-            "decode": "decode_split", "merge_lse": "merge_lse", "extend": "decode_split"}[name]
+            "decode": "decode_split", "merge_lse": "merge_lse", "extend": "decode_split",
+            "bwd": "attn_bwd_dkdv", "bwd_causal": "attn_bwd_dkdv"}[name]
     lines = [f"# rocprofv3 summary: {name}", ""]
     trace = os.path.join(trace_dir, "trace", "run_kernel_trace.csv")
     avg_ns = None
@@ -131,7 +136,8 @@ def summarize(name, trace_dir, out):
                          f"{min(d) / 1e3:.1f} | {max(d) / 1e3:.1f} |")
         want = {"fwd": ("attn_fwd", 2048), "fwd_causal": ("attn_fwd", 4096),
                 "softmax": ("softmax_rows", None), "decode": ("decode_split", None),
-                "merge_lse": ("merge_lse", None), "extend": ("decode_split", None)}[name]
+                "merge_lse": ("merge_lse", None), "extend": ("decode_split", None),
+                "bwd": ("attn_bwd_dkdv", None), "bwd_causal": ("attn_bwd_dkdv", None)}[name]
         for (short, wg), d in groups.items():
             if want[0] in short and (want[1] is None or wg == want[1]):
                 avg_ns = sum(d) / len(d)
@@ -186,8 +192,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", choices=["softmax", "fwd", "fwd_causal", "decode", "merge_lse", "extend"],
-                    default=None,
+    ap.add_argument("--only", choices=WORKLOADS, default=None,
                     help="run one operation only (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -211,8 +216,7 @@ def main():
 
     osm.load_library()
     torch.cuda.set_device(0)
-    names = (["softmax", "fwd", "fwd_causal", "decode", "merge_lse", "extend"] if args.only is None
-             else [args.only])
+    names = list(WORKLOADS) if args.only is None else [args.only]
     calls, work = {}, {}
 
     if "softmax" in names:
@@ -222,17 +226,27 @@ def main():
         calls["softmax"] = lambda: osm.softmax_rows(x, out=y)
         # one HBM read + one HBM write per element: the row stays in registers
         work["softmax"] = ("hbm", 8.0 * x.numel(), "4096 x 32000 fp32, 8 B/elem")
-    if "fwd" in names or args.only is None:
+    if "fwd" in names or "bwd" in names or args.only is None:
         log("inputs: fwd B4 H32 N4096 d128")
         inp3 = inputs.config3()
         q3, k3, v3 = (bf16_dev(a, torch) for a in (inp3.q, inp3.k, inp3.v))
         o3 = torch.empty_like(q3)
         l3 = torch.empty(q3.shape[:3], dtype=torch.float32, device="cuda")
+        B, H, N, d = q3.shape
         if "fwd" in names:
             calls["fwd"] = lambda: osm.attn_fwd(q3, k3, v3, scale=inp3.scale, out=o3, lse=l3)
-            B, H, N, d = q3.shape
             work["fwd"] = ("mfma", 4.0 * B * H * N * N * d, "B4 H32 N4096 d128 non-causal")
-    if "fwd_causal" in names:
+        if "bwd" in names:
+            log("inputs: bwd B4 H32 N4096 d128, output gradient")
+            osm.attn_fwd(q3, k3, v3, scale=inp3.scale, out=o3, lse=l3)
+            do3 = bf16_dev(inputs.output_grad(4, 32, 4096, 128, inputs.SEED_BASE + 8), torch)
+            ws3 = torch.empty(osm.attn_bwd_workspace_bytes(4, 32, 4096), dtype=torch.uint8, device="cuda")
+            g3 = [torch.empty_like(t) for t in (q3, k3, v3)]
+            calls["bwd"] = lambda: osm.attn_bwd(q3, k3, v3, o3, l3, do3, scale=inp3.scale, workspace=ws3,
+                                                dq=g3[0], dk=g3[1], dv=g3[2])
+            # five products per (query, key) pair: S again, dP, dV, dQ, dK
+            work["bwd"] = ("mfma", 10.0 * B * H * N * N * d, "backward of B4 H32 N4096 d128 non-causal")
+    if "fwd_causal" in names or "bwd_causal" in names:
         log("inputs: fwd causal B8 H16 N8192 d128 varlen")
         inp4 = inputs.config4()
         q4, k4, v4 = (bf16_dev(a, torch) for a in (inp4.q, inp4.k, inp4.v))
@@ -243,8 +257,21 @@ def main():
         calls["fwd_causal"] = lambda: osm.attn_fwd(q4, k4, v4, scale=scale4, causal=True,
                                                    seqlens_q=lens4, seqlens_k=lens4, out=o4, lse=l4)
         Lb = inp4.seqlens_q.astype(np.float64)
-        work["fwd_causal"] = ("mfma", 4.0 * 128 * 16 * float(np.sum(Lb * (Lb + 1) / 2)),
-                              "B8 H16 N8192 d128 causal, L_b U[1024,8192]")
+        pairs4 = 128 * 16 * float(np.sum(Lb * (Lb + 1) / 2))
+        work["fwd_causal"] = ("mfma", 4.0 * pairs4, "B8 H16 N8192 d128 causal, L_b U[1024,8192]")
+        if "bwd_causal" in names:
+            log("inputs: bwd causal, output gradient")
+            calls["fwd_causal"]()
+            do4 = bf16_dev(inputs.output_grad(8, 16, 8192, 128, inputs.SEED_BASE + 9,
+                                              seqlens_q=inp4.seqlens_q, poison=True), torch)
+            ws4 = torch.empty(osm.attn_bwd_workspace_bytes(8, 16, 8192), dtype=torch.uint8, device="cuda")
+            g4 = [torch.empty_like(t) for t in (q4, k4, v4)]
+            calls["bwd_causal"] = lambda: osm.attn_bwd(q4, k4, v4, o4, l4, do4, scale=scale4, causal=True,
+                                                       seqlens_q=lens4, seqlens_k=lens4, workspace=ws4,
+                                                       dq=g4[0], dk=g4[1], dv=g4[2])
+            # five products per visible (query, key) pair: S again, dP, dV, dQ, dK
+            work["bwd_causal"] = ("mfma", 10.0 * pairs4,
+                                  "backward of B8 H16 N8192 d128 causal, L_b U[1024,8192]")
         del inp4
     if "decode" in names:
         log("inputs: decode B16 Hq32 Hkv8 L<=32768 d128")
@@ -348,7 +375,8 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": f"attn_fwd {hc['workload']}" if head == "fwd" else hc["workload"],
                       "step": "softmax_rows + attn_fwd (non-causal) + attn_fwd (causal varlen) "
-                              "+ attn_decode_splitkv + merge_lse + attn_extend" if args.only is None
+                              "+ attn_decode_splitkv + merge_lse + attn_extend + attn_bwd (non-causal) "
+                              "+ attn_bwd (causal varlen)" if args.only is None
                               else args.only,
                       "global_batch": 4, "seq_len": 4096, "parallelism": "none (1 GPU)"},
            "roofline": roofline, "components": comps}

@@ -28,7 +28,8 @@ OSM_BF16 = 1
 STATUS = {0: "OSM_OK", 1: "OSM_ERR_NULL", 2: "OSM_ERR_SHAPE", 3: "OSM_ERR_UNSUPPORTED",
           4: "OSM_ERR_WORKSPACE", 5: "OSM_ERR_HIP"}
 EXPORTS = ("osm_status_str", "osm_softmax_rows", "osm_attn_fwd", "osm_decode_workspace_bytes",
-           "osm_attn_decode_splitkv", "osm_merge_partials", "osm_merge_lse", "osm_attn_extend")
+           "osm_attn_decode_splitkv", "osm_merge_partials", "osm_merge_lse", "osm_attn_extend",
+           "osm_attn_bwd_workspace_bytes", "osm_attn_bwd")
 
 
 class OsmError(RuntimeError):
@@ -63,8 +64,12 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.osm_merge_lse.argtypes = [vp, vp, i64, i32, i32, ctypes.c_int, vp, ctypes.c_int, vp, vp]
     lib.osm_attn_extend.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32, f32, vp, vp, vp,
                                     i32, vp, ctypes.c_size_t, vp]
+    lib.osm_attn_bwd_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.osm_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.osm_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, i32, i32, i32,
+                                 i32, i32, vp, vp, f32, i32, vp, ctypes.c_size_t, vp]
     for name in ("osm_softmax_rows", "osm_attn_fwd", "osm_attn_decode_splitkv",
-                 "osm_merge_partials", "osm_merge_lse", "osm_attn_extend"):
+                 "osm_merge_partials", "osm_merge_lse", "osm_attn_extend", "osm_attn_bwd"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -173,6 +178,44 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, seqlens_q=None, seqlens_k=Non
                             _dtype_code(q.dtype), B, Hq, Hkv, Nq, Nk, d, _ptr(sq), _ptr(sk),
                             float(scale), int(bool(causal)), _stream()))
     return o, lse_t
+
+
+def attn_bwd_workspace_bytes(batch, heads_q, seqlen_q):
+    return int(load_library().osm_attn_bwd_workspace_bytes(batch, heads_q, seqlen_q))
+
+
+def attn_bwd(q, k, v, o, lse, dout, *, scale=None, causal=False, seqlens_q=None, seqlens_k=None,
+             workspace=None, dq=None, dk=None, dv=None):
+    """Attention backward from the forward's o and lse.  q, o, dout
+    [B, Hq, Nq, d]; k, v [B, Hkv, Nk, d] bf16; lse [B, Hq, Nq] fp32.
+    Returns (dq, dk, dv) shaped like q, k, v."""
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _device_tensor(t, name, (torch.bfloat16,))
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [batch, heads, positions, head_dim]")
+    _device_tensor(lse, "lse", (torch.float32,))
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk_ = k.shape
+    if (Bk != B or dk_ != d or tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape)
+            or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, Nq)):
+        raise ValueError("q, k, v, o, lse, dout shapes are inconsistent")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    sq = _lengths(seqlens_q, "seqlens_q", B, q.device)
+    sk = _lengths(seqlens_k, "seqlens_k", B, q.device)
+    nbytes = attn_bwd_workspace_bytes(B, Hq, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check(lib.osm_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                            _ptr(dk), _ptr(dv), _dtype_code(q.dtype), B, Hq, Hkv, Nq, Nk, d, _ptr(sq),
+                            _ptr(sk), float(scale), int(bool(causal)), _ptr(workspace),
+                            workspace.numel(), _stream()))
+    return dq, dk, dv
 
 
 def decode_workspace_bytes(batch, heads_q, max_seqlen_k, head_dim, split_size=256):

@@ -61,6 +61,41 @@ osm_status osm_attn_fwd(const void *q, const void *k, const void *v, void *o, fl
     return hip_status(osm::launch_attn_fwd(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t osm_attn_bwd_workspace_bytes(int32_t batch, int32_t heads_q, int32_t seqlen_q) {
+    if (batch < 1 || heads_q < 1 || seqlen_q < 0) return 0;
+    return osm::attn_bwd_workspace_bytes(batch, heads_q, seqlen_q);
+}
+
+osm_status osm_attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                        const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                        osm_dtype dtype, int32_t batch, int32_t heads_q, int32_t heads_kv,
+                        int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                        const int32_t *seqlens_q, const int32_t *seqlens_k, float scale,
+                        int32_t causal, void *workspace, size_t workspace_bytes,
+                        osm_stream stream) {
+    if (batch < 1 || heads_q < 1 || heads_kv < 1 || head_dim < 1 || seqlen_q < 0 || seqlen_k < 0 ||
+        heads_q % heads_kv != 0 || !(scale > 0.0f) || !isfinite(scale) || (causal != 0 && causal != 1))
+        return OSM_ERR_SHAPE;
+    if (dtype != OSM_BF16 || head_dim != 128) return OSM_ERR_UNSUPPORTED;
+    // one head's rows are addressed with 32-bit byte offsets
+    if ((int64_t)seqlen_k * head_dim * 2 >= ((int64_t)1 << 31) ||
+        (int64_t)seqlen_q * head_dim * 2 >= ((int64_t)1 << 31))
+        return OSM_ERR_UNSUPPORTED;
+    if (seqlen_q == 0 && seqlen_k == 0) return OSM_OK;
+    if ((seqlen_q > 0 && (!q || !o || !dout || !lse || !dq)) || (seqlen_k > 0 && (!k || !v || !dk || !dv)))
+        return OSM_ERR_NULL;
+    // operands are read 16 bytes at a time
+    const void *ptrs[] = {q, k, v, o, dout, dq, dk, dv};
+    for (const void *p : ptrs)
+        if (reinterpret_cast<uintptr_t>(p) & 15) return OSM_ERR_UNSUPPORTED;
+    const size_t need = osm::attn_bwd_workspace_bytes(batch, heads_q, seqlen_q);
+    if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255)))
+        return OSM_ERR_WORKSPACE;
+    osm::AttnBwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, batch, heads_q, heads_kv, seqlen_q, seqlen_k,
+                       head_dim, seqlens_q, seqlens_k, scale, causal, workspace};
+    return hip_status(osm::launch_attn_bwd(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t osm_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t max_seqlen_k,
                                   int32_t head_dim, int32_t split_size) {
     if (batch < 1 || heads_q < 1 || max_seqlen_k < 1 || head_dim < 1 || split_size < 1) return 0;

@@ -344,45 +344,6 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
         }
     };
 
-    // O~^T += V^T P~^T.  A operand, lane l, dim row 32 dt + c: keys
-    // 16 hh + 4 g + 0..3 and + 8, the same keys in the same order as the B
-    // operand's elements
-    auto pv = [&](const uint8_t *vb, const bf16x8 (&p)[2][2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                const uint8_t *base = vb + 16 * hh * ROWB + voff[dt];
-                const bf16x4 lo = lds_read_tr(base);
-                const bf16x4 hi = lds_read_tr(base + 8 * ROWB);
-                const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) mfma_acc(oacc[qb][dt], a, p[qb][hh]);
-            }
-    };
-
-    // P~ = exp2(S scale log2e - m scale log2e) as bf16 B operands, l += row sums
-    auto expo = [&](const f32x16 (&s)[2], bf16x8 (&p)[2][2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            float e[16];
-            float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                e[i] = fast_exp2(fmaf(s[qb][i], scale_log2, -msub[qb]));
-                rs[i & 3] += e[i];
-            }
-            l[qb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                f32x8 f;
-#pragma unroll
-                for (int k = 0; k < 8; ++k) f[k] = e[8 * hh + k];
-                p[qb][hh] = __builtin_convertvector(f, bf16x8);
-            }
-        }
-    };
-
     // key 32 t + 8 r + 4 g + u is visible to query q iff it is <= min(Lk-1, q)
     // (causal) or <= Lk - 1
     auto mask = [&](f32x16 (&s)[2], int t) __attribute__((always_inline)) {

@@ -36,6 +36,20 @@ struct AttnFwdArgs {
 };
 hipError_t launch_attn_fwd(const AttnFwdArgs &a, hipStream_t s);
 
+// ---- attention backward ----------------------------------------------------
+struct AttnBwdArgs {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;
+    void *dq, *dk, *dv;
+    int batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim;
+    const int32_t *seqlens_q, *seqlens_k;
+    float scale;
+    int causal;
+    void *workspace;     // attn_bwd_workspace_bytes(): (lse2, D) per query row
+};
+size_t attn_bwd_workspace_bytes(int64_t batch, int64_t heads_q, int64_t seqlen_q);
+hipError_t launch_attn_bwd(const AttnBwdArgs &a, hipStream_t s);
+
 // ---- split-KV decode + merge ----------------------------------------------
 struct DecodeLayout {
     int64_t rows;        // batch * heads_q

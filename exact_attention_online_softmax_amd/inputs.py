@@ -133,6 +133,17 @@ def attention_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, seed: 
     return AttnInputs(q, k, v, dtype, sq, sk, float(scale), bool(causal))
 
 
+def output_grad(B: int, Hq: int, Nq: int, d: int, seed: int, *, seqlens_q=None,
+                poison: bool = False) -> np.ndarray:
+    """An output gradient dO ~ N(0, 1) [B, Hq, Nq, d] as bf16 bits, with
+    optional NaN poison in rows past the valid query length."""
+    g = rng(seed)
+    do = normal_f32(g, (B, Hq, Nq, d))
+    if poison and seqlens_q is not None:
+        poison_tail(do, np.asarray(seqlens_q, np.int32), Nq)
+    return to_bf16_bits(do)
+
+
 def causal_padded_inputs(B: int, H: int, N: int, d: int, seed: int, lo: int, hi: int,
                          poison: bool = True) -> AttnInputs:
     """Self-attention with right padding: valid lengths uniform in [lo, hi],

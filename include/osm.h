@@ -130,6 +130,54 @@ osm_status osm_attn_fwd(const void *q, const void *k, const void *v, void *o, fl
                         int32_t causal, osm_stream stream);
 
 /*
+ * osm_attn_bwd_workspace_bytes -- bytes of device workspace that
+ * osm_attn_bwd needs: 8 bytes per query row (batch * heads_q * seqlen_q).
+ * Returns 0 for invalid sizes.
+ */
+size_t osm_attn_bwd_workspace_bytes(int32_t batch, int32_t heads_q, int32_t seqlen_q);
+
+/*
+ * osm_attn_bwd -- gradients of osm_attn_fwd's output with respect to Q, K
+ * and V, given the gradient dO of the output and the forward's O and LSE.
+ *
+ * [P3] "From weights to outputs", the log-sum-exp paragraph: the stored lse
+ * is all a backward pass needs to rebuild the weights, P_ij =
+ * exp(s_ij - lse_i).  The pages do not write the backward out; it is the
+ * derivative of the forward definition (chain rule through O = P V and the
+ * softmax): dV = P^T dO, dP = dO V^T, dS = P * (dP - D) with
+ * D_i = dO_i . O_i, dQ = scale dS K, dK = scale dS^T Q.  dK and dV of a
+ * key/value head sum over the query heads that read it.
+ *
+ *   q, o, dout  [batch][heads_q][seqlen_q][head_dim] (dtype); o as written
+ *         by osm_attn_fwd for the same q, k, v and arguments
+ *   k, v  [batch][heads_kv][seqlen_k][head_dim] (dtype)
+ *   lse   fp32 [batch][heads_q][seqlen_q], as written by osm_attn_fwd
+ *   dq    shaped like q; dk, dv shaped like k (dtype, written)
+ *   seqlens_q, seqlens_k, scale, causal, heads: as osm_attn_fwd.  Rows past
+ *         the valid lengths are never read into a sum (q, k, v, o and dout
+ *         there may hold any bits) and their gradients are written as 0;
+ *         a query row that sees no key contributes nothing.
+ *   workspace  DEVICE memory of at least osm_attn_bwd_workspace_bytes()
+ *         bytes (caller-owned, 256-byte aligned, contents on entry ignored).
+ * Three kernels are enqueued on `stream`: the per-row (lse, dO . O), then
+ * dK/dV (key-major), then dQ (query-major).  No atomics: the result is
+ * deterministic.
+ * Supported: dtype OSM_BF16, head_dim 128; fp32 accumulation, P and dS
+ * rounded to bf16 as matrix-product operands, gradients rounded to bf16
+ * once at the end; every pointer 16-byte aligned.
+ * Errors: OSM_ERR_NULL, OSM_ERR_SHAPE (as osm_attn_fwd),
+ * OSM_ERR_UNSUPPORTED (other dtype or head_dim, a pointer not 16-byte
+ * aligned, seqlen_q or seqlen_k >= 2^23), OSM_ERR_WORKSPACE, OSM_ERR_HIP.
+ */
+osm_status osm_attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                        const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                        osm_dtype dtype, int32_t batch, int32_t heads_q, int32_t heads_kv,
+                        int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                        const int32_t *seqlens_q, const int32_t *seqlens_k, float scale,
+                        int32_t causal, void *workspace, size_t workspace_bytes,
+                        osm_stream stream);
+
+/*
  * osm_decode_workspace_bytes -- bytes of device workspace that
  * osm_attn_decode_splitkv needs for these sizes: fp32 partial triples
  * m [batch][heads_q][C], l [batch][heads_q][C], O~ [batch][heads_q][C][head_dim]

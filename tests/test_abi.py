@@ -167,6 +167,34 @@ def test_extend_validation(lib):
     assert call(ws=ctypes.c_void_p(0x10004)) == 4    # not 256-byte aligned
 
 
+def test_attn_bwd_validation(lib):
+    ws_ok = lib.osm_attn_bwd_workspace_bytes(1, 2, 8)
+    assert ws_ok == 1 * 2 * 8 * 8
+    assert lib.osm_attn_bwd_workspace_bytes(0, 2, 8) == 0
+
+    def call(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+             dtype=osm.OSM_BF16, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=128, scale=0.1, causal=0,
+             ws=FAKE, wsb=ws_ok):
+        return lib.osm_attn_bwd(q, k, v, o, do, lse, dq, dk, dv, dtype, B, Hq, Hkv, Nq, Nk, d,
+                                None, None, scale, causal, ws, wsb, None)
+    assert call(B=0) == 2
+    assert call(Nq=-1) == 2
+    assert call(Hq=3, Hkv=2) == 2
+    assert call(scale=0.0) == 2
+    assert call(scale=float("inf")) == 2
+    assert call(causal=2) == 2
+    assert call(d=64) == 3
+    assert call(dtype=osm.OSM_F32) == 3
+    assert call(Nk=1 << 23) == 3                    # one head's rows span 2 GiB
+    assert call(Nq=0, Nk=0, q=None, k=None) == 0    # nothing to do
+    for name in ("q", "o", "do", "lse", "dq", "k", "v", "dk", "dv"):
+        assert call(**{name: None}) == 1, name
+    assert call(dk=ctypes.c_void_p(0x10008)) == 3   # not 16-byte aligned
+    assert call(wsb=ws_ok - 1) == 4
+    assert call(ws=None) == 4
+    assert call(ws=ctypes.c_void_p(0x10010)) == 4   # not 256-byte aligned
+
+
 @no_gpu_only
 def test_no_device_reports_hip_error(lib):
     """A fully valid request in a process without a GPU fails cleanly with
