@@ -13,6 +13,8 @@ inputs already resident in HBM:
                                     (log-sum-exp merge of results over disjoint key sets)
   extend    osm_attn_extend         bf16 B=16 Hq=32 Hkv=8 d=128, 4096 new keys per call folded
                                     into a persisted (m, l, O~) state (streaming attention)
+  fwd_fp8   osm_attn_fwd_fp8        the fwd workload with OCP E4M3 Q, K, V (both products on the FP8
+                                    matrix instruction; peak 5033 TFLOP/s)
   bwd       osm_attn_bwd            backward of the fwd workload (dQ, dK, dV from O, LSE, dO)
   bwd_causal osm_attn_bwd           backward of the fwd_causal workload
 
@@ -38,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attn fwd TFLOP/s & % MFMA peak (N=4K/32K); softmax/decode GB/s & % HBM peak"
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12     # 2516.6 dense bf16 MFMA
+PEAK_FP8_TFLOPS = 256 * 2.4e9 * 8192 / 1e12      # 5033.2 dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 PROFILE_FWD = os.path.join(ROOT, "profiles", "attn_fwd_bf16_d128_B4_H32_N4096.md")
 
@@ -52,8 +55,9 @@ def bf16_dev(bits, torch):
 
 KERNEL_SOURCES = {"fwd": "attn_fwd.hip", "fwd_causal": "attn_fwd.hip", "softmax": "softmax_rows.hip",
                   "decode": "decode.hip", "merge_lse": "merge_lse.hip", "extend": "decode.hip",
-                  "bwd": "attn_bwd.hip", "bwd_causal": "attn_bwd.hip"}
-WORKLOADS = ["softmax", "fwd", "fwd_causal", "decode", "merge_lse", "extend", "bwd", "bwd_causal"]
+                  "bwd": "attn_bwd.hip", "bwd_causal": "attn_bwd.hip", "fwd_fp8": "attn_fwd_fp8.hip"}
+WORKLOADS = ["softmax", "fwd", "fwd_causal", "decode", "merge_lse", "extend", "bwd", "bwd_causal",
+             "fwd_fp8"]
 
 
 def source_hash(name):
@@ -116,7 +120,7 @@ def summarize(name, trace_dir, out):
     import glob
     kern = {"fwd": "attn_fwd", "fwd_causal": "attn_fwd", "softmax": "softmax_rows",
             "decode": "decode_split", "merge_lse": "merge_lse", "extend": "decode_split",
-            "bwd": "attn_bwd_dkdv", "bwd_causal": "attn_bwd_dkdv"}[name]
+            "bwd": "attn_bwd_dkdv", "bwd_causal": "attn_bwd_dkdv", "fwd_fp8": "attn_fwd_fp8"}[name]
     lines = [f"# rocprofv3 summary: {name}", ""]
     trace = os.path.join(trace_dir, "trace", "run_kernel_trace.csv")
     avg_ns = None
@@ -137,7 +141,8 @@ def summarize(name, trace_dir, out):
         want = {"fwd": ("attn_fwd", 2048), "fwd_causal": ("attn_fwd", 4096),
                 "softmax": ("softmax_rows", None), "decode": ("decode_split", None),
                 "merge_lse": ("merge_lse", None), "extend": ("decode_split", None),
-                "bwd": ("attn_bwd_dkdv", None), "bwd_causal": ("attn_bwd_dkdv", None)}[name]
+                "bwd": ("attn_bwd_dkdv", None), "bwd_causal": ("attn_bwd_dkdv", None),
+                "fwd_fp8": ("attn_fwd_fp8", None)}[name]
         for (short, wg), d in groups.items():
             if want[0] in short and (want[1] is None or wg == want[1]):
                 avg_ns = sum(d) / len(d)
@@ -325,6 +330,17 @@ def main():
                                        + 2 * B7 * Hq7 * (D7 + 2) * 4 + 2 * B7 * Hq7 * pieces7 * (D7 + 2) * 4),
                           "B16 Hq32 Hkv8 d128 bf16, 4096 new keys folded into a persisted state")
 
+    if "fwd_fp8" in names:
+        log("inputs: fwd fp8 B4 H32 N4096 d128 (E4M3 codes)")
+        inp8 = inputs.attention_inputs(4, 32, 32, 4096, 4096, 128, seed=inputs.SEED_BASE + 10, dtype="fp8")
+        q8, k8, v8 = (torch.from_numpy(a).to("cuda") for a in (inp8.q, inp8.k, inp8.v))
+        o8 = torch.empty(q8.shape, dtype=torch.bfloat16, device="cuda")
+        l8 = torch.empty(q8.shape[:3], dtype=torch.float32, device="cuda")
+        scale8 = inp8.scale
+        calls["fwd_fp8"] = lambda: osm.attn_fwd_fp8(q8, k8, v8, scale=scale8, out=o8, lse=l8)
+        work["fwd_fp8"] = ("mfma8", 4.0 * 4 * 32 * 4096 * 4096 * 128, "B4 H32 N4096 d128 non-causal, E4M3 Q/K/V")
+        del inp8
+
     if args.copy_calibration:
         n = args.copy_calibration * 1024 * 1024 // 4
         csrc = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -358,12 +374,16 @@ def main():
         t = ms[n] / 1e3
         if bound == "mfma":
             ach, peak, unit = amount / t / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+        elif bound == "mfma8":
+            ach, peak, unit = amount / t / 1e12, PEAK_FP8_TFLOPS, "TFLOP/s"
         else:
             ach, peak, unit = amount / t / 1e9, PEAK_HBM_GBS, "GB/s"
         comps[n] = {"workload": desc, "ms": round(ms[n], 4), "achieved": round(ach, 2),
                     "unit": unit, "bound": "hbm" if bound == "hbm" else "mfma",
                     "peak": round(peak, 1), "frac": round(ach / peak, 4),
                     "algorithmic": amount}
+        if bound == "mfma8":
+            comps[n]["dtype"] = "fp8"
     head = "fwd" if "fwd" in comps else names[0]
     hc = comps[head]
     roofline = {"bound": hc["bound"], "achieved": hc["achieved"], "peak": hc["peak"],
@@ -376,7 +396,7 @@ def main():
            "config": {"workload": f"attn_fwd {hc['workload']}" if head == "fwd" else hc["workload"],
                       "step": "softmax_rows + attn_fwd (non-causal) + attn_fwd (causal varlen) "
                               "+ attn_decode_splitkv + merge_lse + attn_extend + attn_bwd (non-causal) "
-                              "+ attn_bwd (causal varlen)" if args.only is None
+                              "+ attn_bwd (causal varlen) + attn_fwd_fp8" if args.only is None
                               else args.only,
                       "global_batch": 4, "seq_len": 4096, "parallelism": "none (1 GPU)"},
            "roofline": roofline, "components": comps}

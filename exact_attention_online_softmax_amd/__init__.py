@@ -29,7 +29,7 @@ STATUS = {0: "OSM_OK", 1: "OSM_ERR_NULL", 2: "OSM_ERR_SHAPE", 3: "OSM_ERR_UNSUPP
           4: "OSM_ERR_WORKSPACE", 5: "OSM_ERR_HIP"}
 EXPORTS = ("osm_status_str", "osm_softmax_rows", "osm_attn_fwd", "osm_decode_workspace_bytes",
            "osm_attn_decode_splitkv", "osm_merge_partials", "osm_merge_lse", "osm_attn_extend",
-           "osm_attn_bwd_workspace_bytes", "osm_attn_bwd")
+           "osm_attn_bwd_workspace_bytes", "osm_attn_bwd", "osm_attn_fwd_fp8")
 
 
 class OsmError(RuntimeError):
@@ -64,12 +64,15 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.osm_merge_lse.argtypes = [vp, vp, i64, i32, i32, ctypes.c_int, vp, ctypes.c_int, vp, vp]
     lib.osm_attn_extend.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32, f32, vp, vp, vp,
                                     i32, vp, ctypes.c_size_t, vp]
+    lib.osm_attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, f32, f32,
+                                     i32, vp]
     lib.osm_attn_bwd_workspace_bytes.argtypes = [i32, i32, i32]
     lib.osm_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.osm_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, i32, i32, i32,
                                  i32, i32, vp, vp, f32, i32, vp, ctypes.c_size_t, vp]
     for name in ("osm_softmax_rows", "osm_attn_fwd", "osm_attn_decode_splitkv",
-                 "osm_merge_partials", "osm_merge_lse", "osm_attn_extend", "osm_attn_bwd"):
+                 "osm_merge_partials", "osm_merge_lse", "osm_attn_extend", "osm_attn_bwd",
+                 "osm_attn_fwd_fp8"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -177,6 +180,34 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, seqlens_q=None, seqlens_k=Non
     _check(lib.osm_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t),
                             _dtype_code(q.dtype), B, Hq, Hkv, Nq, Nk, d, _ptr(sq), _ptr(sk),
                             float(scale), int(bool(causal)), _stream()))
+    return o, lse_t
+
+
+def attn_fwd_fp8(q, k, v, *, scale=None, v_scale=1.0, causal=False, seqlens_q=None, seqlens_k=None,
+                 out=None, lse=None):
+    """Fused attention forward with FP8 E4M3 inputs (torch.float8_e4m3fn, or
+    uint8 tensors of E4M3 codes).  q [B, Hq, Nq, d], k/v [B, Hkv, Nk, d].
+    Returns (o [B, Hq, Nq, d] bf16, lse [B, Hq, Nq] fp32)."""
+    torch = _torch()
+    lib = load_library()
+    fp8 = tuple(t for t in (getattr(torch, "float8_e4m3fn", None), torch.uint8) if t is not None)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _device_tensor(t, name, fp8)
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [batch, heads, positions, head_dim]")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("q, k, v shapes are inconsistent")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=q.device) if out is None else out
+    lse_t = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    sq = _lengths(seqlens_q, "seqlens_q", B, q.device)
+    sk = _lengths(seqlens_k, "seqlens_k", B, q.device)
+    _check(lib.osm_attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, Hq, Hkv, Nq, Nk, d,
+                                _ptr(sq), _ptr(sk), float(scale), float(v_scale), int(bool(causal)),
+                                _stream()))
     return o, lse_t
 
 

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIBRARY = os.path.join(HERE, "libosm.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["abi.cpp", "softmax_rows.hip", "attn_fwd.hip", "attn_bwd.hip", "decode.hip", "merge_lse.hip"]
+SOURCES = ["abi.cpp", "softmax_rows.hip", "attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "decode.hip", "merge_lse.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no packed fp32 VALU instructions are generated.

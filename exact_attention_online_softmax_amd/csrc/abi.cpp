@@ -61,6 +61,29 @@ osm_status osm_attn_fwd(const void *q, const void *k, const void *v, void *o, fl
     return hip_status(osm::launch_attn_fwd(a, static_cast<hipStream_t>(stream)));
 }
 
+osm_status osm_attn_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+                            int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t seqlen_q,
+                            int32_t seqlen_k, int32_t head_dim, const int32_t *seqlens_q,
+                            const int32_t *seqlens_k, float scale, float v_scale, int32_t causal,
+                            osm_stream stream) {
+    if (batch < 1 || heads_q < 1 || heads_kv < 1 || head_dim < 1 || seqlen_q < 0 || seqlen_k < 0 ||
+        heads_q % heads_kv != 0 || !(scale > 0.0f) || !isfinite(scale) || !isfinite(v_scale) ||
+        (causal != 0 && causal != 1))
+        return OSM_ERR_SHAPE;
+    if (head_dim != 128) return OSM_ERR_UNSUPPORTED;
+    // one head's K (or V) rows are addressed with 32-bit byte offsets
+    if ((int64_t)seqlen_k * head_dim >= ((int64_t)1 << 31)) return OSM_ERR_UNSUPPORTED;
+    if (seqlen_q == 0) return OSM_OK;
+    if (!q || !o || (seqlen_k > 0 && (!k || !v))) return OSM_ERR_NULL;
+    // operands are read 16 bytes at a time
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
+         reinterpret_cast<uintptr_t>(o)) & 15)
+        return OSM_ERR_UNSUPPORTED;
+    osm::AttnFwdFp8Args a{q, k, v, o, lse, batch, heads_q, heads_kv, seqlen_q, seqlen_k,
+                          seqlens_q, seqlens_k, scale, v_scale, causal};
+    return hip_status(osm::launch_attn_fwd_fp8(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t osm_attn_bwd_workspace_bytes(int32_t batch, int32_t heads_q, int32_t seqlen_q) {
     if (batch < 1 || heads_q < 1 || seqlen_q < 0) return 0;
     return osm::attn_bwd_workspace_bytes(batch, heads_q, seqlen_q);

@@ -1,0 +1,390 @@
+// attn_fwd_fp8.hip -- fused exact attention forward with FP8 (OCP E4M3) Q, K
+// and V on gfx950 (head_dim 128).
+//
+// [P3] "Precision, and what can still go wrong": kernels keep the running
+// m, l and O~ in float32 even when Q, K and V are bf16 or FP8, because those
+// few numbers per row decide the output's accuracy.  The computation is the
+// block step of [P3] "Blocks, the bridge to FlashAttention", exactly as in
+// attn_fwd.hip (running maximum with a lazy reference, rescale of O~ and l,
+// one division at the end, LSE = m + log l, masks inside the tile loop);
+// what changes is the precision of the two matrix products:
+//  * S^T = K Q^T on v_mfma_scale_f32_32x32x64_f8f6f4 with both operands E4M3
+//    and unit scales: products of E4M3 values are exact, sums are fp32.
+//  * P~ = exp2(S scale log2e - m) is at most 2^8 under the lazy reference;
+//    it is rounded to E4M3 (nearest even) as the B operand of
+//    O~^T += V^T P~^T on the same instruction.  l sums the fp32 P~.
+//  * m, l, O~ and the epilogue stay fp32; O is written as bf16, times
+//    v_scale (the dequantization factor of V), and the LSE as fp32.
+//
+// Mapping to CDNA4:
+//  * workgroup = 4 wavefronts = 256 queries; each wave owns 64 queries as two
+//    32-query blocks and holds their Q as MFMA B operands (32 bytes per lane
+//    per 64-dim k-step).
+//  * tiles of 64 keys (the MFMA's k for P~V): K and V tiles of 64 rows x 128
+//    bytes go from HBM straight into LDS through buffer loads with LDS
+//    destination (rows past Lk read as zeros), through a ring of three slots.
+//  * key order: row c = 8 r + 4 h + u of a 32-key score block is key
+//    16 h + 4 r + u of that block, so each lane half of the score accumulator
+//    holds 16 consecutive keys.  P~ packs them, in order, into the B operand
+//    of P~V; its A operand V^T comes from ds_read_b64_tr_b8 reads (lane j of
+//    a 16-lane group receives eight consecutive rows of column j), eight keys
+//    per read, in the same order.
+//  * LDS rows are unpadded, 16-byte chunk c of row r in slot c ^ swz8(r):
+//    both the row-wise K operand reads and the transposing V reads are free
+//    of bank conflicts.
+#include "osm_device.h"
+#include "osm_internal.h"
+
+namespace osm {
+
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int D = 128;            // head dim
+constexpr int ROWB = D;           // bytes per E4M3 row
+constexpr int NW = 4;             // wavefronts per workgroup
+constexpr int QW = 64;            // queries per wavefront (two blocks of 32)
+constexpr int BQ = QW * NW;       // queries per workgroup
+constexpr int BK = 64;            // keys per tile
+constexpr int NT = 64 * NW;
+constexpr int TILEB = BK * ROWB;  // bytes per K or V tile (8 KiB)
+constexpr int LPW = TILEB / 1024 / NW;   // 1 KiB loads per wave per K (or V) tile
+static_assert(2 * LPW == 4, "kWaitVm4 assumes four loads per wave per tile");
+
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
+constexpr int kWaitVm0 = 0x0F70;         // s_waitcnt vmcnt(0)
+constexpr int kWaitVm4 = 0x0F74;         // s_waitcnt vmcnt(4)
+constexpr int kUnitScale = 127;          // E8M0 exponent of 1.0 for the MFMA's block scales
+
+template <int N> struct Slot { static constexpr int value = N; };
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+__device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// chunk c of LDS row r sits in slot c ^ swz8(r); see the header comment
+__device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 3) | (((r >> 4) & 1) << 2); }
+
+__device__ __forceinline__ f32x16 mfma8(const i32x8 &a, const i32x8 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kUnitScale, 0, kUnitScale);
+}
+
+__device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t *p) {
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 __attribute__((address_space(3))) *)(p));
+}
+
+__device__ __forceinline__ void tile_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__global__ void __launch_bounds__(NT, 1)
+attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
+                  const uint8_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE,
+                  int Hq, int Hkv, int Nq, int Nk, const int32_t *__restrict__ seqlens_q,
+                  const int32_t *__restrict__ seqlens_k, float scale_log2, float v_scale, int causal,
+                  int nqb, int xcd_heads) {
+    __shared__ __attribute__((aligned(1024))) uint8_t k0[TILEB], k1[TILEB], k2[TILEB];
+    __shared__ __attribute__((aligned(1024))) uint8_t v0[TILEB], v1[TILEB], v2[TILEB];
+
+    // ---- which (batch, head, query block) ------------------------------
+    const int L = blockIdx.x;
+    int head, qrev;
+    if (xcd_heads) {
+        // block L runs on XCD L % 8: whole heads per XCD, so the blocks of
+        // one head share its K and V in that XCD's L2
+        const int xcd = L & 7, slot = L >> 3;
+        qrev = slot % nqb;
+        head = (slot / nqb) * 8 + xcd;
+    } else {
+        head = L / nqb;
+        qrev = L % nqb;
+    }
+    head = rfl(head);
+    qrev = rfl(qrev);
+    const int qb0 = causal ? (nqb - 1 - qrev) : qrev;     // causal: heaviest blocks first
+    const int b = head / Hq, h = head % Hq;
+    const int kvh = h / (Hq / Hkv);
+    const int Lq = rfl(seqlens_q ? clampi(seqlens_q[b], 0, Nq) : Nq);
+    const int Lk = rfl(seqlens_k ? clampi(seqlens_k[b], 0, Nk) : Nk);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = rfl(tid >> 6);
+    const int g = lane >> 5, c = lane & 31;
+    const int q0 = qb0 * BQ;
+    const int qw0 = q0 + QW * wave;             // queries qw0 + 32 qb + c
+    const size_t qrow0 = (size_t)(b * Hq + h) * Nq;
+    const uint8_t *Kh = K + (size_t)(b * Hkv + kvh) * Nk * D;
+    const uint8_t *Vh = V + (size_t)(b * Hkv + kvh) * Nk * D;
+
+    if (q0 >= Lq) {
+        const int rows = min(BQ, Nq - q0);
+        for (int i = tid; i < rows * (D / 8); i += NT)
+            *reinterpret_cast<uint4 *>(O + (qrow0 + q0 + i / (D / 8)) * D + (i % (D / 8)) * 8) =
+                make_uint4(0, 0, 0, 0);
+        if (LSE)
+            for (int r = tid; r < rows; r += NT) LSE[qrow0 + q0 + r] = kNegInf;
+        return;
+    }
+
+    int kend = Lk;
+    if (causal) kend = min(kend, min(q0 + BQ, Lq));
+    const int ntiles = (kend + BK - 1) / BK;
+    int wtiles = (qw0 >= Lq) ? 0 : ntiles;
+    if (causal) wtiles = min(wtiles, (qw0 + QW - 1) / BK + 1);
+    int wmask = wtiles;                           // first tile that needs a mask
+    if (causal) wmask = min(wmask, qw0 / BK);
+    if (Lk % BK) wmask = min(wmask, Lk / BK);
+
+    // ---- Q (B operands of S^T = K Q^T): lane (g, c) holds row qw0 + 32 qb + c,
+    // bytes 64 ks + 32 g .. + 31; rows at or past Lq are zero
+    i32x8 qf[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int qi = qw0 + 32 * qb + c;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+            if (qi < Lq) {
+                const uint4 *src = reinterpret_cast<const uint4 *>(Q + (qrow0 + qi) * D + 64 * ks + 32 * g);
+                lo = src[0];
+                hi = src[1];
+            }
+            qf[qb][ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+    }
+
+    f32x16 oacc[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[qb][dt][i] = 0.0f;
+    float m[2], msub[2], l[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        m[qb] = kNegInf;     // reference maximum of raw scores q.k
+        msub[qb] = 0.0f;     // m * scale * log2(e) (0 while m = -inf)
+        l[qb] = 0.0f;        // this lane's part of the running sum
+    }
+    // The reference only moves when a tile's maximum exceeds it by more than
+    // 2^8 in weight, so every P~ is at most 2^8 (E4M3 holds up to 448).
+    constexpr float kLazy = 8.0f;
+    const float lazy_raw = kLazy / scale_log2;
+
+    // ---- tile DMA: load i of wave w fills LDS block LPW w + i (8 rows);
+    // lane l row 8 blk + l/8, slot l%8, holding global chunk slot ^ swz8(row)
+    uint32_t dmo[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int row = 8 * (LPW * wave + i) + (lane >> 3);
+        dmo[i] = row * ROWB + (((lane & 7) ^ swz8(row)) << 4);
+    }
+    auto issue = [&](uint8_t *kd, uint8_t *vd, int t) __attribute__((always_inline)) {
+        const int j0 = t * BK;
+        const int bytes = max(0, Lk - j0) * ROWB;   // < 2^31: the ABI bounds Nk * 128
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(Kh) + (size_t)j0 * D, 0, bytes, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(Vh) + (size_t)j0 * D, 0, bytes, kRsrcWord3);
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (void __attribute__((address_space(3))) *)(kd + (LPW * wave + i) * 1024),
+                                                     16, dmo[i], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (void __attribute__((address_space(3))) *)(vd + (LPW * wave + i) * 1024),
+                                                     16, dmo[i], 0, 0, 0);
+        }
+    };
+
+    // K operand (rows of a 32-key block, permuted): lane (g, c) with
+    // c = 8 r + 4 hh + u reads key row 16 hh + 4 r + u, chunks 4 ks + 2 g and + 1;
+    // the second 32-key block is the same offsets + 32 rows
+    uint32_t koff[2][2];
+    {
+        const int row = 16 * ((c >> 2) & 1) + 4 * (c >> 3) + (c & 3);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) koff[ks][hf] = row * ROWB + (((4 * ks + 2 * g + hf) ^ swz8(row)) << 4);
+    }
+    // V^T operand (dim rows 32 dt + c): bytes 8 e .. 8 e + 7 of lane half g are
+    // keys 32 (e/2) + 16 g + 8 (e%2) + 0..7.  16-lane group t = lane/16,
+    // index i = lane%16 points at key row 16 (t/2) + i/2 (+ 8 (e%2) + 32 (e/2),
+    // which leave the swizzle unchanged), dims 32 dt + 16 (t%2) + 8 (i%2)
+    uint32_t voff[4];
+    {
+        const int t = lane >> 4, i = lane & 15;
+        const int row = 16 * (t >> 1) + (i >> 1);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) voff[dt] = row * ROWB + (((2 * dt + (t & 1)) ^ swz8(row)) << 4) + 8 * (i & 1);
+    }
+
+    // S^T of one tile: s[kb][qb] element 4 r + u of lane (g, c) is key
+    // 32 kb + 16 g + 4 r + u of the tile, query qw0 + 32 qb + c
+    auto qk = [&](const uint8_t *kb, f32x16 (&s)[2][2]) __attribute__((always_inline)) {
+        const f32x16 zero = {};
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const uint4 lo = *reinterpret_cast<const uint4 *>(kb + 32 * kbk * ROWB + koff[ks][0]);
+                const uint4 hi = *reinterpret_cast<const uint4 *>(kb + 32 * kbk * ROWB + koff[ks][1]);
+                const i32x8 a = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) s[kbk][qb] = mfma8(a, qf[qb][ks], ks ? s[kbk][qb] : zero);
+            }
+    };
+
+    auto mask = [&](f32x16 (&s)[2][2], int t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int qi = qw0 + 32 * qb + c;
+            const int lim = (causal ? min(Lk - 1, qi) : Lk - 1) - t * BK - 16 * g;
+#pragma unroll
+            for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (32 * kbk + i > lim) s[kbk][qb][i] = kNegInf;
+        }
+    };
+
+    auto compute = [&](const uint8_t *kb, const uint8_t *vb, int t, bool masked) __attribute__((always_inline)) {
+        f32x16 s[2][2];
+        qk(kb, s);
+        if (masked) mask(s, t);
+        // tile maximum per query (both lane halves), then the lazy reference
+        float tm[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float x = fmaxf(s[0][qb][0], s[1][qb][0]);
+#pragma unroll
+            for (int i = 1; i < 16; ++i) x = fmaxf(x, fmaxf(s[0][qb][i], s[1][qb][i]));
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+            tm[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        if (!__all((tm[0] <= m[0] + lazy_raw) && (tm[1] <= m[1] + lazy_raw))) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const float mn = fmaxf(m[qb], tm[qb]);
+                const float alpha = (mn == kNegInf || m[qb] == mn) ? 1.0f
+                                  : (m[qb] == kNegInf ? 0.0f : fast_exp2((m[qb] - mn) * scale_log2));
+                l[qb] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[qb][dt][i] *= alpha;
+                m[qb] = mn;
+                msub[qb] = (mn == kNegInf) ? 0.0f : mn * scale_log2;
+            }
+        }
+        // P~ = exp2(S scale log2e - m scale log2e), l += row sums, E4M3 operands:
+        // dword 4 kb + r holds elements 4 r .. 4 r + 3 of block kb
+        i32x8 pf[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float rs = 0.0f;
+#pragma unroll
+            for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float e[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        e[u] = fast_exp2(fmaf(s[kbk][qb][4 * r + u], scale_log2, -msub[qb]));
+                        rs += e[u];
+                    }
+                    int w = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+                    w = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], w, true);
+                    pf[qb][4 * kbk + r] = w;
+                }
+            l[qb] += rs;
+        }
+        // O~^T += V^T P~^T
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const uint8_t *base = vb + voff[dt];
+            const i32x2 r0 = lds_read_tr8(base);
+            const i32x2 r1 = lds_read_tr8(base + 8 * ROWB);
+            const i32x2 r2 = lds_read_tr8(base + 32 * ROWB);
+            const i32x2 r3 = lds_read_tr8(base + 40 * ROWB);
+            const i32x8 a = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) oacc[qb][dt] = mfma8(a, pf[qb], oacc[qb][dt]);
+        }
+    };
+
+    auto kslot = [&](auto S) __attribute__((always_inline)) -> uint8_t * {
+        constexpr int s = decltype(S)::value % 3;
+        return s == 0 ? k0 : s == 1 ? k1 : k2;
+    };
+    auto vslot = [&](auto S) __attribute__((always_inline)) -> uint8_t * {
+        constexpr int s = decltype(S)::value % 3;
+        return s == 0 ? v0 : s == 1 ? v1 : v2;
+    };
+    // iteration j (slot j % 3): this wave's loads of tile j are done (tile
+    // j + 1's may be in flight), the barrier publishes every wave's and frees
+    // slot (j + 2) % 3 for tile j + 2; every iteration issues exactly four
+    // loads per wave (tiles past the end are zero fills)
+    auto iter = [&](auto S, int j) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(kWaitVm4);
+        tile_barrier();
+        issue(kslot(Slot<decltype(S)::value + 2>{}), vslot(Slot<decltype(S)::value + 2>{}), j + 2);
+        if (j < wtiles) compute(kslot(S), vslot(S), j, j >= wmask);
+    };
+
+    issue(k0, v0, 0);
+    issue(k1, v1, 1);
+    const int nend = ((ntiles + 2) / 3) * 3;
+    for (int j = 0; j < nend; j += 3) {
+        iter(Slot<0>{}, j);
+        iter(Slot<1>{}, j + 1);
+        iter(Slot<2>{}, j + 2);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);       // no load outlives the kernel
+
+    // ---- epilogue: O = v_scale O~ / l, LSE = m + log l ------------------------
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int qi = qw0 + 32 * qb + c;
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l[qb]), __float_as_uint(l[qb]), false, false);
+        const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const bool valid = (qi < Lq) && (lt > 0.0f);
+        const float inv = valid ? v_scale / lt : 0.0f;
+        if (qi < Nq) {
+            uint16_t *orow = O + (qrow0 + qi) * D;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    uint2 w;
+                    w.x = valid ? pack_bf16x2(oacc[qb][dt][4 * r + 0] * inv, oacc[qb][dt][4 * r + 1] * inv) : 0u;
+                    w.y = valid ? pack_bf16x2(oacc[qb][dt][4 * r + 2] * inv, oacc[qb][dt][4 * r + 3] * inv) : 0u;
+                    *reinterpret_cast<uint2 *>(orow + 32 * dt + 8 * r + 4 * g) = w;
+                }
+            if (LSE && g == 0)
+                LSE[qrow0 + qi] = valid ? (m[qb] * scale_log2 + __log2f(lt)) * kLn2 : kNegInf;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_fp8(const AttnFwdFp8Args &a, hipStream_t s) {
+    const int nqb = (a.seqlen_q + BQ - 1) / BQ;
+    const int nheads = a.batch * a.heads_q;
+    const int64_t blocks = (int64_t)nqb * nheads;
+    if (blocks == 0) return hipSuccess;
+    const int xcd_heads = (nheads % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL(attn_fwd_fp8_d128, dim3((unsigned)blocks), dim3(NT), 0, s,
+                       static_cast<const uint8_t *>(a.q), static_cast<const uint8_t *>(a.k),
+                       static_cast<const uint8_t *>(a.v), static_cast<uint16_t *>(a.o), a.lse,
+                       a.heads_q, a.heads_kv, a.seqlen_q, a.seqlen_k, a.seqlens_q, a.seqlens_k,
+                       a.scale * kLog2e, a.v_scale, a.causal, nqb, xcd_heads);
+    return hipGetLastError();
+}
+
+}  // namespace osm

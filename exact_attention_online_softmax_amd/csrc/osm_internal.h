@@ -36,6 +36,18 @@ struct AttnFwdArgs {
 };
 hipError_t launch_attn_fwd(const AttnFwdArgs &a, hipStream_t s);
 
+// ---- fused attention forward, FP8 (OCP E4M3) inputs -------------------------
+struct AttnFwdFp8Args {
+    const void *q, *k, *v;   // E4M3 codes
+    void *o;                 // bf16
+    float *lse;
+    int batch, heads_q, heads_kv, seqlen_q, seqlen_k;
+    const int32_t *seqlens_q, *seqlens_k;
+    float scale, v_scale;
+    int causal;
+};
+hipError_t launch_attn_fwd_fp8(const AttnFwdFp8Args &a, hipStream_t s);
+
 // ---- attention backward ----------------------------------------------------
 struct AttnBwdArgs {
     const void *q, *k, *v, *o, *dout;

@@ -52,6 +52,47 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
+def _e4m3_table() -> np.ndarray:
+    """fp32 value of each OCP FP8 E4M3 code: sign, 4 exponent bits (bias 7),
+    3 mantissa bits; exponent 0 is subnormal (m 2^-9); S.1111.111 is NaN and
+    there are no infinities (largest finite 448)."""
+    t = np.empty(256, np.float32)
+    for v in range(256):
+        sgn, e, m = v >> 7, (v >> 3) & 15, v & 7
+        if e == 15 and m == 7:
+            x = np.nan
+        elif e == 0:
+            x = m * 2.0 ** -9
+        else:
+            x = (1.0 + m / 8.0) * 2.0 ** (e - 7)
+        t[v] = -x if sgn else x
+    return t
+
+
+E4M3 = _e4m3_table()
+_E4M3_POS = E4M3[:127]                 # codes 0x00..0x7e: 0 .. 448, increasing
+
+
+def to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> OCP FP8 E4M3 codes (uint8), round to nearest, ties to the even
+    code; magnitudes beyond 448 saturate to +-448; NaN -> 0x7f."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    a = np.minimum(np.abs(x), np.float32(448.0))
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 126)   # first code >= a
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - _E4M3_POS[lo]
+    dhi = _E4M3_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(np.signbit(x), code | np.uint8(0x80), code).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def e4m3_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of OCP FP8 E4M3 codes to fp32."""
+    return E4M3[np.ascontiguousarray(b, dtype=np.uint8)]
+
+
 def normal_f32(g: np.random.Generator, shape, sigma: float = 1.0) -> np.ndarray:
     x = g.standard_normal(size=shape, dtype=np.float32)
     if sigma != 1.0:
@@ -84,7 +125,7 @@ class AttnInputs:
     q: np.ndarray            # fp32 [B, Hq, Nq, d] or uint16 bf16 bits
     k: np.ndarray            # [B, Hkv, Nk, d]
     v: np.ndarray
-    dtype: str               # "bf16" or "f32"
+    dtype: str               # "bf16", "f32" or "fp8" (OCP E4M3 codes)
     seqlens_q: np.ndarray | None
     seqlens_k: np.ndarray | None
     scale: float
@@ -94,6 +135,8 @@ class AttnInputs:
         """(q, k, v) as exact fp32 arrays, for the oracle."""
         if self.dtype == "bf16":
             return tuple(bf16_bits_to_f32(a) for a in (self.q, self.k, self.v))
+        if self.dtype == "fp8":
+            return tuple(e4m3_bits_to_f32(a) for a in (self.q, self.k, self.v))
         return self.q, self.k, self.v
 
 
@@ -128,6 +171,8 @@ def attention_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, seed: 
             poison_tail(v, sk, Nk)
     if dtype == "bf16":
         q, k, v = to_bf16_bits(q), to_bf16_bits(k), to_bf16_bits(v)
+    elif dtype == "fp8":
+        q, k, v = to_e4m3_bits(q), to_e4m3_bits(k), to_e4m3_bits(v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     return AttnInputs(q, k, v, dtype, sq, sk, float(scale), bool(causal))

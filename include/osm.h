@@ -130,6 +130,39 @@ osm_status osm_attn_fwd(const void *q, const void *k, const void *v, void *o, fl
                         int32_t causal, osm_stream stream);
 
 /*
+ * osm_attn_fwd_fp8 -- the fused attention forward of osm_attn_fwd with Q, K
+ * and V in FP8 (OCP E4M3 codes, one byte per element): O = v_scale *
+ * softmax(scale * Q K^T) V, plus the per-query log-sum-exp.
+ *
+ * [P3] "Precision, and what can still go wrong": the running m, l and O~
+ * stay in float32 when the inputs are FP8.  The block step is that of
+ * osm_attn_fwd ([P3] "Blocks, the bridge to FlashAttention"); both matrix
+ * products run on the FP8 matrix instruction: Q K^T of E4M3 codes with fp32
+ * accumulation, and P~ V with the weights P~ (at most 2^8 each, relative to
+ * the running reference) rounded to E4M3.
+ *
+ *   q     [batch][heads_q][seqlen_q][head_dim]  (E4M3 codes)
+ *   k, v  [batch][heads_kv][seqlen_k][head_dim] (E4M3 codes)
+ *   o     [batch][heads_q][seqlen_q][head_dim]  (bf16, written)
+ *   lse   fp32 [batch][heads_q][seqlen_q] (written; may be NULL); natural log
+ *         of sum_j exp(scale q.k_j)
+ *   scale multiplies Q K^T (fold the dequantization factors of Q and K in
+ *         here); finite and > 0.  v_scale multiplies O (the dequantization
+ *         factor of V); finite.
+ *   heads, seqlens_q, seqlens_k, causal: as osm_attn_fwd.  Codes past the
+ *         valid lengths may hold anything (NaN codes included).
+ * Supported: head_dim 128; every pointer 16-byte aligned.
+ * Errors: OSM_ERR_NULL, OSM_ERR_SHAPE (as osm_attn_fwd, or v_scale not
+ * finite), OSM_ERR_UNSUPPORTED (other head_dim, a misaligned pointer,
+ * seqlen_k >= 2^24), OSM_ERR_HIP.
+ */
+osm_status osm_attn_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+                            int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t seqlen_q,
+                            int32_t seqlen_k, int32_t head_dim, const int32_t *seqlens_q,
+                            const int32_t *seqlens_k, float scale, float v_scale, int32_t causal,
+                            osm_stream stream);
+
+/*
  * osm_attn_bwd_workspace_bytes -- bytes of device workspace that
  * osm_attn_bwd needs: 8 bytes per query row (batch * heads_q * seqlen_q).
  * Returns 0 for invalid sizes.

@@ -32,7 +32,7 @@ def lib():
 
 def test_header_symbols_exported(lib):
     text = open(HEADER).read()
-    declared = set(re.findall(r"\b(osm_[a-z_]+)\s*\(", text))
+    declared = set(re.findall(r"\b(osm_[a-z0-9_]+)\s*\(", text))
     assert declared == set(osm.EXPORTS), declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -165,6 +165,24 @@ def test_extend_validation(lib):
     assert call(q=None) == 1
     assert call(wsb=ws_ok - 1) == 4
     assert call(ws=ctypes.c_void_p(0x10004)) == 4    # not 256-byte aligned
+
+
+def test_attn_fwd_fp8_validation(lib):
+    def call(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=128, scale=0.1,
+             vs=1.0, causal=0):
+        return lib.osm_attn_fwd_fp8(q, k, v, o, None, B, Hq, Hkv, Nq, Nk, d, None, None, scale, vs,
+                                    causal, None)
+    assert call(B=0) == 2
+    assert call(Hq=3, Hkv=2) == 2
+    assert call(scale=-1.0) == 2
+    assert call(vs=float("nan")) == 2
+    assert call(causal=3) == 2
+    assert call(d=64) == 3
+    assert call(Nk=1 << 24) == 3
+    assert call(Nq=0, q=None) == 0
+    assert call(q=None) == 1
+    assert call(v=None) == 1
+    assert call(o=ctypes.c_void_p(0x10001)) == 3     # not 16-byte aligned
 
 
 def test_attn_bwd_validation(lib):

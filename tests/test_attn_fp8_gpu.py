@@ -1,0 +1,119 @@
+"""osm_attn_fwd_fp8 on the GPU against the oracle: exact attention of the
+decoded E4M3 inputs, on small ragged shapes, padded and NaN-poisoned
+inputs, and sampled rows at the full benchmark size.
+
+Tolerance (the pages state none for FP8): O normwise ||o - o_ref||_F /
+||o_ref||_F <= 5e-2 and max |o - o_ref| <= 5e-2 max |o_ref|; LSE within
+1e-3 (it does not see the rounding of the weights).  An fp32 emulation of
+this arithmetic (weights rounded to E4M3 for the P~V product, O to bf16)
+measured normwise 1.0e-2 to 2.6e-2 and at most 2.3e-2 max |o_ref| on such
+inputs; the rounding of the weights (3 mantissa bits) dominates."""
+import numpy as np
+import pytest
+
+import exact_attention_online_softmax_amd as osm
+from exact_attention_online_softmax_amd import inputs
+from gpu_util import announce, dev_i32, host, host_bits, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+
+def dev_u8(a):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(a, np.uint8)).to("cuda")
+
+
+def run(inp, v_scale=1.0):
+    q, k, v = dev_u8(inp.q), dev_u8(inp.k), dev_u8(inp.v)
+    sq = None if inp.seqlens_q is None else dev_i32(inp.seqlens_q)
+    sk = None if inp.seqlens_k is None else dev_i32(inp.seqlens_k)
+    return osm.attn_fwd_fp8(q, k, v, scale=inp.scale, v_scale=v_scale, causal=inp.causal,
+                            seqlens_q=sq, seqlens_k=sk)
+
+
+def oracle(orc, inp, rows=None, v_scale=1.0):
+    q, k, v = inp.widened()
+    return orc.attention(q, k, v * np.float32(v_scale), scale=inp.scale, causal=inp.causal,
+                         seqlens_q=inp.seqlens_q, seqlens_k=inp.seqlens_k, rows=rows)
+
+
+def check_fp8(o, lse, o_ref, lse_ref):
+    o = o.reshape(-1, o.shape[-1])
+    o_ref = o_ref.reshape(-1, o_ref.shape[-1])
+    lse = lse.reshape(-1)
+    lse_ref = lse_ref.reshape(-1)
+    dead = np.isneginf(lse_ref)
+    assert np.all(np.isneginf(lse[dead])) and np.all(o[dead] == 0.0), "rows with no key: 0 / -inf"
+    assert not np.isnan(o).any() and not np.isnan(lse).any(), "NaN in output"
+    live = ~dead
+    if not live.any():
+        return
+    top = np.abs(o_ref[live]).max()
+    ea = np.abs(o[live] - o_ref[live]).max()
+    assert ea <= 5e-2 * top, f"max abs err {ea} vs max |o_ref| {top}"
+    nw = np.linalg.norm(o[live] - o_ref[live]) / np.linalg.norm(o_ref[live])
+    assert nw <= 5e-2, f"normwise err {nw}"
+    el = np.abs(lse[live] - lse_ref[live]).max()
+    assert el <= 1e-3, f"lse err {el}"
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,causal", [
+    (2, 4, 2, 300, 300, False),
+    (2, 4, 2, 300, 300, True),
+    (1, 2, 1, 129, 517, False),
+    (1, 2, 2, 1, 1, False),
+    (1, 1, 1, 1, 64, True),
+    (3, 8, 1, 64, 200, False),
+    (1, 2, 2, 640, 640, True),
+])
+def test_small(orc, B, Hq, Hkv, Nq, Nk, causal):
+    announce(f"fwd fp8 B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} causal={causal}")
+    inp = inputs.attention_inputs(B, Hq, Hkv, Nq, Nk, 128, seed=9000 + B * 1000 + Nq + Nk,
+                                  causal=causal, dtype="fp8")
+    o, lse = run(inp)
+    check_fp8(host(o), host(lse), *oracle(orc, inp))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_poisoned(orc, causal):
+    """NaN codes past the valid lengths never leak; padded rows are 0 / -inf;
+    bit-identical to zero padding."""
+    announce(f"fwd fp8 varlen poisoned causal={causal}")
+    B, H, N = 4, 2, 400
+    lens = np.array([1, 130, 257, 400], np.int32)
+    inp = inputs.attention_inputs(B, H, H, N, N, 128, seed=71, causal=causal, seqlens_q=lens,
+                                  seqlens_k=lens, poison=True, dtype="fp8")
+    assert (inp.k == 0x7F).any()
+    o, lse = run(inp)
+    oh, lh = host(o), host(lse)
+    check_fp8(oh, lh, *oracle(orc, inp))
+    for b, L in enumerate(lens):
+        assert np.all(oh[b, :, L:] == 0.0) and np.all(np.isneginf(lh[b, :, L:]))
+    clean = [np.where(a == 0x7F, 0, a).astype(np.uint8) for a in (inp.q, inp.k, inp.v)]
+    o0, l0 = run(inputs.AttnInputs(*clean, "fp8", lens, lens, inp.scale, causal))
+    assert np.array_equal(host_bits(o), host_bits(o0)) and np.array_equal(host_bits(lse), host_bits(l0))
+
+
+def test_v_scale_and_key_padding(orc):
+    """v_scale multiplies O; only keys padded (a batch with no key gives
+    0 / -inf)."""
+    announce("fwd fp8 v_scale, key padding")
+    lens = np.array([0, 77, 300], np.int32)
+    inp = inputs.attention_inputs(3, 2, 2, 150, 300, 128, seed=72, seqlens_k=lens, poison=True,
+                                  dtype="fp8", scale=0.05)
+    o, lse = run(inp, v_scale=0.5)
+    check_fp8(host(o), host(lse), *oracle(orc, inp, v_scale=0.5))
+
+
+def test_full_size_sampled(orc):
+    """B4 H32 N4096 d128 non-causal with E4M3 inputs: sampled rows vs the
+    oracle."""
+    announce("fwd fp8 B4 H32 N4096 full size, sampled rows")
+    inp = inputs.attention_inputs(4, 32, 32, 4096, 4096, 128, seed=inputs.SEED_BASE + 10,
+                                  dtype="fp8")
+    o, lse = run(inp)
+    g = np.random.default_rng(10)
+    rows = np.unique(np.concatenate([g.integers(0, 4 * 32 * 4096, 400), [0, 63, 64, 255, 256, 4095]]))
+    o_ref, lse_ref = oracle(orc, inp, rows=rows)
+    check_fp8(host(o).reshape(-1, 128)[rows], host(lse).reshape(-1)[rows], o_ref, lse_ref)
+    assert np.isfinite(host(lse)).all()
