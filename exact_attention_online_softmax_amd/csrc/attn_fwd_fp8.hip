@@ -17,12 +17,21 @@
 //    v_scale (the dequantization factor of V), and the LSE as fp32.
 //
 // Mapping to CDNA4:
-//  * workgroup = 4 wavefronts = 256 queries; each wave owns 64 queries as two
-//    32-query blocks and holds their Q as MFMA B operands (32 bytes per lane
-//    per 64-dim k-step).
+//  * workgroup = 8 wavefronts = 256 queries, two waves per SIMD; each wave
+//    owns 32 queries and holds their Q as MFMA B operands (32 bytes per lane
+//    per 64-dim k-step).  The softmax VALU per MFMA clock is twice the bf16
+//    kernel's (an FP8 MFMA does twice the work per clock), so the second wave
+//    on the SIMD is what keeps the matrix core fed while one wave
+//    exponentiates; 208 registers per wave make that possible.
 //  * tiles of 64 keys (the MFMA's k for P~V): K and V tiles of 64 rows x 128
 //    bytes go from HBM straight into LDS through buffer loads with LDS
-//    destination (rows past Lk read as zeros), through a ring of three slots.
+//    destination (rows past Lk read as zeros), through a ring of four slots
+//    loaded three tiles ahead.
+//  * software pipeline: iteration j issues the score MFMAs of tile j + 1
+//    while the vector ALU exponentiates tile j, then adds P~(j) V(j) to O~.
+//    The scores are read by the VALU, so the score MFMAs write VGPRs (the
+//    compiler is told to use the VGPR form); O~ lives in the AGPRs through
+//    inline assembly.
 //  * key order: row c = 8 r + 4 h + u of a 32-key score block is key
 //    16 h + 4 r + u of that block, so each lane half of the score accumulator
 //    holds 16 consecutive keys.  P~ packs them, in order, into the B operand
@@ -45,18 +54,20 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int D = 128;            // head dim
 constexpr int ROWB = D;           // bytes per E4M3 row
-constexpr int NW = 4;             // wavefronts per workgroup
-constexpr int QW = 64;            // queries per wavefront (two blocks of 32)
+constexpr int NQB = 1;            // 32-query blocks per wavefront
+constexpr int QW = 32 * NQB;      // queries per wavefront
+constexpr int NW = 256 / QW;      // wavefronts per workgroup (two per SIMD)
 constexpr int BQ = QW * NW;       // queries per workgroup
 constexpr int BK = 64;            // keys per tile
 constexpr int NT = 64 * NW;
 constexpr int TILEB = BK * ROWB;  // bytes per K or V tile (8 KiB)
 constexpr int LPW = TILEB / 1024 / NW;   // 1 KiB loads per wave per K (or V) tile
-static_assert(2 * LPW == 4, "kWaitVm4 assumes four loads per wave per tile");
+static_assert(LPW == 1, "the wait counts assume one K and one V load per wave per tile");
 
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
 constexpr int kWaitVm0 = 0x0F70;         // s_waitcnt vmcnt(0)
-constexpr int kWaitVm4 = 0x0F74;         // s_waitcnt vmcnt(4)
+constexpr int kWaitVm2 = 0x0F72;         // s_waitcnt vmcnt(2): one tile's loads in flight
+constexpr int kWaitVm4 = 0x0F74;         // s_waitcnt vmcnt(4): two tiles' loads in flight
 constexpr int kUnitScale = 127;          // E8M0 exponent of 1.0 for the MFMA's block scales
 
 template <int N> struct Slot { static constexpr int value = N; };
@@ -69,6 +80,26 @@ __device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 3) | (((r >> 4) 
 
 __device__ __forceinline__ f32x16 mfma8(const i32x8 &a, const i32x8 &b, const f32x16 &c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kUnitScale, 0, kUnitScale);
+}
+
+// O~^T accumulation with the accumulator pinned to AGPRs (see the header).
+// The hazard recognizer does not look into inline assembly: the VALU writes
+// of the B operand need wait states before the MFMA reads them.
+__device__ __forceinline__ void mfma8_acc(f32x16 &acc, const i32x8 &a, const i32x8 &b, int sc) {
+    asm("s_nop 3\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3" : "+a"(acc) : "v"(a), "v"(b), "v"(sc));
+}
+
+__device__ __forceinline__ void acc_zero8(f32x16 &acc, const i32x8 &z, int sc) {
+    asm volatile("s_nop 3\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %1, 0, %2, %2" : "=a"(acc) : "v"(z), "v"(sc));
+}
+
+// Before ordinary code reads accumulators written by mfma8_acc: wait out the
+// MFMA's result latency (generously: 40 wait states).
+__device__ __forceinline__ void acc_settle8(f32x16 (&o)[NQB][4]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]));
+    if constexpr (NQB == 2)
+        asm volatile("" : "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
 }
 
 __device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t *p) {
@@ -87,8 +118,8 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
                   int Hq, int Hkv, int Nq, int Nk, const int32_t *__restrict__ seqlens_q,
                   const int32_t *__restrict__ seqlens_k, float scale_log2, float v_scale, int causal,
                   int nqb, int xcd_heads) {
-    __shared__ __attribute__((aligned(1024))) uint8_t k0[TILEB], k1[TILEB], k2[TILEB];
-    __shared__ __attribute__((aligned(1024))) uint8_t v0[TILEB], v1[TILEB], v2[TILEB];
+    __shared__ __attribute__((aligned(1024))) uint8_t k0[TILEB], k1[TILEB], k2[TILEB], k3[TILEB];
+    __shared__ __attribute__((aligned(1024))) uint8_t v0[TILEB], v1[TILEB], v2[TILEB], v3[TILEB];
 
     // ---- which (batch, head, query block) ------------------------------
     const int L = blockIdx.x;
@@ -141,9 +172,9 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
 
     // ---- Q (B operands of S^T = K Q^T): lane (g, c) holds row qw0 + 32 qb + c,
     // bytes 64 ks + 32 g .. + 31; rows at or past Lq are zero
-    i32x8 qf[2][2];
+    i32x8 qf[NQB][2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
         const int qi = qw0 + 32 * qb + c;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -157,16 +188,18 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
         }
     }
 
-    f32x16 oacc[2][4];
+    const int unit_scale = kUnitScale;
+    f32x16 oacc[NQB][4];
+    {
+        const i32x8 z8 = {};
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+            for (int dt = 0; dt < 4; ++dt) acc_zero8(oacc[qb][dt], z8, unit_scale);
+    }
+    float m[NQB], msub[NQB], l[NQB];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[qb][dt][i] = 0.0f;
-    float m[2], msub[2], l[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
         m[qb] = kNegInf;     // reference maximum of raw scores q.k
         msub[qb] = 0.0f;     // m * scale * log2(e) (0 while m = -inf)
         l[qb] = 0.0f;        // this lane's part of the running sum
@@ -225,7 +258,7 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
 
     // S^T of one tile: s[kb][qb] element 4 r + u of lane (g, c) is key
     // 32 kb + 16 g + 4 r + u of the tile, query qw0 + 32 qb + c
-    auto qk = [&](const uint8_t *kb, f32x16 (&s)[2][2]) __attribute__((always_inline)) {
+    auto qk = [&](const uint8_t *kb, f32x16 (&s)[2][NQB]) __attribute__((always_inline)) {
         const f32x16 zero = {};
 #pragma unroll
         for (int kbk = 0; kbk < 2; ++kbk)
@@ -235,13 +268,13 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
                 const uint4 hi = *reinterpret_cast<const uint4 *>(kb + 32 * kbk * ROWB + koff[ks][1]);
                 const i32x8 a = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) s[kbk][qb] = mfma8(a, qf[qb][ks], ks ? s[kbk][qb] : zero);
+                for (int qb = 0; qb < NQB; ++qb) s[kbk][qb] = mfma8(a, qf[qb][ks], ks ? s[kbk][qb] : zero);
             }
     };
 
-    auto mask = [&](f32x16 (&s)[2][2], int t) __attribute__((always_inline)) {
+    auto mask = [&](f32x16 (&s)[2][NQB], int t) __attribute__((always_inline)) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < NQB; ++qb) {
             const int qi = qw0 + 32 * qb + c;
             const int lim = (causal ? min(Lk - 1, qi) : Lk - 1) - t * BK - 16 * g;
 #pragma unroll
@@ -252,23 +285,30 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
         }
     };
 
-    auto compute = [&](const uint8_t *kb, const uint8_t *vb, int t, bool masked) __attribute__((always_inline)) {
-        f32x16 s[2][2];
-        qk(kb, s);
-        if (masked) mask(s, t);
+    // iteration body for tile t whose scores are in s: mask, lazy reference,
+    // then (one scheduling region) the scores of tile t + 1 into sn, the
+    // exponentials of tile t, and O~ += P~(t) V(t)
+    auto body = [&](const uint8_t *kn, const uint8_t *vb, int t, f32x16 (&s)[2][NQB], f32x16 (&sn)[2][NQB])
+        __attribute__((always_inline)) {
+        if (t >= wmask) mask(s, t);
         // tile maximum per query (both lane halves), then the lazy reference
-        float tm[2];
+        float tm[NQB];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            float x = fmaxf(s[0][qb][0], s[1][qb][0]);
+        for (int qb = 0; qb < NQB; ++qb) {
+            float x = fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), s[1][qb][0]);
+            x = fmaxf(x, s[1][qb][1]);
 #pragma unroll
-            for (int i = 1; i < 16; ++i) x = fmaxf(x, fmaxf(s[0][qb][i], s[1][qb][i]));
+            for (int i = 2; i < 16; ++i) x = fmaxf(fmaxf(x, s[0][qb][i]), s[1][qb][i]);
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
             tm[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         }
-        if (!__all((tm[0] <= m[0] + lazy_raw) && (tm[1] <= m[1] + lazy_raw))) {
+        bool keep = true;
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < NQB; ++qb) keep = keep && (tm[qb] <= m[qb] + lazy_raw);
+        if (!__all(keep)) {
+            acc_settle8(oacc);
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
                 const float mn = fmaxf(m[qb], tm[qb]);
                 const float alpha = (mn == kNegInf || m[qb] == mn) ? 1.0f
                                   : (m[qb] == kNegInf ? 0.0f : fast_exp2((m[qb] - mn) * scale_log2));
@@ -281,12 +321,14 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
                 msub[qb] = (mn == kNegInf) ? 0.0f : mn * scale_log2;
             }
         }
-        // P~ = exp2(S scale log2e - m scale log2e), l += row sums, E4M3 operands:
-        // dword 4 kb + r holds elements 4 r .. 4 r + 3 of block kb
-        i32x8 pf[2];
+        qk(kn, sn);
+        // P~ = exp2(S scale log2e - m scale log2e), l += row sums (four
+        // partial sums), E4M3 operands: dword 4 kb + r holds elements
+        // 4 r .. 4 r + 3 of block kb
+        i32x8 pf[NQB];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            float rs = 0.0f;
+        for (int qb = 0; qb < NQB; ++qb) {
+            float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
@@ -295,13 +337,13 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         e[u] = fast_exp2(fmaf(s[kbk][qb][4 * r + u], scale_log2, -msub[qb]));
-                        rs += e[u];
+                        rs[u] += e[u];
                     }
                     int w = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
                     w = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], w, true);
                     pf[qb][4 * kbk + r] = w;
                 }
-            l[qb] += rs;
+            l[qb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
         }
         // O~^T += V^T P~^T
 #pragma unroll
@@ -313,42 +355,61 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
             const i32x2 r3 = lds_read_tr8(base + 40 * ROWB);
             const i32x8 a = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) oacc[qb][dt] = mfma8(a, pf[qb], oacc[qb][dt]);
+            for (int qb = 0; qb < NQB; ++qb) mfma8_acc(oacc[qb][dt], a, pf[qb], unit_scale);
+        }
+        // interleave the score MFMAs of tile t + 1 with the exponentials
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
         }
     };
 
     auto kslot = [&](auto S) __attribute__((always_inline)) -> uint8_t * {
-        constexpr int s = decltype(S)::value % 3;
-        return s == 0 ? k0 : s == 1 ? k1 : k2;
+        constexpr int s = decltype(S)::value % 4;
+        return s == 0 ? k0 : s == 1 ? k1 : s == 2 ? k2 : k3;
     };
     auto vslot = [&](auto S) __attribute__((always_inline)) -> uint8_t * {
-        constexpr int s = decltype(S)::value % 3;
-        return s == 0 ? v0 : s == 1 ? v1 : v2;
+        constexpr int s = decltype(S)::value % 4;
+        return s == 0 ? v0 : s == 1 ? v1 : s == 2 ? v2 : v3;
     };
-    // iteration j (slot j % 3): this wave's loads of tile j are done (tile
-    // j + 1's may be in flight), the barrier publishes every wave's and frees
-    // slot (j + 2) % 3 for tile j + 2; every iteration issues exactly four
-    // loads per wave (tiles past the end are zero fills)
+    // iteration j (slot j % 4): this wave's loads of tile j + 1 are done (tile
+    // j + 2's may be in flight); the barrier publishes every wave's and frees
+    // slot (j + 3) % 4 (every wave is past iteration j - 1), which receives
+    // tile j + 3.  Every iteration issues exactly four loads per wave (tiles
+    // past the end are zero fills), so the wait count is the same everywhere.
+    // Two score buffers alternate: even iterations read sa and fill sb.
+    f32x16 sa[2][NQB], sb[2][NQB];
     auto iter = [&](auto S, int j) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(kWaitVm4);
+        constexpr int si = decltype(S)::value;
+        __builtin_amdgcn_s_waitcnt(kWaitVm2);
         tile_barrier();
-        issue(kslot(Slot<decltype(S)::value + 2>{}), vslot(Slot<decltype(S)::value + 2>{}), j + 2);
-        if (j < wtiles) compute(kslot(S), vslot(S), j, j >= wmask);
+        issue(kslot(Slot<si + 3>{}), vslot(Slot<si + 3>{}), j + 3);
+        if (j < wtiles) {
+            if constexpr (si % 2 == 0) body(kslot(Slot<si + 1>{}), vslot(S), j, sa, sb);
+            else body(kslot(Slot<si + 1>{}), vslot(S), j, sb, sa);
+        }
     };
 
     issue(k0, v0, 0);
     issue(k1, v1, 1);
-    const int nend = ((ntiles + 2) / 3) * 3;
-    for (int j = 0; j < nend; j += 3) {
+    issue(k2, v2, 2);
+    __builtin_amdgcn_s_waitcnt(kWaitVm4);       // this wave's part of tile 0
+    tile_barrier();
+    if (wtiles > 0) qk(k0, sa);
+    const int nend = ((ntiles + 3) / 4) * 4;
+    for (int j = 0; j < nend; j += 4) {
         iter(Slot<0>{}, j);
         iter(Slot<1>{}, j + 1);
         iter(Slot<2>{}, j + 2);
+        iter(Slot<3>{}, j + 3);
     }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);       // no load outlives the kernel
 
     // ---- epilogue: O = v_scale O~ / l, LSE = m + log l ------------------------
+    acc_settle8(oacc);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
         const int qi = qw0 + 32 * qb + c;
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l[qb]), __float_as_uint(l[qb]), false, false);
         const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
