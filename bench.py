@@ -118,7 +118,7 @@ def summarize(name, trace_dir, out):
     size (the torch copy kernel run with --copy-calibration)."""
     import csv
     import glob
-    kern = {"fwd": "attn_fwd", "fwd_causal": "attn_fwd", "softmax": "softmax_rows",
+    kern = {"fwd": "attn_fwd_bf16", "fwd_causal": "attn_fwd_bf16", "softmax": "softmax_rows",
             "decode": "decode_split", "merge_lse": "merge_lse", "extend": "decode_split",
             "bwd": "attn_bwd_dkdv", "bwd_causal": "attn_bwd_dkdv", "fwd_fp8": "attn_fwd_fp8"}[name]
     lines = [f"# rocprofv3 summary: {name}", ""]
@@ -138,7 +138,7 @@ def summarize(name, trace_dir, out):
         for (short, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
             lines.append(f"| {short} | {wg} | {len(d)} | {sum(d) / len(d) / 1e3:.1f} | "
                          f"{min(d) / 1e3:.1f} | {max(d) / 1e3:.1f} |")
-        want = {"fwd": ("attn_fwd", 2048), "fwd_causal": ("attn_fwd", 4096),
+        want = {"fwd": ("attn_fwd_bf16", 2048), "fwd_causal": ("attn_fwd_bf16", 4096),
                 "softmax": ("softmax_rows", None), "decode": ("decode_split", None),
                 "merge_lse": ("merge_lse", None), "extend": ("decode_split", None),
                 "bwd": ("attn_bwd_dkdv", None), "bwd_causal": ("attn_bwd_dkdv", None),
