@@ -28,7 +28,9 @@
 //    destination (rows past Lk read as zeros), through a ring of four slots
 //    loaded three tiles ahead.
 //  * software pipeline: iteration j issues the score MFMAs of tile j + 1
-//    while the vector ALU exponentiates tile j, then adds P~(j) V(j) to O~.
+//    while the vector ALU exponentiates tile j, then adds P~(j) V(j) to O~,
+//    and last masks tile j + 1 and takes its maximum (under the P~V MFMAs),
+//    so that iteration j + 1 starts with the reference decision.
 //    The scores are read by the VALU, so the score MFMAs write VGPRs (the
 //    compiler is told to use the VGPR form); O~ lives in the AGPRs through
 //    inline assembly.
@@ -288,11 +290,9 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
     // iteration body for tile t whose scores are in s: mask, lazy reference,
     // then (one scheduling region) the scores of tile t + 1 into sn, the
     // exponentials of tile t, and O~ += P~(t) V(t)
-    auto body = [&](const uint8_t *kn, const uint8_t *vb, int t, f32x16 (&s)[2][NQB], f32x16 (&sn)[2][NQB])
-        __attribute__((always_inline)) {
+    // mask (when tile t needs it) and tile maximum of scores s of tile t
+    auto tmax = [&](f32x16 (&s)[2][NQB], int t, float (&tm)[NQB]) __attribute__((always_inline)) {
         if (t >= wmask) mask(s, t);
-        // tile maximum per query (both lane halves), then the lazy reference
-        float tm[NQB];
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
             float x = fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), s[1][qb][0]);
@@ -302,6 +302,13 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
             tm[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         }
+    };
+    float tmc[NQB];     // tile maximum of the scores whose softmax is next
+    auto body = [&](const uint8_t *kn, const uint8_t *vb, int t, f32x16 (&s)[2][NQB], f32x16 (&sn)[2][NQB])
+        __attribute__((always_inline)) {
+        float tm[NQB];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) tm[qb] = tmc[qb];
         bool keep = true;
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) keep = keep && (tm[qb] <= m[qb] + lazy_raw);
@@ -363,6 +370,7 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
         }
+        tmax(sn, t + 1, tmc);
     };
 
     auto kslot = [&](auto S) __attribute__((always_inline)) -> uint8_t * {
@@ -396,7 +404,10 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
     issue(k2, v2, 2);
     __builtin_amdgcn_s_waitcnt(kWaitVm4);       // this wave's part of tile 0
     tile_barrier();
-    if (wtiles > 0) qk(k0, sa);
+    if (wtiles > 0) {
+        qk(k0, sa);
+        tmax(sa, 0, tmc);
+    }
     const int nend = ((ntiles + 3) / 4) * 4;
     for (int j = 0; j < nend; j += 4) {
         iter(Slot<0>{}, j);
