@@ -293,18 +293,22 @@ merge_partials_kernel(const float *__restrict__ pm, const float *__restrict__ pl
         for (int k = 0; k < NDL; ++k) acc[k] = 0.0f;
         float lsum = 0.0f;
         if (m != kNegInf) {
-            constexpr int U = 4;
+            // Every load of a group of U pieces is issued before any weight
+            // is known (one memory round trip per group); a piece with m = -inf
+            // is the empty set and is dropped by a select, so whatever its l
+            // and O~ slots hold never reaches the sums.
+            constexpr int U = 8;
             for (int c0 = wave; c0 < C; c0 += MRG_WAVES * U) {
-                float w[U], lv[U], ov[U][NDL];
+                float mc[U], lv[U], ov[U][NDL];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int c = c0 + u * MRG_WAVES;
-                    const float mc = (c < C) ? pmr[c] : kNegInf;
-                    w[u] = (mc == kNegInf) ? 0.0f : exp_acc(mc - m);
+                    mc[u] = kNegInf;
                     lv[u] = 0.0f;
 #pragma unroll
                     for (int k = 0; k < NDL; ++k) ov[u][k] = 0.0f;
-                    if (w[u] != 0.0f) {
+                    if (c < C) {
+                        mc[u] = pmr[c];
                         lv[u] = pl[r * C + c];
                         const float *oc = po + (r * C + c) * HD;
 #pragma unroll
@@ -314,9 +318,11 @@ merge_partials_kernel(const float *__restrict__ pm, const float *__restrict__ pl
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    lsum = fmaf(w[u], lv[u], lsum);
+                    const bool live = mc[u] != kNegInf;
+                    const float w = live ? exp_acc(mc[u] - m) : 0.0f;
+                    lsum = live ? fmaf(w, lv[u], lsum) : lsum;
 #pragma unroll
-                    for (int k = 0; k < NDL; ++k) acc[k] = fmaf(w[u], ov[u][k], acc[k]);
+                    for (int k = 0; k < NDL; ++k) acc[k] = live ? fmaf(w, ov[u][k], acc[k]) : acc[k];
                 }
             }
         }
