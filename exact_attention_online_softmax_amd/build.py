@@ -29,9 +29,11 @@ FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-
 # inputs.  Its score MFMAs must write VGPRs (the softmax reads them), so the
 # compiler is told to select the VGPR form of the MFMA builtins; the output
 # accumulators stay in AGPRs through inline assembly.  The FP8 forward is
-# built the same way, for the same reasons.
+# built the same way, for the same reasons, and so is the backward (its
+# gradient accumulators are the AGPR-resident ones).
 EXTRA = {"attn_fwd.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=true"],
-         "attn_fwd_fp8.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+         "attn_fwd_fp8.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+         "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 def _compile(src: str) -> str:

@@ -16,8 +16,11 @@
 //    units (lse2 = lse log2 e, so P = exp2(s scale log2 e - lse2)).  Rows
 //    that see no key (padding, or lse = -inf) get (lse2, D) = (+inf, 0): their
 //    rebuilt weights are exactly 0 and they add nothing.
-//  * attn_bwd_dkdv: key-major.  A workgroup owns 128 keys of one key/value
-//    head, 32 per wave, whose K and V stay in registers as MFMA operands.
+//  * attn_bwd_dkdv: key-major.  A workgroup owns 256 keys of one key/value
+//    head, 32 per wave, eight waves (two per SIMD, so one wave's matrix
+//    products overlap the other's exponentials and LDS reads); each wave's
+//    K and V stay in registers as MFMA operands and its dK, dV accumulators
+//    in the AGPRs.
 //    Every query row that can see those keys -- all query heads that read
 //    the key/value head -- streams through LDS, 128 rows of Q and dO per
 //    stage, double-buffered.  Per 32-query block: S = Q K^T and dP = dO V^T
@@ -81,6 +84,26 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t *p) {
     const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (s16x4 __attribute__((address_space(3))) *)(p));
     return __builtin_bit_cast(bf16x4, r);
+}
+
+// Accumulation MFMA with the accumulator pinned to AGPRs.  The products
+// whose results the vector ALU reads (S, dP) write VGPRs (the file is built
+// with the VGPR form of the MFMA builtins); the gradient accumulators, read
+// only at the end, fit only in the AGPRs, so their MFMAs are inline
+// assembly.  The hazard recognizer does not look into inline assembly: two
+// wait states let a VALU-written operand settle before the MFMA reads it.
+__device__ __forceinline__ void mfma_acc(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+__device__ __forceinline__ void acc_zero(f32x16 &acc, const bf16x8 &z) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(z));
+}
+
+// Before ordinary code reads accumulators written by mfma_acc: wait out the
+// MFMA result latency (24 wait states; the compiler's model asks for 12).
+__device__ __forceinline__ void acc_settle(f32x16 (&o)[4]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]));
 }
 
 __device__ __forceinline__ bf16x8 cat4(const bf16x4 &lo, const bf16x4 &hi) {
@@ -155,14 +178,14 @@ attn_bwd_pre(const uint16_t *__restrict__ O, const uint16_t *__restrict__ dO,
 // ---------------------------------------------------------------------------
 // attn_bwd_dkdv
 // ---------------------------------------------------------------------------
-constexpr int KV_NW = 4;                       // wavefronts per workgroup
+constexpr int KV_NW = 8;                       // wavefronts per workgroup (two per SIMD)
 constexpr int KV_KW = 32;                      // keys per wavefront
 constexpr int KV_BK = KV_KW * KV_NW;           // keys per workgroup
 constexpr int KV_NT = 64 * KV_NW;
 constexpr int KV_QT = 128;                     // query rows per LDS stage
 constexpr int KV_STB = KV_QT * ROWB;           // bytes of Q (or dO) per stage
 constexpr int KV_BLK = KV_STB / 1024 / KV_NW;  // 1 KiB DMA blocks per wave per array per stage
-static_assert(KV_QT * 8 == 256 * KV_NW, "one 4-byte-per-lane load per wave covers a stage's (lse2, D)");
+static_assert(KV_QT * 8 == 256 * 4, "waves 0-3 load a stage's (lse2, D), 256 bytes each");
 
 template <bool CAUSAL>
 __global__ void __launch_bounds__(KV_NT, 1)
@@ -235,13 +258,14 @@ attn_bwd_dkdv(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
         }
     }
     f32x16 dka[4], dva[4];
+    {
+        const bf16x8 z8 = {};
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            dka[dt][i] = 0.0f;
-            dva[dt][i] = 0.0f;
+        for (int dt = 0; dt < 4; ++dt) {
+            acc_zero(dka[dt], z8);
+            acc_zero(dva[dt], z8);
         }
+    }
 
     // ---- the query rows to visit: every head of the group, rows qbeg..Lq-1
     // (with a causal mask, queries before kb0 see none of these keys)
@@ -251,9 +275,9 @@ attn_bwd_dkdv(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 
     // DMA of one stage: wave w fills 1 KiB blocks KV_BLK w .. +KV_BLK-1 (four
     // rows each) of the Q and dO arrays, lane l row 4 blk + l/16, slot l%16
-    // (holding global chunk slot ^ swz(row)); and (lse2, D) of rows
-    // 32 w .. 32 w + 31.  Rows at or past Lq read as zeros: their Q and dO
-    // are 0, so whatever their weight, they add nothing.
+    // (holding global chunk slot ^ swz(row)); waves 0-3 also load (lse2, D)
+    // of rows 32 w .. 32 w + 31.  Rows at or past Lq read as zeros: their Q
+    // and dO are 0, so whatever their weight, they add nothing.
     uint32_t dmo[KV_BLK];
 #pragma unroll
     for (int i = 0; i < KV_BLK; ++i) {
@@ -272,7 +296,7 @@ attn_bwd_dkdv(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
         for (int i = 0; i < KV_BLK; ++i) dma16(rq, qd + (KV_BLK * wave + i) * 1024, dmo[i]);
 #pragma unroll
         for (int i = 0; i < KV_BLK; ++i) dma16(ro, od + (KV_BLK * wave + i) * 1024, dmo[i]);
-        dma4(rl, reinterpret_cast<uint8_t *>(ld) + 256 * wave, 256 * wave + 4 * lane);
+        if (wave < 4) dma4(rl, reinterpret_cast<uint8_t *>(ld) + 256 * wave, 256 * wave + 4 * lane);
     };
 
     // operand offsets within a 32-row block of a stage.  Row-wise A operand
@@ -340,8 +364,8 @@ attn_bwd_dkdv(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                                        lds_read_tr(ob + 16 * hh * ROWB + thi[dt]));
                 const bf16x8 aq = cat4(lds_read_tr(qb + 16 * hh * ROWB + tlo[dt]),
                                        lds_read_tr(qb + 16 * hh * ROWB + thi[dt]));
-                dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb[hh], dva[dt], 0, 0, 0);
-                dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, db[hh], dka[dt], 0, 0, 0);
+                mfma_acc(dva[dt], ao, pb[hh]);
+                mfma_acc(dka[dt], aq, db[hh]);
             }
     };
 
@@ -373,6 +397,8 @@ attn_bwd_dkdv(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     }
 
     // ---- epilogue: dK = scale dK~, dV; keys past Lk get zeros --------------
+    acc_settle(dka);
+    acc_settle(dva);
     const int key = kw0 + c;
     if (key < Nk) {
         const bool valid = key < Lk;
@@ -483,12 +509,13 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
         dd[qb] = x.y;
     }
     f32x16 dqa[2][4];
+    {
+        const bf16x8 z8 = {};
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) dqa[qb][dt][i] = 0.0f;
+            for (int dt = 0; dt < 4; ++dt) acc_zero(dqa[qb][dt], z8);
+    }
 
     // tile DMA: load i of wave w fills LDS block DQ_LPW w + i (rows 4 blk ..
     // + 3) of a slot; lane l row 4 blk + l/16, slot l%16.  Rows at or past
@@ -576,8 +603,7 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                 const bf16x8 a = cat4(lds_read_tr(kb + 16 * hh * ROWB + tlo[dt]),
                                       lds_read_tr(kb + 16 * hh * ROWB + thi[dt]));
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-                    dqa[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, db[qb][hh], dqa[qb][dt], 0, 0, 0);
+                for (int qb = 0; qb < 2; ++qb) mfma_acc(dqa[qb][dt], a, db[qb][hh]);
             }
     };
 
@@ -612,6 +638,8 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     __builtin_amdgcn_s_waitcnt(kWaitVm0);       // no load outlives the kernel
 
     // ---- epilogue: dQ = scale dQ~; rows past Lq get zeros ------------------
+    acc_settle(dqa[0]);
+    acc_settle(dqa[1]);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         const int qi = qw0 + 32 * qb + c;
