@@ -29,9 +29,10 @@
 //    transposed operands read from LDS with ds_read_b64_tr_b16.  dK and dV
 //    sum over the whole head group in registers: no atomics.
 //  * attn_bwd_dq: query-major, laid out like the forward.  A workgroup owns
-//    256 queries (64 per wave, Q and dO fragments in registers) and streams
-//    K and V tiles of 32 keys through a ring of three LDS slots: S^T = K Q^T,
-//    dP^T = V dO^T, dS^T, and dQ^T += K^T dS^T.
+//    256 queries (32 per wave, eight waves, two per SIMD; Q and dO fragments
+//    in registers, dQ accumulators in the AGPRs) and streams K and V tiles of
+//    32 keys through a ring of three LDS slots: S^T = K Q^T, dP^T = V dO^T,
+//    dS^T, and dQ^T += K^T dS^T.
 // Splitting dQ from dK/dV computes S and dP twice (7 matrix products per
 // score tile instead of 5) but needs no atomic accumulation, so the result
 // is deterministic.
@@ -62,7 +63,7 @@ constexpr float kPosInf = __builtin_inff();
 constexpr int kRsrcWord3 = 0x00020000;
 // s_waitcnt encodings (gfx9): vmcnt in bits 3:0 and 15:14, lgkmcnt 11:8.
 constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitVm4 = 0x0F74;
+constexpr int kWaitVm2 = 0x0F72;
 
 template <int N> struct Slot { static constexpr int value = N; };
 
@@ -422,14 +423,15 @@ attn_bwd_dkdv(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 // ---------------------------------------------------------------------------
 // attn_bwd_dq
 // ---------------------------------------------------------------------------
-constexpr int DQ_NW = 4;                       // wavefronts per workgroup
-constexpr int DQ_QW = 64;                      // queries per wavefront (two blocks of 32)
+constexpr int DQ_NQB = 1;                      // 32-query blocks per wavefront
+constexpr int DQ_QW = 32 * DQ_NQB;             // queries per wavefront
+constexpr int DQ_NW = 256 / DQ_QW;             // wavefronts per workgroup (two per SIMD)
 constexpr int DQ_BQ = DQ_QW * DQ_NW;           // queries per workgroup
 constexpr int DQ_BK = 32;                      // keys per tile
 constexpr int DQ_NT = 64 * DQ_NW;
 constexpr int DQ_TILEB = DQ_BK * ROWB;         // bytes per K or V tile
 constexpr int DQ_LPW = DQ_TILEB / 1024 / DQ_NW;  // 1 KiB loads per wave per K (or V) tile
-static_assert(2 * DQ_LPW == 4, "kWaitVm4 assumes four loads per wave per tile");
+static_assert(DQ_LPW == 1, "kWaitVm2 assumes two loads per wave per tile");
 
 __global__ void __launch_bounds__(DQ_NT, 1)
 attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
@@ -464,7 +466,7 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const int wave = rfl(tid >> 6);
     const int g = lane >> 5, c = lane & 31;
     const int q0 = qb0 * DQ_BQ;
-    const int qw0 = q0 + DQ_QW * wave;           // queries qw0 + 32 qb + c, qb = 0, 1
+    const int qw0 = q0 + DQ_QW * wave;           // queries qw0 + 32 qb + c
     const size_t qrow0 = (size_t)(b * Hq + h) * Nq;
     const uint16_t *Kh = K + (size_t)(b * Hkv + kvh) * Nk * D;
     const uint16_t *Vh = V + (size_t)(b * Hkv + kvh) * Nk * D;
@@ -489,10 +491,10 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 
     // Q and dO fragments (B operands): lane (g, c) holds row qw0 + 32 qb + c,
     // dims 64 g + 8 ks + 0..7; rows at or past Lq are zero
-    bf16x8 qf[2][8], df[2][8];
-    float l2[2], dd[2];
+    bf16x8 qf[DQ_NQB][8], df[DQ_NQB][8];
+    float l2[DQ_NQB], dd[DQ_NQB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < DQ_NQB; ++qb) {
         const int qi = qw0 + 32 * qb + c;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
@@ -508,11 +510,11 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
         l2[qb] = x.x;
         dd[qb] = x.y;
     }
-    f32x16 dqa[2][4];
+    f32x16 dqa[DQ_NQB][4];
     {
         const bf16x8 z8 = {};
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < DQ_NQB; ++qb)
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) acc_zero(dqa[qb][dt], z8);
     }
@@ -557,9 +559,9 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 
     // key 32 t + 8 r + 4 g + u is visible to query qi iff it is
     // <= min(Lk - 1, qi) (causal) or <= Lk - 1
-    auto mask = [&](f32x16 (&s)[2], int t) __attribute__((always_inline)) {
+    auto mask = [&](f32x16 (&s)[DQ_NQB], int t) __attribute__((always_inline)) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < DQ_NQB; ++qb) {
             const int qi = qw0 + 32 * qb + c;
             const int lim = (causal ? min(Lk - 1, qi) : Lk - 1) - t * DQ_BK - 4 * g;
 #pragma unroll
@@ -572,22 +574,22 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 
     auto compute = [&](const uint8_t *kb, const uint8_t *vb, int t, bool masked) __attribute__((always_inline)) {
         const f32x16 zero = {};
-        f32x16 s[2], dp[2];
+        f32x16 s[DQ_NQB], dp[DQ_NQB];
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(kb + aoff[ks]);
             const bf16x8 av = *reinterpret_cast<const bf16x8 *>(vb + aoff[ks]);
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
+            for (int qb = 0; qb < DQ_NQB; ++qb) {
                 s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[qb][ks], ks ? s[qb] : zero, 0, 0, 0);
                 dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, df[qb][ks], ks ? dp[qb] : zero, 0, 0, 0);
             }
         }
         if (masked) mask(s, t);
         // dS^T = P^T (dP^T - D), P^T = exp2(S^T scale log2e - lse2): one query per lane
-        bf16x8 db[2][2];
+        bf16x8 db[DQ_NQB][2];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < DQ_NQB; ++qb) {
             float e[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i)
@@ -603,7 +605,7 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                 const bf16x8 a = cat4(lds_read_tr(kb + 16 * hh * ROWB + tlo[dt]),
                                       lds_read_tr(kb + 16 * hh * ROWB + thi[dt]));
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) mfma_acc(dqa[qb][dt], a, db[qb][hh]);
+                for (int qb = 0; qb < DQ_NQB; ++qb) mfma_acc(dqa[qb][dt], a, db[qb][hh]);
             }
     };
 
@@ -621,7 +623,7 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     // issues exactly four loads per wave (tiles past the end are zero fills),
     // so the wait count is the same everywhere.
     auto iter = [&](auto S, int j) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(kWaitVm4);
+        __builtin_amdgcn_s_waitcnt(kWaitVm2);
         tile_barrier();
         issue(kslot(Slot<decltype(S)::value + 2>{}), vslot(Slot<decltype(S)::value + 2>{}), j + 2);
         if (j < wtiles) compute(kslot(S), vslot(S), j, j >= wmask);
@@ -638,10 +640,10 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     __builtin_amdgcn_s_waitcnt(kWaitVm0);       // no load outlives the kernel
 
     // ---- epilogue: dQ = scale dQ~; rows past Lq get zeros ------------------
-    acc_settle(dqa[0]);
-    acc_settle(dqa[1]);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < DQ_NQB; ++qb) acc_settle(dqa[qb]);
+#pragma unroll
+    for (int qb = 0; qb < DQ_NQB; ++qb) {
         const int qi = qw0 + 32 * qb + c;
         if (qi < Nq) {
             const bool valid = qi < Lq;
