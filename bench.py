@@ -320,12 +320,12 @@ def main():
         q7 = bf16_dev(inp7.q[:, :, 0, :], torch)
         k7, v7 = bf16_dev(inp7.k, torch), bf16_dev(inp7.v, torch)
         state7 = osm.attn_state(B7, Hq7, D7)
-        ws7 = torch.empty(osm.decode_workspace_bytes(B7, Hq7, N7, D7, 256), dtype=torch.uint8, device="cuda")
+        ws7 = torch.empty(osm.decode_workspace_bytes(B7, Hq7, N7, D7, 512), dtype=torch.uint8, device="cuda")
         scale7 = inp7.scale
         del inp7
-        calls["extend"] = lambda: osm.attn_extend(q7, k7, v7, state7, scale=scale7, split_size=256,
+        calls["extend"] = lambda: osm.attn_extend(q7, k7, v7, state7, scale=scale7, split_size=512,
                                                   workspace=ws7)
-        pieces7 = N7 // 256
+        pieces7 = N7 // 512
         work["extend"] = ("hbm", float(B7 * Hkv7 * N7 * D7 * 2 * 2 + B7 * Hq7 * D7 * 2
                                        + 2 * B7 * Hq7 * (D7 + 2) * 4 + 2 * B7 * Hq7 * pieces7 * (D7 + 2) * 4),
                           "B16 Hq32 Hkv8 d128 bf16, 4096 new keys folded into a persisted state")

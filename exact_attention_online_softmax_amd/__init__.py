@@ -333,7 +333,7 @@ def attn_state(batch, heads_q, head_dim, device="cuda"):
             torch.zeros((rows, head_dim), dtype=torch.float32, device=device))
 
 
-def attn_extend(q, k_new, v_new, state, *, scale=None, split_size=256, workspace=None):
+def attn_extend(q, k_new, v_new, state, *, scale=None, split_size=512, workspace=None):
     """Fold new keys k_new, v_new [B, Hkv, n, d] into the streaming summary
     `state` = (m, l, O~) of the queries q [B, Hq, d], in place."""
     torch = _torch()

@@ -73,6 +73,7 @@ def test_fresh_state_equals_split_decode(orc):
 
 
 def test_bench_shape_sampled(orc):
-    """The measured shape: B16 Hq32 Hkv8 d128 bf16, four chunks of 4096 keys."""
-    announce("extend B16 Hq32 Hkv8 d128 bf16, 4 x 4096 keys")
-    stream(orc, 16, 32, 8, 128, "bf16", [4096] * 4, 5300, split=256, check_every=False)
+    """The measured shape and launch configuration: B16 Hq32 Hkv8 d128 bf16,
+    four chunks of 4096 keys, 512-key pieces."""
+    announce("extend B16 Hq32 Hkv8 d128 bf16, 4 x 4096 keys, split 512")
+    stream(orc, 16, 32, 8, 128, "bf16", [4096] * 4, 5300, split=512, check_every=False)
