@@ -16,6 +16,11 @@ inline osm_status hip_status(hipError_t e) { return e == hipSuccess ? OSM_OK : O
 
 constexpr int64_t kMaxDecodeScores = 16384;   // heads-per-group * split_size (64 KiB of LDS)
 
+// (batch, head) pairs are numbered with 32-bit integers inside the kernels
+inline bool too_many_heads(int32_t batch, int32_t heads) { return (int64_t)batch * heads > INT32_MAX; }
+
+inline bool misaligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
+
 }  // namespace
 
 extern "C" {
@@ -51,11 +56,13 @@ osm_status osm_attn_fwd(const void *q, const void *k, const void *v, void *o, fl
     if (batch < 1 || heads_q < 1 || heads_kv < 1 || head_dim < 1 || seqlen_q < 0 || seqlen_k < 0 ||
         heads_q % heads_kv != 0 || !(scale > 0.0f) || !isfinite(scale) || (causal != 0 && causal != 1))
         return OSM_ERR_SHAPE;
-    if (dtype != OSM_BF16 || head_dim != 128) return OSM_ERR_UNSUPPORTED;
+    if (dtype != OSM_BF16 || head_dim != 128 || too_many_heads(batch, heads_q)) return OSM_ERR_UNSUPPORTED;
     // one head's K (or V) rows are addressed with 32-bit byte offsets
     if ((int64_t)seqlen_k * head_dim * 2 >= ((int64_t)1 << 31)) return OSM_ERR_UNSUPPORTED;
     if (seqlen_q == 0) return OSM_OK;
     if (!q || !o || (seqlen_k > 0 && (!k || !v))) return OSM_ERR_NULL;
+    // rows are read and written 16 bytes at a time
+    if (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(o)) return OSM_ERR_UNSUPPORTED;
     osm::AttnFwdArgs a{q, k, v, o, lse, batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim,
                        seqlens_q, seqlens_k, scale, causal};
     return hip_status(osm::launch_attn_fwd(a, static_cast<hipStream_t>(stream)));
@@ -70,15 +77,13 @@ osm_status osm_attn_fwd_fp8(const void *q, const void *k, const void *v, void *o
         heads_q % heads_kv != 0 || !(scale > 0.0f) || !isfinite(scale) || !isfinite(v_scale) ||
         (causal != 0 && causal != 1))
         return OSM_ERR_SHAPE;
-    if (head_dim != 128) return OSM_ERR_UNSUPPORTED;
+    if (head_dim != 128 || too_many_heads(batch, heads_q)) return OSM_ERR_UNSUPPORTED;
     // one head's K (or V) rows are addressed with 32-bit byte offsets
     if ((int64_t)seqlen_k * head_dim >= ((int64_t)1 << 31)) return OSM_ERR_UNSUPPORTED;
     if (seqlen_q == 0) return OSM_OK;
     if (!q || !o || (seqlen_k > 0 && (!k || !v))) return OSM_ERR_NULL;
     // operands are read 16 bytes at a time
-    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
-         reinterpret_cast<uintptr_t>(o)) & 15)
-        return OSM_ERR_UNSUPPORTED;
+    if (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(o)) return OSM_ERR_UNSUPPORTED;
     osm::AttnFwdFp8Args a{q, k, v, o, lse, batch, heads_q, heads_kv, seqlen_q, seqlen_k,
                           seqlens_q, seqlens_k, scale, v_scale, causal};
     return hip_status(osm::launch_attn_fwd_fp8(a, static_cast<hipStream_t>(stream)));
@@ -99,7 +104,7 @@ osm_status osm_attn_bwd(const void *q, const void *k, const void *v, const void 
     if (batch < 1 || heads_q < 1 || heads_kv < 1 || head_dim < 1 || seqlen_q < 0 || seqlen_k < 0 ||
         heads_q % heads_kv != 0 || !(scale > 0.0f) || !isfinite(scale) || (causal != 0 && causal != 1))
         return OSM_ERR_SHAPE;
-    if (dtype != OSM_BF16 || head_dim != 128) return OSM_ERR_UNSUPPORTED;
+    if (dtype != OSM_BF16 || head_dim != 128 || too_many_heads(batch, heads_q)) return OSM_ERR_UNSUPPORTED;
     // one head's rows are addressed with 32-bit byte offsets
     if ((int64_t)seqlen_k * head_dim * 2 >= ((int64_t)1 << 31) ||
         (int64_t)seqlen_q * head_dim * 2 >= ((int64_t)1 << 31))
@@ -110,7 +115,7 @@ osm_status osm_attn_bwd(const void *q, const void *k, const void *v, const void 
     // operands are read 16 bytes at a time
     const void *ptrs[] = {q, k, v, o, dout, dq, dk, dv};
     for (const void *p : ptrs)
-        if (reinterpret_cast<uintptr_t>(p) & 15) return OSM_ERR_UNSUPPORTED;
+        if (misaligned16(p)) return OSM_ERR_UNSUPPORTED;
     const size_t need = osm::attn_bwd_workspace_bytes(batch, heads_q, seqlen_q);
     if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255)))
         return OSM_ERR_WORKSPACE;
@@ -137,9 +142,12 @@ osm_status osm_attn_decode_splitkv(const void *q, const void *k_cache, const voi
     const int group = heads_q / heads_kv;
     if ((dtype != OSM_F32 && dtype != OSM_BF16) || (head_dim != 64 && head_dim != 128) ||
         (group != 1 && group != 2 && group != 4 && group != 8) || split_size % 64 != 0 ||
-        split_size > 8192 || (int64_t)group * split_size > kMaxDecodeScores)
+        split_size > 8192 || (int64_t)group * split_size > kMaxDecodeScores ||
+        too_many_heads(batch, heads_q))
         return OSM_ERR_UNSUPPORTED;
     if (!q || !k_cache || !v_cache || !o || !seqlens_k) return OSM_ERR_NULL;
+    // rows are read 16 bytes at a time
+    if (misaligned16(q) || misaligned16(k_cache) || misaligned16(v_cache)) return OSM_ERR_UNSUPPORTED;
     const osm::DecodeLayout lay = osm::decode_layout(batch, heads_q, max_seqlen_k, head_dim, split_size);
     if (!workspace || workspace_bytes < lay.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
         return OSM_ERR_WORKSPACE;
@@ -180,11 +188,14 @@ osm_status osm_attn_extend(const void *q, const void *k_new, const void *v_new, 
     const int group = heads_q / heads_kv;
     if ((dtype != OSM_F32 && dtype != OSM_BF16) || (head_dim != 64 && head_dim != 128) ||
         (group != 1 && group != 2 && group != 4 && group != 8) || split_size % 64 != 0 ||
-        split_size > 8192 || (int64_t)group * split_size > kMaxDecodeScores)
+        split_size > 8192 || (int64_t)group * split_size > kMaxDecodeScores ||
+        too_many_heads(batch, heads_q))
         return OSM_ERR_UNSUPPORTED;
     if (!state_m || !state_l || !state_o) return OSM_ERR_NULL;
     if (n_new == 0) return OSM_OK;                 // no new keys: the state is already the answer
     if (!q || !k_new || !v_new) return OSM_ERR_NULL;
+    // rows are read 16 bytes at a time
+    if (misaligned16(q) || misaligned16(k_new) || misaligned16(v_new)) return OSM_ERR_UNSUPPORTED;
     const osm::DecodeLayout lay = osm::decode_layout(batch, heads_q, n_new, head_dim, split_size);
     if (!workspace || workspace_bytes < lay.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
         return OSM_ERR_WORKSPACE;

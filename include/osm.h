@@ -116,12 +116,14 @@ osm_status osm_softmax_rows(const float *x, float *y, int64_t rows, int64_t cols
  *         written as O = 0, LSE = -inf.
  *   scale multiplies Q K^T (for example 1/sqrt(head_dim)); must be finite and > 0.
  *   causal 0 or 1 (top-left aligned: j <= i).
- * Supported: dtype OSM_BF16, head_dim 128; fp32 accumulation of both
- * products, fp32 running state, O rounded to bf16 once at the end.
+ * Supported: dtype OSM_BF16, head_dim 128, batch * heads_q < 2^31; q, k,
+ * v and o 16-byte aligned; fp32 accumulation of both products, fp32
+ * running state, O rounded to bf16 once at the end.
  * Errors: OSM_ERR_NULL, OSM_ERR_SHAPE (non-positive batch/heads/head_dim,
  * negative seqlens, heads_q % heads_kv != 0, scale not finite or <= 0),
- * OSM_ERR_UNSUPPORTED (other dtype or head_dim, or one head's K rows
- * spanning 2 GiB or more: seqlen_k >= 2^23 at head_dim 128), OSM_ERR_HIP.
+ * OSM_ERR_UNSUPPORTED (other dtype or head_dim, a misaligned pointer,
+ * batch * heads_q >= 2^31, or one head's K rows spanning 2 GiB or more:
+ * seqlen_k >= 2^23 at head_dim 128), OSM_ERR_HIP.
  */
 osm_status osm_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                         osm_dtype dtype, int32_t batch, int32_t heads_q, int32_t heads_kv,
@@ -151,10 +153,11 @@ osm_status osm_attn_fwd(const void *q, const void *k, const void *v, void *o, fl
  *         factor of V); finite.
  *   heads, seqlens_q, seqlens_k, causal: as osm_attn_fwd.  Codes past the
  *         valid lengths may hold anything (NaN codes included).
- * Supported: head_dim 128; every pointer 16-byte aligned.
+ * Supported: head_dim 128, batch * heads_q < 2^31; every pointer 16-byte
+ * aligned.
  * Errors: OSM_ERR_NULL, OSM_ERR_SHAPE (as osm_attn_fwd, or v_scale not
  * finite), OSM_ERR_UNSUPPORTED (other head_dim, a misaligned pointer,
- * seqlen_k >= 2^24), OSM_ERR_HIP.
+ * batch * heads_q >= 2^31, seqlen_k >= 2^24), OSM_ERR_HIP.
  */
 osm_status osm_attn_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
                             int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t seqlen_q,
@@ -195,12 +198,13 @@ size_t osm_attn_bwd_workspace_bytes(int32_t batch, int32_t heads_q, int32_t seql
  * Three kernels are enqueued on `stream`: the per-row (lse, dO . O), then
  * dK/dV (key-major), then dQ (query-major).  No atomics: the result is
  * deterministic.
- * Supported: dtype OSM_BF16, head_dim 128; fp32 accumulation, P and dS
- * rounded to bf16 as matrix-product operands, gradients rounded to bf16
- * once at the end; every pointer 16-byte aligned.
+ * Supported: dtype OSM_BF16, head_dim 128, batch * heads_q < 2^31; fp32
+ * accumulation, P and dS rounded to bf16 as matrix-product operands,
+ * gradients rounded to bf16 once at the end; every pointer 16-byte aligned.
  * Errors: OSM_ERR_NULL, OSM_ERR_SHAPE (as osm_attn_fwd),
  * OSM_ERR_UNSUPPORTED (other dtype or head_dim, a pointer not 16-byte
- * aligned, seqlen_q or seqlen_k >= 2^23), OSM_ERR_WORKSPACE, OSM_ERR_HIP.
+ * aligned, batch * heads_q >= 2^31, seqlen_q or seqlen_k >= 2^23),
+ * OSM_ERR_WORKSPACE, OSM_ERR_HIP.
  */
 osm_status osm_attn_bwd(const void *q, const void *k, const void *v, const void *o,
                         const void *dout, const float *lse, void *dq, void *dk, void *dv,
@@ -246,9 +250,11 @@ size_t osm_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t max_se
  *            (caller-owned, 256-byte aligned, contents on entry ignored).
  * Two kernels are enqueued on `stream`: the per-piece summaries, then the
  * merge (same as osm_merge_partials) reading the workspace.
- * Supported: dtype OSM_F32 or OSM_BF16; head_dim 64 or 128.
- * Errors: OSM_ERR_NULL, OSM_ERR_SHAPE, OSM_ERR_UNSUPPORTED,
- * OSM_ERR_WORKSPACE, OSM_ERR_HIP.
+ * Supported: dtype OSM_F32 or OSM_BF16; head_dim 64 or 128;
+ * heads_q / heads_kv in {1, 2, 4, 8} with (heads_q / heads_kv) * split_size
+ * <= 16384; batch * heads_q < 2^31; q, k_cache and v_cache 16-byte aligned.
+ * Errors: OSM_ERR_NULL, OSM_ERR_SHAPE, OSM_ERR_UNSUPPORTED (anything outside
+ * the supported set), OSM_ERR_WORKSPACE, OSM_ERR_HIP.
  */
 osm_status osm_attn_decode_splitkv(const void *q, const void *k_cache, const void *v_cache,
                                    void *o, float *lse, osm_dtype dtype, int32_t batch,
@@ -311,9 +317,10 @@ osm_status osm_merge_partials(const float *part_m, const float *part_l, const fl
  * Two kernels are enqueued on `stream`; calls that update the same state
  * must be ordered on one stream.
  * Supported: dtype OSM_F32 or OSM_BF16; head_dim 64 or 128;
- * heads_q / heads_kv in {1, 2, 4, 8}.
- * Errors: OSM_ERR_NULL, OSM_ERR_SHAPE, OSM_ERR_UNSUPPORTED,
- * OSM_ERR_WORKSPACE, OSM_ERR_HIP.
+ * heads_q / heads_kv in {1, 2, 4, 8} with (heads_q / heads_kv) * split_size
+ * <= 16384; batch * heads_q < 2^31; q, k_new and v_new 16-byte aligned.
+ * Errors: OSM_ERR_NULL, OSM_ERR_SHAPE, OSM_ERR_UNSUPPORTED (anything outside
+ * the supported set), OSM_ERR_WORKSPACE, OSM_ERR_HIP.
  */
 osm_status osm_attn_extend(const void *q, const void *k_new, const void *v_new, osm_dtype dtype,
                            int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t n_new,

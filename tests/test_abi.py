@@ -87,6 +87,9 @@ def test_attn_fwd_validation(lib):
     assert call(k=None) == 1
     assert call(k=None, v=None, Nk=0) != 1          # no keys: k/v may be NULL
     assert call(q=None, Nq=0) == 0                  # nothing to compute
+    assert call(q=ctypes.c_void_p(0x10002)) == 3    # not 16-byte aligned
+    assert call(o=ctypes.c_void_p(0x10008)) == 3
+    assert call(B=65536, Hq=32768) == 3             # 2^31 (batch, head) pairs
 
 
 @no_gpu_only
@@ -112,6 +115,8 @@ def test_decode_validation(lib):
     assert call(ws=None) == 4
     assert call(wsb=ws_ok - 1) == 4
     assert call(ws=ctypes.c_void_p(0x10010)) == 4   # not 256-byte aligned
+    assert call(kc=ctypes.c_void_p(0x10008)) == 3   # not 16-byte aligned
+    assert call(B=65536, Hq=32768, Hkv=4096) == 3   # 2^31 (batch, head) pairs
 
 
 @no_gpu_only
@@ -165,6 +170,8 @@ def test_extend_validation(lib):
     assert call(q=None) == 1
     assert call(wsb=ws_ok - 1) == 4
     assert call(ws=ctypes.c_void_p(0x10004)) == 4    # not 256-byte aligned
+    assert call(v=ctypes.c_void_p(0x10004)) == 3     # not 16-byte aligned
+    assert call(B=65536, Hq=32768, Hkv=32768) == 3   # 2^31 (batch, head) pairs
 
 
 def test_attn_fwd_fp8_validation(lib):
@@ -183,6 +190,7 @@ def test_attn_fwd_fp8_validation(lib):
     assert call(q=None) == 1
     assert call(v=None) == 1
     assert call(o=ctypes.c_void_p(0x10001)) == 3     # not 16-byte aligned
+    assert call(B=65536, Hq=32768) == 3              # 2^31 (batch, head) pairs
 
 
 def test_attn_bwd_validation(lib):
@@ -208,6 +216,7 @@ def test_attn_bwd_validation(lib):
     for name in ("q", "o", "do", "lse", "dq", "k", "v", "dk", "dv"):
         assert call(**{name: None}) == 1, name
     assert call(dk=ctypes.c_void_p(0x10008)) == 3   # not 16-byte aligned
+    assert call(B=65536, Hq=32768) == 3             # 2^31 (batch, head) pairs
     assert call(wsb=ws_ok - 1) == 4
     assert call(ws=None) == 4
     assert call(ws=ctypes.c_void_p(0x10010)) == 4   # not 256-byte aligned
