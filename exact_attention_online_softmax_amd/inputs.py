@@ -267,3 +267,17 @@ def lse_parts(parts: int, rows: int, d: int, seed: int, *, dtype: str = "f32",
     if dtype == "bf16":
         o = to_bf16_bits(o)
     return o, lse
+
+
+def tiled_rows(n_rows: int, d: int, seed: int, *, dtype: str = "bf16", table_rows: int = 4096):
+    """Rows for tensors too large to draw element by element in a test:
+    row j is table[idx[j]], with the table's rows N(0, 1) (rounded to bf16
+    bits, or E4M3 codes for dtype "fp8") and idx uniform over the table.
+    Neighbouring positions hold different rows, so reading the wrong
+    position changes the result.  Returns (table [table_rows, d], idx
+    int64 [n_rows]); the caller gathers (on the host or on the device)."""
+    g = rng(seed)
+    t = normal_f32(g, (table_rows, d))
+    table = to_e4m3_bits(t) if dtype == "fp8" else to_bf16_bits(t)
+    idx = g.integers(0, table_rows, size=n_rows, dtype=np.int64)
+    return table, idx

@@ -117,3 +117,34 @@ def test_full_size_sampled(orc):
     o_ref, lse_ref = oracle(orc, inp, rows=rows)
     check_fp8(host(o).reshape(-1, 128)[rows], host(lse).reshape(-1)[rows], o_ref, lse_ref)
     assert np.isfinite(host(lse)).all()
+
+
+def test_max_key_length_and_head_offsets(orc):
+    """The longest supported key sequence, 2^24 - 1 keys of one byte per
+    element (one head's K just under 2 GiB, ragged last tile), on two KV
+    heads, so the last head starts 2 GiB into K and V.  Sampled rows of the
+    last query head against the oracle on the decoded codes; every head
+    finite."""
+    torch = torch_mod()
+    B, Hq, Hkv, Nq, Nk, d = 1, 2, 2, 64, (1 << 24) - 1, 128
+    announce(f"fwd fp8 max key length B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk}")
+    ktab, kidx = inputs.tiled_rows(Hkv * Nk, d, seed=inputs.SEED_BASE + 71, dtype="fp8")
+    vtab, vidx = inputs.tiled_rows(Hkv * Nk, d, seed=inputs.SEED_BASE + 72, dtype="fp8")
+    qcodes = inputs.to_e4m3_bits(inputs.normal_f32(inputs.rng(inputs.SEED_BASE + 73), (B, Hq, Nq, d)))
+    k = dev_u8(ktab)[torch.from_numpy(kidx).to("cuda")].view(B, Hkv, Nk, d)
+    v = dev_u8(vtab)[torch.from_numpy(vidx).to("cuda")].view(B, Hkv, Nk, d)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = osm.attn_fwd_fp8(dev_u8(qcodes), k, v, scale=scale)
+    oh, lh = host(o), host(lse)
+    del k, v, o, lse
+    torch.cuda.empty_cache()
+    assert np.isfinite(oh).all() and np.isfinite(lh).all()
+    h = Hq - 1
+    rows = np.array([0, 31, Nq - 1])
+    sel = slice(h * Nk, (h + 1) * Nk)
+    kh = inputs.e4m3_bits_to_f32(ktab)[kidx[sel]][None, None]
+    vh = inputs.e4m3_bits_to_f32(vtab)[vidx[sel]][None, None]
+    qh = inputs.e4m3_bits_to_f32(qcodes[0, h, rows])[None, None]
+    o_ref, lse_ref = orc.attention(qh, kh, vh, scale=scale)
+    del kh, vh
+    check_fp8(oh[0, h, rows], lh[0, h, rows], o_ref, lse_ref)

@@ -6,7 +6,7 @@ import pytest
 
 import exact_attention_online_softmax_amd as osm
 from exact_attention_online_softmax_amd import inputs
-from gpu_util import announce, check_attn, dev_bf16, dev_i32, host, host_bits
+from gpu_util import announce, check_attn, dev_bf16, dev_i32, host, host_bits, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -139,3 +139,35 @@ def test_config4_full_sampled(orc):
     for b, L in enumerate(lens):
         assert np.all(oh_all[b, :, L:] == 0.0) and np.all(np.isneginf(lh_all[b, :, L:]))
         assert np.all(np.isfinite(lh_all[b, :, :L]))
+
+
+def test_max_key_length_and_head_offsets(orc):
+    """The longest supported key sequence, 2^23 - 1 keys (one head's K just
+    under 2 GiB, with a ragged last tile), on three KV heads, so that the
+    last head starts 4 GiB into K and V.  GQA 2:1, 100 queries (one partial
+    block).  Sampled rows of the last query head against the oracle; every
+    head finite."""
+    torch = torch_mod()
+    B, Hq, Hkv, Nq, Nk, d = 1, 6, 3, 100, (1 << 23) - 1, 128
+    announce(f"fwd max key length B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk}")
+    ktab, kidx = inputs.tiled_rows(Hkv * Nk, d, seed=inputs.SEED_BASE + 61)
+    vtab, vidx = inputs.tiled_rows(Hkv * Nk, d, seed=inputs.SEED_BASE + 62)
+    qbits = inputs.to_bf16_bits(inputs.normal_f32(inputs.rng(inputs.SEED_BASE + 63), (B, Hq, Nq, d)))
+    k = dev_bf16(ktab)[torch.from_numpy(kidx).to("cuda")].view(B, Hkv, Nk, d)
+    v = dev_bf16(vtab)[torch.from_numpy(vidx).to("cuda")].view(B, Hkv, Nk, d)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = osm.attn_fwd(dev_bf16(qbits), k, v, scale=scale)
+    oh, lh = host(o), host(lse)
+    del k, v, o, lse
+    torch.cuda.empty_cache()
+    assert np.isfinite(oh).all() and np.isfinite(lh).all()
+    h = Hq - 1
+    g = h // (Hq // Hkv)               # its KV head: the last one
+    rows = np.array([0, 57, Nq - 1])
+    sel = slice(g * Nk, (g + 1) * Nk)
+    kh = inputs.bf16_bits_to_f32(ktab)[kidx[sel]][None, None]
+    vh = inputs.bf16_bits_to_f32(vtab)[vidx[sel]][None, None]
+    qh = inputs.bf16_bits_to_f32(qbits[0, h, rows])[None, None]
+    o_ref, lse_ref = orc.attention(qh, kh, vh, scale=scale)
+    del kh, vh
+    check_attn(oh[0, h, rows], lh[0, h, rows], o_ref, lse_ref, "bf16")
