@@ -153,7 +153,6 @@ osm_status osm_attn_decode_splitkv(const void *q, const void *k_cache, const voi
         return OSM_ERR_WORKSPACE;
     osm::DecodeArgs a{q, k_cache, v_cache, o, lse, dtype == OSM_BF16 ? 1 : 0, batch, heads_q,
                       heads_kv, max_seqlen_k, head_dim, seqlens_k, scale, split_size, workspace};
-    a.kv_nontemporal = 1;   // a KV cache is read once per step and dwarfs the caches
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = osm::launch_decode_split(a, lay, s);
     if (e != hipSuccess) return OSM_ERR_HIP;

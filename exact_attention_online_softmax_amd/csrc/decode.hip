@@ -108,11 +108,12 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-// NT: the cache rows are read with nontemporal (streaming) loads.  A decode
-// reads a cache far larger than L2 and the MALL exactly once (6% faster
-// measured); the extend call reads keys the caller has just written, which
-// cached loads may still find on chip.
-template <typename T, int HD, int G, bool NT>
+// K and V rows are read with nontemporal (streaming) loads: every row is read
+// exactly once.  A decode step reads a cache far larger than L2 and the MALL
+// (6% faster measured); an extend call was 2x faster with them when its keys
+// had been pushed out of the caches by other work, and within 3% when they
+// were still on chip.
+template <typename T, int HD, int G>
 __global__ void __launch_bounds__(DEC_THREADS)
 decode_split(const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V,
              const int32_t *__restrict__ seqlens_k, int Hq, int Hkv, int Lmax, int split,
@@ -155,10 +156,7 @@ decode_split(const T *__restrict__ Q, const T *__restrict__ K, const T *__restri
     // Every load of a round is issued before any is used.  Keys past n are
     // clamped to the last valid key (in bounds, finite) and never used.
     Row8<T> kr[R], vr[R];
-    auto kv_load = [&](Row8<T> &r, const T *p) __attribute__((always_inline)) {
-        if constexpr (NT) r.load_nt(p);
-        else r.load(p);
-    };
+    auto kv_load = [&](Row8<T> &r, const T *p) __attribute__((always_inline)) { r.load_nt(p); };
     const bool one_round = (n <= DEC_ROUND);
 #pragma unroll
     for (int u = 0; u < R; ++u) kv_load(kr[u], Kp + (size_t)min(kbase + u * KPB, n - 1) * HD);
@@ -372,24 +370,18 @@ merge_partials_kernel(const float *__restrict__ pm, const float *__restrict__ pl
     }
 }
 
-template <typename T, int HD, int G, bool NT>
-hipError_t launch_split_nt(const DecodeArgs &a, const DecodeLayout &lay, hipStream_t s) {
+template <typename T, int HD, int G>
+hipError_t launch_split(const DecodeArgs &a, const DecodeLayout &lay, hipStream_t s) {
     char *ws = static_cast<char *>(a.workspace);
     dim3 grid(lay.chunks, a.heads_kv, a.batch);
     const size_t shmem = (size_t)G * a.split * sizeof(float);
-    hipLaunchKernelGGL((decode_split<T, HD, G, NT>), grid, dim3(DEC_THREADS), shmem, s,
+    hipLaunchKernelGGL((decode_split<T, HD, G>), grid, dim3(DEC_THREADS), shmem, s,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), a.seqlens_k, a.heads_q, a.heads_kv,
                        a.max_seqlen_k, a.split, lay.chunks, a.scale * kLog2e,
                        reinterpret_cast<float *>(ws + lay.off_m), reinterpret_cast<float *>(ws + lay.off_l),
                        reinterpret_cast<float *>(ws + lay.off_o));
     return hipGetLastError();
-}
-
-template <typename T, int HD, int G>
-hipError_t launch_split(const DecodeArgs &a, const DecodeLayout &lay, hipStream_t s) {
-    return a.kv_nontemporal ? launch_split_nt<T, HD, G, true>(a, lay, s)
-                            : launch_split_nt<T, HD, G, false>(a, lay, s);
 }
 
 template <typename T, int HD>

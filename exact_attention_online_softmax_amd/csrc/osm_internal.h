@@ -81,7 +81,6 @@ struct DecodeArgs {
     float scale;
     int split;
     void *workspace;
-    int kv_nontemporal = 0;   // read K, V with streaming loads (each row once, cache >> L2)
 };
 hipError_t launch_decode_split(const DecodeArgs &a, const DecodeLayout &lay, hipStream_t s);
 
