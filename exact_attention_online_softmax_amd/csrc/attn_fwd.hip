@@ -441,7 +441,7 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
         const TileRsrc lr = tile_rsrc(j + AHEAD);
         const f32x16 zero = {};
         float e[2][16];
-        float rs[2][4] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+        float rs[2][4];      // four partial row sums per block, set by their first item
         bf16x8 pb[2][2];
         f32x16 sn[2];
         bf16x8 ka[8];
@@ -459,7 +459,12 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
                 } else if constexpr (stg == 1) {
                     e[qb][i] = fast_exp2(e[qb][i]);
                 } else {
-                    rs[qb][i & 3] += e[qb][i];
+                    // items n < 4 and 8 <= n < 12 are the first to reach rs[qb][n & 3]
+                    // (starting from 0.0f would cost an add: 0 + x is not x for x = -0)
+                    if constexpr (n < 16 && !(n & 4))
+                        rs[qb][i & 3] = e[qb][i];
+                    else
+                        rs[qb][i & 3] += e[qb][i];
                     if constexpr ((n & 7) == 7) {
                         constexpr int hh = n >> 4;
                         f32x8 f;

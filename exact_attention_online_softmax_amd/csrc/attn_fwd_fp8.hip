@@ -335,7 +335,7 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
         i32x8 pf[NQB];
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
-            float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            float rs[4];     // set by the first weight of each (0 + x would cost an add)
 #pragma unroll
             for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
@@ -344,7 +344,7 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         e[u] = fast_exp2(fmaf(s[kbk][qb][4 * r + u], scale_log2, -msub[qb]));
-                        rs[u] += e[u];
+                        rs[u] = (kbk == 0 && r == 0) ? e[u] : rs[u] + e[u];
                     }
                     int w = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
                     w = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], w, true);

@@ -142,6 +142,75 @@ softmax_rows_resident(const float *x, float *y, int64_t rows,
     }
 }
 
+// Buffer resource word 3 for raw (unformatted, unswizzled) dword access.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kAuxNontemporal = 2;   // cache-policy bit NT of a buffer access on gfx950
+
+// The resident kernel for rows whose width is a multiple of four on 16-byte
+// aligned rows: every vector is whole, so a lane's vectors are in or out of
+// the row as a unit.  Loads and stores go through a buffer resource spanning
+// exactly the row; its range check turns a vector past the end into a load of
+// zeros and a dropped store, so there is no per-vector branch (the generic
+// kernel above pays an exec-mask branch per vector and per element of a
+// partial vector).  Vectors past the end are then set to -inf by a select.
+// The range check covers the VGPR offset only, so each load's whole byte
+// offset is carried there.
+template <int NV>
+__global__ void __launch_bounds__(1024)
+softmax_rows_resident_whole(const float *x, float *y, int64_t rows, int64_t cols, int64_t ld_x,
+                            int64_t ld_y, float *__restrict__ row_max, float *__restrict__ row_sum) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    __shared__ float sm[kMaxWaves], sl[kMaxWaves];
+    const uint32_t bytes = (uint32_t)(cols * 4);            // <= 2^18: the plan keeps cols <= 65536
+    const uint32_t off0 = threadIdx.x * 16u, step = blockDim.x * 16u;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const __amdgpu_buffer_rsrc_t xr =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(x + r * ld_x), 0, (int)bytes, kRsrcWord3);
+        float4 v[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const uint32_t off = off0 + i * step;
+            const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, kAuxNontemporal);
+            const bool in = off < bytes;
+            v[i].x = in ? __uint_as_float(w[0]) : kNegInf;
+            v[i].y = in ? __uint_as_float(w[1]) : kNegInf;
+            v[i].z = in ? __uint_as_float(w[2]) : kNegInf;
+            v[i].w = in ? __uint_as_float(w[3]) : kNegInf;
+        }
+        float m_lane = kNegInf;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) m_lane = fmaxf(m_lane, max4(v[i]));
+        // a lane with no element of the row (m_lane = -inf) gets exp_acc(NaN)
+        // = 0 for each: exp_acc clamps its argument with fmaxf, which drops
+        // the NaN of -inf - (-inf); no branch is needed around it
+        float l_lane = 0.0f;
+        const bool empty = (m_lane == kNegInf);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            v[i].x = exp_acc(v[i].x - m_lane);
+            v[i].y = exp_acc(v[i].y - m_lane);
+            v[i].z = exp_acc(v[i].z - m_lane);
+            v[i].w = exp_acc(v[i].w - m_lane);
+            l_lane += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+        }
+        float m = m_lane, l = l_lane;
+        block_merge_ml(m, l, sm, sl);
+        const float w = (empty || m == kNegInf) ? 0.0f : exp_acc(m_lane - m) / l;
+        const __amdgpu_buffer_rsrc_t yr =
+            __builtin_amdgcn_make_buffer_rsrc(y + r * ld_y, 0, (int)bytes, kRsrcWord3);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const u32x4 o = {__float_as_uint(v[i].x * w), __float_as_uint(v[i].y * w),
+                             __float_as_uint(v[i].z * w), __float_as_uint(v[i].w * w)};
+            __builtin_amdgcn_raw_buffer_store_b128(o, yr, off0 + i * step, 0, kAuxNontemporal);
+        }
+        if (threadIdx.x == 0) {
+            if (row_max) row_max[r] = m;
+            if (row_sum) row_sum[r] = l;
+        }
+    }
+}
+
 template <bool ALIGNED>
 __global__ void __launch_bounds__(1024)
 softmax_rows_streaming(const float *x, float *y, int64_t rows,
@@ -188,11 +257,23 @@ softmax_rows_streaming(const float *x, float *y, int64_t rows,
     }
 }
 
-template <int NV, bool A>
+// MODE 0: unaligned rows; 1: 16-byte aligned rows; 2: aligned rows of whole vectors
+template <int NV, int MODE>
 hipError_t launch_resident(const SoftmaxArgs &a, int threads, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((softmax_rows_resident<NV, A>), dim3(grid), dim3(threads), 0, s, a.x, a.y,
-                       a.rows, a.cols, a.ld_x, a.ld_y, a.row_max, a.row_sum);
+    if constexpr (MODE == 2)
+        hipLaunchKernelGGL((softmax_rows_resident_whole<NV>), dim3(grid), dim3(threads), 0, s, a.x, a.y,
+                           a.rows, a.cols, a.ld_x, a.ld_y, a.row_max, a.row_sum);
+    else
+        hipLaunchKernelGGL((softmax_rows_resident<NV, MODE == 1>), dim3(grid), dim3(threads), 0, s, a.x,
+                           a.y, a.rows, a.cols, a.ld_x, a.ld_y, a.row_max, a.row_sum);
     return hipGetLastError();
+}
+
+template <int NV>
+hipError_t launch_resident_mode(const SoftmaxArgs &a, int mode, int threads, int grid, hipStream_t s) {
+    return mode == 2 ? launch_resident<NV, 2>(a, threads, grid, s)
+         : mode == 1 ? launch_resident<NV, 1>(a, threads, grid, s)
+                     : launch_resident<NV, 0>(a, threads, grid, s);
 }
 
 }  // namespace
@@ -236,13 +317,12 @@ hipError_t launch_softmax_rows(const SoftmaxArgs &a, const SoftmaxPlan &p, hipSt
                          (a.ld_x % 4 == 0) && (a.ld_y % 4 == 0);
     const int grid = (int)(a.rows < 1048576 ? a.rows : 1048576);
     if (p.resident) {
+        // resident rows have at most 65536 columns (16 vectors x 1024 lanes)
+        const int mode = !aligned ? 0 : (a.cols % 4 == 0 ? 2 : 1);
         switch (p.nv) {
-            case 4: return aligned ? launch_resident<4, true>(a, p.threads, grid, s)
-                                   : launch_resident<4, false>(a, p.threads, grid, s);
-            case 8: return aligned ? launch_resident<8, true>(a, p.threads, grid, s)
-                                   : launch_resident<8, false>(a, p.threads, grid, s);
-            default: return aligned ? launch_resident<16, true>(a, p.threads, grid, s)
-                                    : launch_resident<16, false>(a, p.threads, grid, s);
+            case 4: return launch_resident_mode<4>(a, mode, p.threads, grid, s);
+            case 8: return launch_resident_mode<8>(a, mode, p.threads, grid, s);
+            default: return launch_resident_mode<16>(a, mode, p.threads, grid, s);
         }
     }
     if (aligned)

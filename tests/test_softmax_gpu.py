@@ -88,3 +88,31 @@ def test_invariance_to_shift(orc):
     y1, _, _ = run(x)
     y2, _, _ = run(x + np.float32(64.0))
     assert np.all(np.abs(y1 - y2) <= 2e-5 * np.abs(y1) + 2.0 ** -126)
+
+
+@pytest.mark.parametrize("cols,ld_x,ld_y", [(32000, 32004, 32008), (3000, 3004, 3000),
+                                            (2048, 2051, 2053), (129, 132, 136)])
+def test_row_stride(orc, cols, ld_x, ld_y):
+    """Rows ld_x / ld_y elements apart, through the C ABI (the binding passes
+    contiguous rows): whole-vector rows on 16-byte strides, odd strides, and
+    a ragged width; the gap between rows of y is never written."""
+    announce(f"softmax strided rows cols={cols} ld_x={ld_x} ld_y={ld_y}")
+    torch = __import__("torch")
+    rows = 37
+    x = inputs.softmax_rows_input(rows, cols, seed=cols + ld_x)
+    xb = np.full((rows, ld_x), np.nan, np.float32)
+    xb[:, :cols] = x
+    xd = dev_f32(xb)
+    sentinel = np.float32(-7.25)
+    yd = torch.full((rows, ld_y), float(sentinel), dtype=torch.float32, device="cuda")
+    md = torch.empty(rows, dtype=torch.float32, device="cuda")
+    sd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    lib = osm.load_library()
+    st = lib.osm_softmax_rows(osm._ptr(xd), osm._ptr(yd), rows, cols, ld_x, ld_y, osm._ptr(md),
+                              osm._ptr(sd), osm._stream())
+    assert st == 0, lib.osm_status_str(st)
+    torch.cuda.synchronize()
+    yb = host(yd)
+    y_ref, m_ref, l_ref = orc.softmax_rows(x)
+    check_softmax(yb[:, :cols], host(md), host(sd), y_ref, m_ref, l_ref)
+    assert np.all(yb[:, cols:] == sentinel)
