@@ -410,10 +410,10 @@ attn_bwd_dkdv(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 uint2 wk, wv;
-                wk.x = valid ? pack_bf16x2(dka[dt][4 * r] * scale, dka[dt][4 * r + 1] * scale) : 0u;
-                wk.y = valid ? pack_bf16x2(dka[dt][4 * r + 2] * scale, dka[dt][4 * r + 3] * scale) : 0u;
-                wv.x = valid ? pack_bf16x2(dva[dt][4 * r], dva[dt][4 * r + 1]) : 0u;
-                wv.y = valid ? pack_bf16x2(dva[dt][4 * r + 2], dva[dt][4 * r + 3]) : 0u;
+                wk.x = valid ? pack_bf16x2_hw(dka[dt][4 * r] * scale, dka[dt][4 * r + 1] * scale) : 0u;
+                wk.y = valid ? pack_bf16x2_hw(dka[dt][4 * r + 2] * scale, dka[dt][4 * r + 3] * scale) : 0u;
+                wv.x = valid ? pack_bf16x2_hw(dva[dt][4 * r], dva[dt][4 * r + 1]) : 0u;
+                wv.y = valid ? pack_bf16x2_hw(dva[dt][4 * r + 2], dva[dt][4 * r + 3]) : 0u;
                 *reinterpret_cast<uint2 *>(dkr + 32 * dt + 8 * r + 4 * g) = wk;
                 *reinterpret_cast<uint2 *>(dvr + 32 * dt + 8 * r + 4 * g) = wv;
             }
@@ -653,8 +653,8 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     uint2 w;
-                    w.x = valid ? pack_bf16x2(dqa[qb][dt][4 * r] * scale, dqa[qb][dt][4 * r + 1] * scale) : 0u;
-                    w.y = valid ? pack_bf16x2(dqa[qb][dt][4 * r + 2] * scale, dqa[qb][dt][4 * r + 3] * scale) : 0u;
+                    w.x = valid ? pack_bf16x2_hw(dqa[qb][dt][4 * r] * scale, dqa[qb][dt][4 * r + 1] * scale) : 0u;
+                    w.y = valid ? pack_bf16x2_hw(dqa[qb][dt][4 * r + 2] * scale, dqa[qb][dt][4 * r + 3] * scale) : 0u;
                     *reinterpret_cast<uint2 *>(row + 32 * dt + 8 * r + 4 * g) = w;
                 }
         }

@@ -433,8 +433,8 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     uint2 w;
-                    w.x = valid ? pack_bf16x2(oacc[qb][dt][4 * r + 0] * inv, oacc[qb][dt][4 * r + 1] * inv) : 0u;
-                    w.y = valid ? pack_bf16x2(oacc[qb][dt][4 * r + 2] * inv, oacc[qb][dt][4 * r + 3] * inv) : 0u;
+                    w.x = valid ? pack_bf16x2_hw(oacc[qb][dt][4 * r + 0] * inv, oacc[qb][dt][4 * r + 1] * inv) : 0u;
+                    w.y = valid ? pack_bf16x2_hw(oacc[qb][dt][4 * r + 2] * inv, oacc[qb][dt][4 * r + 3] * inv) : 0u;
                     *reinterpret_cast<uint2 *>(orow + 32 * dt + 8 * r + 4 * g) = w;
                 }
             if (LSE && g == 0)

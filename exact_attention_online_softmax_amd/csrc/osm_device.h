@@ -78,4 +78,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
+// The same two conversions in one gfx950 instruction (v_cvt_pk_bf16_f32,
+// round-to-nearest-even under the default rounding mode): bit-identical to
+// pack_bf16x2 for every non-NaN input.  For epilogues that convert many
+// accumulators at once.
+__device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
 }  // namespace osm
