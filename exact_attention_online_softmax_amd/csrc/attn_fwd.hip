@@ -133,6 +133,14 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t *p) {
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// a wave-uniform pointer, moved to scalar registers
+__device__ __forceinline__ const uint16_t *uniform_ptr(const uint16_t *p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+    return reinterpret_cast<const uint16_t *>((hi << 32) | lo);
+}
+
 // Workgroup barrier without a memory fence; the empty asm statements keep
 // the compiler from moving LDS accesses across it.  Callers wait for their
 // own outstanding memory operations first.
@@ -150,49 +158,79 @@ constexpr int kRsrcWord3 = 0x00020000;
 // lgkmcnt 11:8; a field at its maximum does not wait.
 constexpr int kWaitVm0 = 0x0F70;   // vmcnt(0)
 constexpr int kWaitVm4 = 0x0F74;   // vmcnt(4): one tile's loads of this wave may stay in flight
+constexpr int kWaitVm20 = 0x4F74;  // vmcnt(20)
+constexpr int kWaitLgkm0 = 0xC07F; // lgkmcnt(0)
 static_assert(2 * LPW == 4, "kWaitVm4 assumes four loads per wave per tile");
 
-__global__ void __launch_bounds__(NT, 1)
-attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
-                   const uint16_t *__restrict__ V, uint16_t *__restrict__ O,
-                   float *__restrict__ LSE, int B, int Hq, int Hkv, int Nq, int Nk,
-                   const int32_t *__restrict__ seqlens_q, const int32_t *__restrict__ seqlens_k,
-                   float scale_log2, int causal, int nqb, int xcd_heads) {
+// (batch, head, KV head, first query) of a query block
+struct Blk {
+    int b, h, kvh, q0;
+};
+
+// PERSIST: one workgroup per CU walks the blocks L = blockIdx.x, + gridDim.x,
+// ...  Used for full-length non-causal inputs, where every block has the same
+// work.  The Q of the next block is copied into LDS (qs) while the current
+// block runs, and the last ring loads of a block fetch the first tiles of
+// the next one, so a block starts with its Q and first tiles on chip and
+// the Q reads and O writes of all CUs no longer fall in the same interval.
+template <bool PERSIST>
+__device__ __forceinline__ void
+attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+              const uint16_t *__restrict__ V, uint16_t *__restrict__ O,
+              float *__restrict__ LSE, int B, int Hq, int Hkv, int Nq, int Nk,
+              const int32_t *__restrict__ seqlens_q, const int32_t *__restrict__ seqlens_k,
+              float scale_log2, int causal_arg, int nqb, int xcd_heads, int nblocks) {
     // ring of four K slots and four V slots, 8 KiB each
     __shared__ __attribute__((aligned(1024))) uint8_t k0[TILEB], k1[TILEB], k2[TILEB], k3[TILEB];
     __shared__ __attribute__((aligned(1024))) uint8_t v0[TILEB], v1[TILEB], v2[TILEB], v3[TILEB];
+    // Q of the block (PERSIST), rows swizzled like K
+    // (less aligned than the slots, so that it is laid out after them and the
+    // slots stay within reach of the 16-bit immediate offset of LDS reads)
+    __shared__ __attribute__((aligned(256))) uint8_t qs[PERSIST ? BQ * ROWB : 256];
+    const int causal = PERSIST ? 0 : causal_arg;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5, c = lane & 31;
 
     // ---- which (batch, head, query block) ------------------------------
-    const int L = blockIdx.x;
-    int head, qrev;
-    if (xcd_heads) {
-        // hardware places block L on XCD L % 8; give every XCD whole heads
-        // (head % 8 == XCD) and run one head's query blocks back to back
-        // (heaviest first), so the blocks resident on an XCD share a few
-        // heads' K and V in its L2.
-        const int xcd = L & 7, slot = L >> 3;
-        qrev = slot % nqb;
-        head = (slot / nqb) * 8 + xcd;
-    } else {
-        head = L / nqb;
-        qrev = L % nqb;
-    }
-    // the integer divisions above run on the vector ALU; the results are
-    // uniform, so move them back to scalar registers
-    head = __builtin_amdgcn_readfirstlane(head);
-    qrev = __builtin_amdgcn_readfirstlane(qrev);
-    const int qb0 = causal ? (nqb - 1 - qrev) : qrev;
-    const int b = head / Hq, h = head % Hq;
-    const int kvh = h / (Hq / Hkv);
+    auto decode = [&](int L) __attribute__((always_inline)) -> Blk {
+        int head, qrev;
+        if (xcd_heads) {
+            // hardware places block L on XCD L % 8 (a persistent grid is a
+            // multiple of 8, so block L still runs on XCD L % 8); give every
+            // XCD whole heads (head % 8 == XCD) and run one head's query
+            // blocks back to back (heaviest first), so the blocks resident
+            // on an XCD share a few heads' K and V in its L2.
+            const int xcd = L & 7, slot = L >> 3;
+            qrev = slot % nqb;
+            head = (slot / nqb) * 8 + xcd;
+        } else {
+            head = L / nqb;
+            qrev = L % nqb;
+        }
+        // the integer divisions above run on the vector ALU; the results are
+        // uniform, so move them back to scalar registers
+        head = __builtin_amdgcn_readfirstlane(head);
+        qrev = __builtin_amdgcn_readfirstlane(qrev);
+        const int qb0 = causal ? (nqb - 1 - qrev) : qrev;
+        const int b = head / Hq, h = head % Hq;
+        return {b, h, h / (Hq / Hkv), qb0 * BQ};
+    };
+
+    int L = blockIdx.x;
+    bool first = true;
+    for (;;) {
+    const Blk cur = decode(L);
+    const int Lnext = L + (int)gridDim.x;
+    const bool has_next = PERSIST && __builtin_amdgcn_readfirstlane(Lnext < nblocks ? 1 : 0) != 0;
+    const Blk nxt = decode(has_next ? Lnext : L);
+    const int b = cur.b, h = cur.h, kvh = cur.kvh, q0 = cur.q0;
     // lengths and the wave index are uniform: keep them in scalar registers
     // so that every tile-level decision is a scalar branch
     const int Lq = __builtin_amdgcn_readfirstlane(seqlens_q ? clampi(seqlens_q[b], 0, Nq) : Nq);
     const int Lk = __builtin_amdgcn_readfirstlane(seqlens_k ? clampi(seqlens_k[b], 0, Nk) : Nk);
 
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = lane >> 5, c = lane & 31;
-    const int q0 = qb0 * BQ;
     const int qw0 = q0 + QW * wave;         // first query of this wave
     // this lane's queries: qw0 + c (block 0) and qw0 + 32 + c (block 1)
 
@@ -200,7 +238,7 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     const uint16_t *Kh = K + (size_t)(b * Hkv + kvh) * Nk * D;
     const uint16_t *Vh = V + (size_t)(b * Hkv + kvh) * Nk * D;
 
-    if (q0 >= Lq) {
+    if (!PERSIST && q0 >= Lq) {
         // every row of this block is padding: O = 0, LSE = -inf
         const int rows = min(BQ, Nq - q0);
         for (int i = tid; i < rows * (D / 8); i += NT) {
@@ -227,20 +265,8 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     if (Lk % BK) wfirst_mask = min(wfirst_mask, Lk / BK);
     // iterations j whose next tile j + 1 is computed without a mask
     const int nfast = max(0, wfirst_mask - 1);
-
-    // ---- Q fragments (B operands of S^T = K Q^T), kept in registers -----
-    // lane l holds Q[qw0 + 32 qb + c][64 g + 8 ks + 0..7] for ks = 0..7
-    bf16x8 qf[2][8];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int qi = qw0 + 32 * qb + c;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            uint4 w = make_uint4(0, 0, 0, 0);
-            if (qi < Lq) w = *reinterpret_cast<const uint4 *>(Q + (qhead + qi) * D + 64 * g + 8 * ks);
-            qf[qb][ks] = __builtin_bit_cast(bf16x8, w);
-        }
-    }
+    // the loops run in whole groups of four iterations (see below)
+    const int wend = (wtiles + 3) & ~3, nend = (ntiles + 3) & ~3;
 
     // O~^T accumulators, zeroed in the AGPRs by an MFMA of zeros (so they
     // never pass through VGPRs)
@@ -290,11 +316,35 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     struct TileRsrc {
         __amdgpu_buffer_rsrc_t k, v;
     };
+    auto rsrc_at = [&](const uint16_t *kb, const uint16_t *vb, int j0, int len) __attribute__((always_inline)) -> TileRsrc {
+        const int bytes = max(0, len - j0) * ROWB;   // < 2^31: the ABI bounds Nk * 256
+        return {__builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(kb) + (size_t)j0 * D, 0, bytes, kRsrcWord3),
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(vb) + (size_t)j0 * D, 0, bytes, kRsrcWord3)};
+    };
+    // tile t of this block; the only kind the unmasked loop loads: it stops
+    // at least two iterations short of the padded end, so t < nend there
+    // (t may pass ntiles, where the range check loads zeros)
+    auto tile_rsrc_cur = [&](int t) __attribute__((always_inline)) -> TileRsrc {
+        return rsrc_at(Kh, Vh, t * BK, Lk);
+    };
+    // With PERSIST, tile nend + i (past this block's padded end, where the
+    // ring would load zeros) is tile i of the next block, if there is one;
+    // every block has the same Lk = Nk and the same nend.  The compiler
+    // evaluates the uniform selects of that case on the vector ALU;
+    // readfirstlane keeps the resource in scalar registers, without which
+    // every load would become a loop over lanes.
+    const uint16_t *Kn = K + (size_t)(nxt.b * Hkv + nxt.kvh) * Nk * D;
+    const uint16_t *Vn = V + (size_t)(nxt.b * Hkv + nxt.kvh) * Nk * D;
     auto tile_rsrc = [&](int t) __attribute__((always_inline)) -> TileRsrc {
-        const int j0 = t * BK;
-        const int bytes = max(0, Lk - j0) * ROWB;   // < 2^31: the ABI bounds Nk * 256
-        return {__builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(Kh) + (size_t)j0 * D, 0, bytes, kRsrcWord3),
-                __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(Vh) + (size_t)j0 * D, 0, bytes, kRsrcWord3)};
+        if constexpr (!PERSIST) {
+            return tile_rsrc_cur(t);
+        } else {
+            const bool next = t >= nend;
+            const uint16_t *kb = uniform_ptr(next ? Kn : Kh), *vb = uniform_ptr(next ? Vn : Vh);
+            const int j0 = __builtin_amdgcn_readfirstlane((next ? t - nend : t) * BK);
+            const int len = __builtin_amdgcn_readfirstlane((next && !has_next) ? 0 : Lk);
+            return rsrc_at(kb, vb, j0, len);
+        }
     };
     // one of the four loads (K block 0, V block 0, K block 1, V block 1) of
     // this wave's share of a tile
@@ -312,6 +362,50 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 #pragma unroll
         for (int w = 0; w < 2 * LPW; ++w) load1(r, kd, vd, w);
     };
+
+    // Q rows q0 .. q0 + BQ - 1 of block n into qs (PERSIST): wave w copies
+    // its own 64 rows, 16 loads of 1 KiB laid out like a K tile's; rows at
+    // or past Nq read as zeros
+    auto issue_q = [&](const Blk &n) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(Q) + ((size_t)(n.b * Hq + n.h) * Nq + n.q0) * D, 0,
+            max(0, Nq - n.q0) * ROWB, kRsrcWord3);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int blk = 16 * wave + i, row = 4 * blk + (lane >> 4), sl = lane & 15;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3))) *)(qs + blk * 1024), 16,
+                                                     row * ROWB + ((sl ^ (row & 15)) << 4), 0, 0, 0);
+        }
+    };
+    if (PERSIST && first) {
+        issue_q(cur);
+        issue(k0, v0, 0);
+        issue(k1, v1, 1);
+        issue(k2, v2, 2);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    // ---- Q fragments (B operands of S^T = K Q^T), kept in registers -----
+    // lane l holds Q[qw0 + 32 qb + c][64 g + 8 ks + 0..7] for ks = 0..7
+    bf16x8 qf[2][8];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int qi = qw0 + 32 * qb + c;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            if constexpr (PERSIST) {
+                // this wave's rows of qs: row 64 wave + 32 qb + c, chunk 8 g + ks
+                const int row = QW * wave + 32 * qb + c;
+                qf[qb][ks] = *reinterpret_cast<const bf16x8 *>(qs + row * ROWB + (((8 * g + ks) ^ (row & 15)) << 4));
+            } else {
+                uint4 w = make_uint4(0, 0, 0, 0);
+                if (qi < Lq) w = *reinterpret_cast<const uint4 *>(Q + (qhead + qi) * D + 64 * g + 8 * ks);
+                qf[qb][ks] = __builtin_bit_cast(bf16x8, w);
+            }
+        }
+    }
+
 
     // per-lane LDS byte offsets (within a tile) of the QK A operand: row c,
     // chunk 8 g + ks -> slot (8 g + ks) ^ (c % 16)
@@ -412,9 +506,16 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     // Every iteration issues exactly four loads per wave (tiles past the end
     // are zero fills of consumed slots), so at the top of iteration j the
     // loads of tiles j+1 and j+2 are the ones in flight.
+    // With PERSIST and a next block, the 16 loads copying its Q are issued
+    // after S(0) (below), behind this block's tiles 1 and 2 and the previous
+    // block's O stores: tiles 1 and 2 are then followed by at least 20
+    // memory operations, and iterations 0 and 1 wait with vmcnt(20), so the
+    // copy and the stores are not waited for there.
     auto enter = [&](int j) __attribute__((always_inline)) {
-        (void)j;
-        __builtin_amdgcn_s_waitcnt(kWaitVm4);
+        if (PERSIST && has_next && j < 2)
+            __builtin_amdgcn_s_waitcnt(kWaitVm20);
+        else
+            __builtin_amdgcn_s_waitcnt(kWaitVm4);
         tile_barrier();
     };
     auto idle = [&](auto S, int j) __attribute__((always_inline)) {
@@ -438,7 +539,7 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
         const uint8_t *vb = vslot(S);
         uint8_t *kd = kslot(Slot<decltype(S)::value + 3>{});
         uint8_t *vd = vslot(Slot<decltype(S)::value + 3>{});
-        const TileRsrc lr = tile_rsrc(j + AHEAD);
+        const TileRsrc lr = masked ? tile_rsrc(j + AHEAD) : tile_rsrc_cur(j + AHEAD);
         const f32x16 zero = {};
         float e[2][16];
         float rs[2][4];      // four partial row sums per block, set by their first item
@@ -553,11 +654,16 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
 
     // ---- prologue: tiles 0 .. AHEAD-1 in flight, S(0) and its maximum ----
     // tiles 0..2 (zero fills past the end); iteration 0 fills slot 3
-    issue(k0, v0, 0);
-    issue(k1, v1, 1);
-    issue(k2, v2, 2);
-    __builtin_amdgcn_s_waitcnt(0);   // nothing in flight (Q included)
-    __syncthreads();
+    // (with PERSIST the tiles were loaded before the Q fragments were read:
+    // by the block start above, or by the last iterations of the previous
+    // block, whose final wait and barrier leave tile 0 resident)
+    if (!PERSIST) {
+        issue(k0, v0, 0);
+        issue(k1, v1, 1);
+        issue(k2, v2, 2);
+        __builtin_amdgcn_s_waitcnt(0);   // nothing in flight (Q included)
+        __syncthreads();
+    }
     if (wtiles > 0) {
         qk(k0, sacc);
         if (wfirst_mask == 0) mask(sacc, 0);
@@ -570,6 +676,12 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
             msub[qb] = (tm[qb] == kNegInf) ? 0.0f : tm[qb] * scale_log2;
         }
     }
+    if (has_next) {
+        // this wave's reads of qs are complete (its own rows only): copy the
+        // next block's Q over them
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        issue_q(nxt);
+    }
 
     // ---- main loop (unrolled by the ring size), then the masked tail -----
     // Control flow never joins two versions of the accumulators that both
@@ -577,7 +689,6 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
     // VGPRs): the masked loop also runs in whole groups of four, and its
     // iterations past wtiles only load and pass the barrier.  Every wave
     // passes the same barriers.
-    const int wend = (wtiles + 3) & ~3, nend = (ntiles + 3) & ~3;
     int j = 0;
     for (; j + 4 <= nfast; j += 4) {
         body(Slot<0>{}, Slot<0>{}, j);
@@ -598,7 +709,9 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
         idle(Slot<2>{}, j + 2);
         idle(Slot<3>{}, j + 3);
     }
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // no load outlives the loop
+    // no load outlives the last block (the next block's tiles 1 and 2 stay
+    // in flight otherwise)
+    if (!has_next) __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
     // ---- epilogue: O = O~ / l once, LSE = m + log l ------------------------
     acc_settle(oacc);
@@ -624,7 +737,30 @@ attn_fwd_bf16_d128(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ 
                 LSE[qhead + qi] = valid ? (m[qb] * scale_log2 + __log2f(lt)) * kLn2 : kNegInf;
         }
     }
+    if (!has_next) break;
+    L = Lnext;
+    first = false;
+    }   // blocks
 }
+
+#define OSM_ATTN_FWD_PARAMS                                                                          \
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, \
+        uint16_t *__restrict__ O, float *__restrict__ LSE, int B, int Hq, int Hkv, int Nq, int Nk,   \
+        const int32_t *__restrict__ seqlens_q, const int32_t *__restrict__ seqlens_k,               \
+        float scale_log2, int causal, int nqb, int xcd_heads, int nblocks
+
+// one query block per workgroup
+__global__ void __launch_bounds__(NT, 1) attn_fwd_bf16_d128(OSM_ATTN_FWD_PARAMS) {
+    attn_fwd_body<false>(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, seqlens_q, seqlens_k, scale_log2, causal, nqb,
+                         xcd_heads, nblocks);
+}
+
+// one workgroup per compute unit walking several query blocks
+__global__ void __launch_bounds__(NT, 1) attn_fwd_bf16_d128_persist(OSM_ATTN_FWD_PARAMS) {
+    attn_fwd_body<true>(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, seqlens_q, seqlens_k, scale_log2, causal, nqb,
+                        xcd_heads, nblocks);
+}
+#undef OSM_ATTN_FWD_PARAMS
 
 }  // namespace
 
@@ -634,11 +770,29 @@ hipError_t launch_attn_fwd(const AttnFwdArgs &a, hipStream_t s) {
     const int64_t blocks = (int64_t)nqb * nheads;
     if (blocks == 0) return hipSuccess;
     const int xcd_heads = (nheads % 8 == 0) ? nheads / 8 : 0;
-    hipLaunchKernelGGL(attn_fwd_bf16_d128, dim3((unsigned)blocks), dim3(NT), 0, s,
-                       static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
-                       static_cast<const uint16_t *>(a.v), static_cast<uint16_t *>(a.o), a.lse,
-                       a.batch, a.heads_q, a.heads_kv, a.seqlen_q, a.seqlen_k, a.seqlens_q,
-                       a.seqlens_k, a.scale * kLog2e, a.causal, nqb, xcd_heads);
+    // full-length non-causal inputs with more blocks than compute units run
+    // on a persistent grid of one workgroup per compute unit
+    int cus = 0;
+    if (!a.causal && !a.seqlens_q && !a.seqlens_k && a.seqlen_k > 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 0;
+        cus &= ~7;   // whole XCDs' worth, so block L keeps running on XCD L % 8
+    }
+    const bool persist = cus > 0 && blocks > cus;
+    const unsigned grid = persist ? (unsigned)cus : (unsigned)blocks;
+    const uint16_t *q = static_cast<const uint16_t *>(a.q), *k = static_cast<const uint16_t *>(a.k),
+                   *v = static_cast<const uint16_t *>(a.v);
+    uint16_t *o = static_cast<uint16_t *>(a.o);
+    if (persist)
+        hipLaunchKernelGGL(attn_fwd_bf16_d128_persist, dim3(grid), dim3(NT), 0, s, q, k, v, o, a.lse, a.batch,
+                           a.heads_q, a.heads_kv, a.seqlen_q, a.seqlen_k, a.seqlens_q, a.seqlens_k,
+                           a.scale * kLog2e, a.causal, nqb, xcd_heads, (int)blocks);
+    else
+        hipLaunchKernelGGL(attn_fwd_bf16_d128, dim3(grid), dim3(NT), 0, s, q, k, v, o, a.lse, a.batch,
+                           a.heads_q, a.heads_kv, a.seqlen_q, a.seqlen_k, a.seqlens_q, a.seqlens_k,
+                           a.scale * kLog2e, a.causal, nqb, xcd_heads, (int)blocks);
     return hipGetLastError();
 }
 
