@@ -138,7 +138,9 @@ def summarize(name, trace_dir, out):
         for (short, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
             lines.append(f"| {short} | {wg} | {len(d)} | {sum(d) / len(d) / 1e3:.1f} | "
                          f"{min(d) / 1e3:.1f} | {max(d) / 1e3:.1f} |")
-        want = {"fwd": ("attn_fwd_bf16", 2048), "fwd_causal": ("attn_fwd_bf16", 4096),
+        # the non-causal forward runs on the persistent grid (one workgroup per
+        # compute unit); the causal one on one workgroup per query block
+        want = {"fwd": ("attn_fwd_bf16_d128_persist", None), "fwd_causal": ("attn_fwd_bf16", 4096),
                 "softmax": ("softmax_rows", None), "decode": ("decode_split", None),
                 "merge_lse": ("merge_lse", None), "extend": ("decode_split", None),
                 "bwd": ("attn_bwd_dkdv", None), "bwd_causal": ("attn_bwd_dkdv", None),

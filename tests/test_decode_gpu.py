@@ -81,7 +81,8 @@ def test_empty_and_poison_bit_invariance(orc):
     check_attn(oh, lh, o_ref, lse_ref, "bf16")
 
 
-@pytest.mark.parametrize("rows,C,d", [(7, 1, 64), (64, 33, 128), (5, 700, 200), (3, 1, 1)])
+@pytest.mark.parametrize("rows,C,d", [(7, 1, 64), (64, 33, 128), (5, 700, 200), (3, 1, 1),
+                                    (16, 128, 128), (9, 129, 64)])
 def test_merge_standalone(orc, rows, C, d):
     announce(f"merge rows={rows} C={C} d={d}")
     pm, pl, po = inputs.random_partials(rows, C, d, seed=rows + C + d)
