@@ -70,12 +70,26 @@ constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
 constexpr int kWaitVm0 = 0x0F70;         // s_waitcnt vmcnt(0)
 constexpr int kWaitVm2 = 0x0F72;         // s_waitcnt vmcnt(2): one tile's loads in flight
 constexpr int kWaitVm4 = 0x0F74;         // s_waitcnt vmcnt(4): two tiles' loads in flight
+constexpr int kWaitVm6 = 0x0F76;         // s_waitcnt vmcnt(6)
+constexpr int kWaitLgkm0 = 0xC07F;       // s_waitcnt lgkmcnt(0)
 constexpr int kUnitScale = 127;          // E8M0 exponent of 1.0 for the MFMA's block scales
 
 template <int N> struct Slot { static constexpr int value = N; };
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 __device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// a wave-uniform pointer, moved to scalar registers
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint64_t lo = (uint32_t)rfl((int)(uint32_t)u), hi = (uint32_t)rfl((int)(uint32_t)(u >> 32));
+    return reinterpret_cast<const uint8_t *>((hi << 32) | lo);
+}
+
+// (batch, head, KV head, first query) of a query block
+struct Blk {
+    int b, h, kvh, q0;
+};
 
 // chunk c of LDS row r sits in slot c ^ swz8(r); see the header comment
 __device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 3) | (((r >> 4) & 1) << 2); }
@@ -114,46 +128,67 @@ __device__ __forceinline__ void tile_barrier() {
     asm volatile("" ::: "memory");
 }
 
-__global__ void __launch_bounds__(NT, 1)
-attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
-                  const uint8_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE,
-                  int Hq, int Hkv, int Nq, int Nk, const int32_t *__restrict__ seqlens_q,
-                  const int32_t *__restrict__ seqlens_k, float scale_log2, float v_scale, int causal,
-                  int nqb, int xcd_heads) {
+// PERSIST: one workgroup per CU walks the blocks L = blockIdx.x, + gridDim.x,
+// ... (full-length non-causal inputs, where every block has the same work).
+// The next block's Q is copied into LDS (qs) while the current block runs,
+// and the ring's loads past a block's padded end fetch the next block's
+// first tiles, so a block starts with its Q and first tile on chip.
+template <bool PERSIST>
+__device__ __forceinline__ void
+attn_fp8_body(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
+              const uint8_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE,
+              int Hq, int Hkv, int Nq, int Nk, const int32_t *__restrict__ seqlens_q,
+              const int32_t *__restrict__ seqlens_k, float scale_log2, float v_scale, int causal_arg,
+              int nqb, int xcd_heads, int nblocks) {
     __shared__ __attribute__((aligned(1024))) uint8_t k0[TILEB], k1[TILEB], k2[TILEB], k3[TILEB];
     __shared__ __attribute__((aligned(1024))) uint8_t v0[TILEB], v1[TILEB], v2[TILEB], v3[TILEB];
-
-    // ---- which (batch, head, query block) ------------------------------
-    const int L = blockIdx.x;
-    int head, qrev;
-    if (xcd_heads) {
-        // block L runs on XCD L % 8: whole heads per XCD, so the blocks of
-        // one head share its K and V in that XCD's L2
-        const int xcd = L & 7, slot = L >> 3;
-        qrev = slot % nqb;
-        head = (slot / nqb) * 8 + xcd;
-    } else {
-        head = L / nqb;
-        qrev = L % nqb;
-    }
-    head = rfl(head);
-    qrev = rfl(qrev);
-    const int qb0 = causal ? (nqb - 1 - qrev) : qrev;     // causal: heaviest blocks first
-    const int b = head / Hq, h = head % Hq;
-    const int kvh = h / (Hq / Hkv);
-    const int Lq = rfl(seqlens_q ? clampi(seqlens_q[b], 0, Nq) : Nq);
-    const int Lk = rfl(seqlens_k ? clampi(seqlens_k[b], 0, Nk) : Nk);
+    // Q of the block (PERSIST), rows swizzled like K; less aligned than the
+    // slots, so that it is laid out after them
+    __shared__ __attribute__((aligned(256))) uint8_t qs[PERSIST ? BQ * ROWB : 256];
+    const int causal = PERSIST ? 0 : causal_arg;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = rfl(tid >> 6);
     const int g = lane >> 5, c = lane & 31;
-    const int q0 = qb0 * BQ;
+
+    // ---- which (batch, head, query block) ------------------------------
+    auto decode = [&](int L) __attribute__((always_inline)) -> Blk {
+        int head, qrev;
+        if (xcd_heads) {
+            // block L runs on XCD L % 8 (a persistent grid is a multiple of
+            // 8): whole heads per XCD, so the blocks of one head share its K
+            // and V in that XCD's L2
+            const int xcd = L & 7, slot = L >> 3;
+            qrev = slot % nqb;
+            head = (slot / nqb) * 8 + xcd;
+        } else {
+            head = L / nqb;
+            qrev = L % nqb;
+        }
+        head = rfl(head);
+        qrev = rfl(qrev);
+        const int qb0 = causal ? (nqb - 1 - qrev) : qrev;     // causal: heaviest blocks first
+        const int b = head / Hq, h = head % Hq;
+        return {b, h, h / (Hq / Hkv), qb0 * BQ};
+    };
+
+    int L = blockIdx.x;
+    bool first = true;
+    for (;;) {
+    const Blk cur = decode(L);
+    const int Lnext = L + (int)gridDim.x;
+    const bool has_next = PERSIST && rfl(Lnext < nblocks ? 1 : 0) != 0;
+    const Blk nxt = decode(has_next ? Lnext : L);
+    const int b = cur.b, h = cur.h, kvh = cur.kvh, q0 = cur.q0;
+    const int Lq = rfl(seqlens_q ? clampi(seqlens_q[b], 0, Nq) : Nq);
+    const int Lk = rfl(seqlens_k ? clampi(seqlens_k[b], 0, Nk) : Nk);
+
     const int qw0 = q0 + QW * wave;             // queries qw0 + 32 qb + c
     const size_t qrow0 = (size_t)(b * Hq + h) * Nq;
     const uint8_t *Kh = K + (size_t)(b * Hkv + kvh) * Nk * D;
     const uint8_t *Vh = V + (size_t)(b * Hkv + kvh) * Nk * D;
 
-    if (q0 >= Lq) {
+    if (!PERSIST && q0 >= Lq) {
         const int rows = min(BQ, Nq - q0);
         for (int i = tid; i < rows * (D / 8); i += NT)
             *reinterpret_cast<uint4 *>(O + (qrow0 + q0 + i / (D / 8)) * D + (i % (D / 8)) * 8) =
@@ -171,24 +206,7 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
     int wmask = wtiles;                           // first tile that needs a mask
     if (causal) wmask = min(wmask, qw0 / BK);
     if (Lk % BK) wmask = min(wmask, Lk / BK);
-
-    // ---- Q (B operands of S^T = K Q^T): lane (g, c) holds row qw0 + 32 qb + c,
-    // bytes 64 ks + 32 g .. + 31; rows at or past Lq are zero
-    i32x8 qf[NQB][2];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-        const int qi = qw0 + 32 * qb + c;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-            if (qi < Lq) {
-                const uint4 *src = reinterpret_cast<const uint4 *>(Q + (qrow0 + qi) * D + 64 * ks + 32 * g);
-                lo = src[0];
-                hi = src[1];
-            }
-            qf[qb][ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
-    }
+    const int nend = ((ntiles + 3) / 4) * 4;
 
     const int unit_scale = kUnitScale;
     f32x16 oacc[NQB][4];
@@ -219,13 +237,14 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
         const int row = 8 * (LPW * wave + i) + (lane >> 3);
         dmo[i] = row * ROWB + (((lane & 7) ^ swz8(row)) << 4);
     }
-    auto issue = [&](uint8_t *kd, uint8_t *vd, int t) __attribute__((always_inline)) {
-        const int j0 = t * BK;
-        const int bytes = max(0, Lk - j0) * ROWB;   // < 2^31: the ABI bounds Nk * 128
+    // loads of tile j0 / BK from K and V rows kb, vb of length len into slots kd, vd
+    auto issue_at = [&](uint8_t *kd, uint8_t *vd, const uint8_t *kb, const uint8_t *vb, int j0, int len)
+        __attribute__((always_inline)) {
+        const int bytes = max(0, len - j0) * ROWB;   // < 2^31: the ABI bounds Nk * 128
         const __amdgpu_buffer_rsrc_t rk =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(Kh) + (size_t)j0 * D, 0, bytes, kRsrcWord3);
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(kb) + (size_t)j0 * D, 0, bytes, kRsrcWord3);
         const __amdgpu_buffer_rsrc_t rv =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(Vh) + (size_t)j0 * D, 0, bytes, kRsrcWord3);
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(vb) + (size_t)j0 * D, 0, bytes, kRsrcWord3);
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (void __attribute__((address_space(3))) *)(kd + (LPW * wave + i) * 1024),
@@ -234,6 +253,71 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
                                                      16, dmo[i], 0, 0, 0);
         }
     };
+    // tile t of this block
+    auto issue = [&](uint8_t *kd, uint8_t *vd, int t) __attribute__((always_inline)) {
+        issue_at(kd, vd, Kh, Vh, t * BK, Lk);
+    };
+    // tile t of the ring in the last group of four iterations: with PERSIST,
+    // tile nend + i (past this block's padded end, where the ring would load
+    // zeros) is tile i of the next block, if there is one.  The selects are
+    // uniform, but the compiler evaluates them on the vector ALU; rfl keeps
+    // the resources in scalar registers (else every load loops over lanes).
+    const uint8_t *Kn = K + (size_t)(nxt.b * Hkv + nxt.kvh) * Nk * D;
+    const uint8_t *Vn = V + (size_t)(nxt.b * Hkv + nxt.kvh) * Nk * D;
+    auto issue_last = [&](uint8_t *kd, uint8_t *vd, int t) __attribute__((always_inline)) {
+        if constexpr (!PERSIST) {
+            issue(kd, vd, t);
+        } else {
+            const bool next = t >= nend;
+            issue_at(kd, vd, uniform_ptr(next ? Kn : Kh), uniform_ptr(next ? Vn : Vh),
+                     rfl((next ? t - nend : t) * BK), rfl((next && !has_next) ? 0 : Lk));
+        }
+    };
+    // Q rows q0 .. q0 + BQ - 1 of block n into qs (PERSIST): wave w copies its
+    // own 32 rows, 4 loads of 1 KiB laid out like a tile's; rows at or past
+    // Nq read as zeros
+    auto issue_q = [&](const Blk &n) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(Q) + ((size_t)(n.b * Hq + n.h) * Nq + n.q0) * D, 0,
+            max(0, Nq - n.q0) * ROWB, kRsrcWord3);
+#pragma unroll
+        for (int i = 0; i < QW * ROWB / 1024; ++i) {
+            const int blk = (QW * ROWB / 1024) * wave + i, row = 8 * blk + (lane >> 3);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3))) *)(qs + blk * 1024), 16,
+                                                     row * ROWB + (((lane & 7) ^ swz8(row)) << 4), 0, 0, 0);
+        }
+    };
+    if (PERSIST && first) {
+        issue_q(cur);
+        issue(k0, v0, 0);
+        issue(k1, v1, 1);
+        issue(k2, v2, 2);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    // ---- Q (B operands of S^T = K Q^T): lane (g, c) holds row qw0 + 32 qb + c,
+    // bytes 64 ks + 32 g .. + 31; rows at or past Lq are zero
+    i32x8 qf[NQB][2];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        const int qi = qw0 + 32 * qb + c;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+            if constexpr (PERSIST) {
+                // this wave's rows of qs: row 32 wave + 32 qb + c, chunks 4 ks + 2 g, + 1
+                const int row = QW * wave + 32 * qb + c, ch = 4 * ks + 2 * g;
+                lo = *reinterpret_cast<const uint4 *>(qs + row * ROWB + ((ch ^ swz8(row)) << 4));
+                hi = *reinterpret_cast<const uint4 *>(qs + row * ROWB + (((ch + 1) ^ swz8(row)) << 4));
+            } else if (qi < Lq) {
+                const uint4 *src = reinterpret_cast<const uint4 *>(Q + (qrow0 + qi) * D + 64 * ks + 32 * g);
+                lo = src[0];
+                hi = src[1];
+            }
+            qf[qb][ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+    }
 
     // K operand (rows of a 32-key block, permuted): lane (g, c) with
     // c = 8 r + 4 hh + u reads key row 16 hh + 4 r + u, chunks 4 ks + 2 g and + 1;
@@ -388,34 +472,65 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
     // past the end are zero fills), so the wait count is the same everywhere.
     // Two score buffers alternate: even iterations read sa and fill sb.
     f32x16 sa[2][NQB], sb[2][NQB];
-    auto iter = [&](auto S, int j) __attribute__((always_inline)) {
+    // With PERSIST and a next block, the 4 loads copying its Q are issued
+    // after S(0) (below), behind this block's tiles 1 and 2 and the previous
+    // block's O stores: tiles 1 and 2 are then followed by at least 6 memory
+    // operations, and iterations 0 and 1 wait with vmcnt(6).
+    auto iter = [&](auto S, auto LAST, int j) __attribute__((always_inline)) {
         constexpr int si = decltype(S)::value;
-        __builtin_amdgcn_s_waitcnt(kWaitVm2);
+        if (PERSIST && has_next && j < 2)
+            __builtin_amdgcn_s_waitcnt(kWaitVm6);
+        else
+            __builtin_amdgcn_s_waitcnt(kWaitVm2);
         tile_barrier();
-        issue(kslot(Slot<si + 3>{}), vslot(Slot<si + 3>{}), j + 3);
+        if constexpr (decltype(LAST)::value)
+            issue_last(kslot(Slot<si + 3>{}), vslot(Slot<si + 3>{}), j + 3);
+        else
+            issue(kslot(Slot<si + 3>{}), vslot(Slot<si + 3>{}), j + 3);
         if (j < wtiles) {
             if constexpr (si % 2 == 0) body(kslot(Slot<si + 1>{}), vslot(S), j, sa, sb);
             else body(kslot(Slot<si + 1>{}), vslot(S), j, sb, sa);
         }
     };
 
-    issue(k0, v0, 0);
-    issue(k1, v1, 1);
-    issue(k2, v2, 2);
-    __builtin_amdgcn_s_waitcnt(kWaitVm4);       // this wave's part of tile 0
-    tile_barrier();
+    // (with PERSIST tile 0 is resident already: loaded at the start, or by
+    // the previous block's last iterations, whose final wait and barrier
+    // cover it)
+    if (!PERSIST) {
+        issue(k0, v0, 0);
+        issue(k1, v1, 1);
+        issue(k2, v2, 2);
+        __builtin_amdgcn_s_waitcnt(kWaitVm4);       // this wave's part of tile 0
+        tile_barrier();
+    }
     if (wtiles > 0) {
         qk(k0, sa);
         tmax(sa, 0, tmc);
     }
-    const int nend = ((ntiles + 3) / 4) * 4;
-    for (int j = 0; j < nend; j += 4) {
-        iter(Slot<0>{}, j);
-        iter(Slot<1>{}, j + 1);
-        iter(Slot<2>{}, j + 2);
-        iter(Slot<3>{}, j + 3);
+    if (has_next) {
+        // this wave's reads of qs are complete (its own rows only): copy the
+        // next block's Q over them
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        issue_q(nxt);
     }
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);       // no load outlives the kernel
+    // the last group of four iterations is the only one that loads past
+    // the padded end (tiles nend .. nend + 2)
+    int j = 0;
+    for (; j + 4 < nend; j += 4) {
+        iter(Slot<0>{}, Slot<0>{}, j);
+        iter(Slot<1>{}, Slot<0>{}, j + 1);
+        iter(Slot<2>{}, Slot<0>{}, j + 2);
+        iter(Slot<3>{}, Slot<0>{}, j + 3);
+    }
+    if (j < nend) {
+        iter(Slot<0>{}, Slot<1>{}, j);
+        iter(Slot<1>{}, Slot<1>{}, j + 1);
+        iter(Slot<2>{}, Slot<1>{}, j + 2);
+        iter(Slot<3>{}, Slot<1>{}, j + 3);
+    }
+    // no load outlives the last block (the next block's tiles 1 and 2 stay
+    // in flight otherwise)
+    if (!has_next) __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
     // ---- epilogue: O = v_scale O~ / l, LSE = m + log l ------------------------
     acc_settle8(oacc);
@@ -441,7 +556,30 @@ attn_fwd_fp8_d128(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
                 LSE[qrow0 + qi] = valid ? (m[qb] * scale_log2 + __log2f(lt)) * kLn2 : kNegInf;
         }
     }
+    if (!has_next) break;
+    L = Lnext;
+    first = false;
+    }   // blocks
 }
+
+#define OSM_FP8_PARAMS                                                                              \
+    const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K, const uint8_t *__restrict__ V,    \
+        uint16_t *__restrict__ O, float *__restrict__ LSE, int Hq, int Hkv, int Nq, int Nk,         \
+        const int32_t *__restrict__ seqlens_q, const int32_t *__restrict__ seqlens_k,               \
+        float scale_log2, float v_scale, int causal, int nqb, int xcd_heads, int nblocks
+
+// one query block per workgroup
+__global__ void __launch_bounds__(NT, 1) attn_fwd_fp8_d128(OSM_FP8_PARAMS) {
+    attn_fp8_body<false>(Q, K, V, O, LSE, Hq, Hkv, Nq, Nk, seqlens_q, seqlens_k, scale_log2, v_scale, causal,
+                         nqb, xcd_heads, nblocks);
+}
+
+// one workgroup per compute unit walking several query blocks
+__global__ void __launch_bounds__(NT, 1) attn_fwd_fp8_d128_persist(OSM_FP8_PARAMS) {
+    attn_fp8_body<true>(Q, K, V, O, LSE, Hq, Hkv, Nq, Nk, seqlens_q, seqlens_k, scale_log2, v_scale, causal,
+                        nqb, xcd_heads, nblocks);
+}
+#undef OSM_FP8_PARAMS
 
 }  // namespace
 
@@ -451,11 +589,29 @@ hipError_t launch_attn_fwd_fp8(const AttnFwdFp8Args &a, hipStream_t s) {
     const int64_t blocks = (int64_t)nqb * nheads;
     if (blocks == 0) return hipSuccess;
     const int xcd_heads = (nheads % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL(attn_fwd_fp8_d128, dim3((unsigned)blocks), dim3(NT), 0, s,
-                       static_cast<const uint8_t *>(a.q), static_cast<const uint8_t *>(a.k),
-                       static_cast<const uint8_t *>(a.v), static_cast<uint16_t *>(a.o), a.lse,
-                       a.heads_q, a.heads_kv, a.seqlen_q, a.seqlen_k, a.seqlens_q, a.seqlens_k,
-                       a.scale * kLog2e, a.v_scale, a.causal, nqb, xcd_heads);
+    // full-length non-causal inputs with more blocks than compute units run
+    // on a persistent grid of one workgroup per compute unit
+    int cus = 0;
+    if (!a.causal && !a.seqlens_q && !a.seqlens_k && a.seqlen_k > 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 0;
+        cus &= ~7;   // whole XCDs' worth, so block L keeps running on XCD L % 8
+    }
+    const bool persist = cus > 0 && blocks > cus;
+    const unsigned grid = persist ? (unsigned)cus : (unsigned)blocks;
+    const uint8_t *q = static_cast<const uint8_t *>(a.q), *k = static_cast<const uint8_t *>(a.k),
+                  *v = static_cast<const uint8_t *>(a.v);
+    uint16_t *o = static_cast<uint16_t *>(a.o);
+    if (persist)
+        hipLaunchKernelGGL(attn_fwd_fp8_d128_persist, dim3(grid), dim3(NT), 0, s, q, k, v, o, a.lse, a.heads_q,
+                           a.heads_kv, a.seqlen_q, a.seqlen_k, a.seqlens_q, a.seqlens_k, a.scale * kLog2e,
+                           a.v_scale, a.causal, nqb, xcd_heads, (int)blocks);
+    else
+        hipLaunchKernelGGL(attn_fwd_fp8_d128, dim3(grid), dim3(NT), 0, s, q, k, v, o, a.lse, a.heads_q,
+                           a.heads_kv, a.seqlen_q, a.seqlen_k, a.seqlens_q, a.seqlens_k, a.scale * kLog2e,
+                           a.v_scale, a.causal, nqb, xcd_heads, (int)blocks);
     return hipGetLastError();
 }
 

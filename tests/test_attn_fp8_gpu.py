@@ -148,3 +148,32 @@ def test_max_key_length_and_head_offsets(orc):
     o_ref, lse_ref = orc.attention(qh, kh, vh, scale=scale)
     del kh, vh
     check_fp8(oh[0, h, rows], lh[0, h, rows], o_ref, lse_ref)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk", [
+    (1, 8, 8, 9000, 1),        # one key: the shortest blocks (one tile, zero fills up to four)
+    (2, 16, 4, 2100, 300),     # GQA 4:1, ragged last query block and last key tile
+    (1, 9, 3, 7500, 70),       # 9 heads: no per-XCD head grouping
+])
+def test_persistent_grid(orc, B, Hq, Hkv, Nq, Nk):
+    """Full-length non-causal inputs with more query blocks than compute
+    units run on a persistent grid (each workgroup walks several blocks,
+    prefetching the next block's Q and first key tiles).  Explicit full
+    lengths select the one-block-per-workgroup kernel, whose per-block
+    arithmetic is the same: the outputs must agree bit for bit.  Sampled rows
+    are also checked against the oracle (the full-size workload runs on the
+    persistent grid in test_full_size_sampled)."""
+    announce(f"fwd fp8 persistent grid B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk}")
+    torch = torch_mod()
+    assert B * Hq * ((Nq + 255) // 256) > torch.cuda.get_device_properties(0).multi_processor_count
+    inp = inputs.attention_inputs(B, Hq, Hkv, Nq, Nk, 128, seed=9100 + B + Hq + Nq + Nk, dtype="fp8")
+    q, k, v = dev_u8(inp.q), dev_u8(inp.k), dev_u8(inp.v)
+    o1, l1 = osm.attn_fwd_fp8(q, k, v, scale=inp.scale)
+    o2, l2 = osm.attn_fwd_fp8(q, k, v, scale=inp.scale, seqlens_q=dev_i32(np.full(B, Nq, np.int32)),
+                              seqlens_k=dev_i32(np.full(B, Nk, np.int32)))
+    assert np.array_equal(host_bits(o1), host_bits(o2))
+    assert np.array_equal(host_bits(l1), host_bits(l2))
+    g = np.random.default_rng(Nq + Nk)
+    rows = np.unique(np.concatenate([g.integers(0, B * Hq * Nq, 300), [0, 255, 256, Nq - 1, B * Hq * Nq - 1]]))
+    o_ref, lse_ref = oracle(orc, inp, rows=rows)
+    check_fp8(host(o1).reshape(-1, 128)[rows], host(l1).reshape(-1)[rows], o_ref, lse_ref)
