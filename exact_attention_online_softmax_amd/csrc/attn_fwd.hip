@@ -105,11 +105,15 @@ constexpr int item_i(int n) { return (n & 7) + 8 * (n >> 4); }
 // inline assembly because the compiler picks one register form for every
 // MFMA of a kernel, and the score MFMAs must write VGPRs (the softmax reads
 // them) while the 128 output registers per lane only fit in the AGPRs.  The
-// hazard recognizer does not look inside inline assembly, so the two wait
-// states a VALU write needs before an MFMA reads it are spelled out here;
-// back-to-back accumulation into the same registers needs none.
+// hazard recognizer does not look inside inline assembly: an MFMA needs two
+// wait states after a VALU instruction writes one of its operands.  In the
+// tile body no VALU instruction writes them near the MFMA: the V^T operand
+// comes straight from LDS reads, and each P~ operand is converted at least
+// one full MFMA step (an MFMA and its vector work) before its first use, so
+// the wait states are there without a nop.  Back-to-back accumulation into
+// the same registers needs none.
 __device__ __forceinline__ void mfma_acc(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
-    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
 __device__ __forceinline__ void acc_zero(f32x16 &acc, const bf16x8 &z) {
