@@ -138,7 +138,8 @@ merge_lse_kernel(const TI *__restrict__ op, const float *__restrict__ lp, int64_
 }
 
 // Fast path: each row is LPR lanes x 16 bytes of o (VE elements per lane),
-// 64 / LPR rows per wave.  Pieces go in batches of 8: their lse values are
+// 64 / LPR rows per wave.  Up to 8 pieces: every load of a row is issued at
+// once.  More pieces go in batches of 8: their lse values are
 // read by every lane of the row (one cache line), their o vectors are all
 // requested before any is used.  An empty piece gets weight 0 through a
 // select, so whatever its o holds (NaN included) never reaches the sum.
@@ -159,6 +160,60 @@ merge_lse_rows(const TI *__restrict__ op, const float *__restrict__ lp, int64_t 
         const int64_t r = r0 + sub;
         const bool live = r < rows;
         const int64_t rc = live ? r : rows - 1;  // rows past the end read the last row, write nothing
+        const TI *base = op + rc * HD + part * VE;
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        if (S <= BATCH) {
+            // one memory round trip: every o vector and lse value of the row
+            // is requested before any is used (each piece is read once:
+            // nontemporal loads)
+            uint4 x[BATCH];
+            float l[BATCH];
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k) {
+                const int sk = (k < S) ? k : S - 1;
+                const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + (int64_t)sk * part_stride));
+                x[k] = make_uint4(t[0], t[1], t[2], t[3]);
+                l[k] = (k < S) ? lp[(int64_t)k * rows + rc] : kNegInf;
+            }
+            float mx = kNegInf;
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k) mx = fmaxf(mx, l[k]);
+            float sum = 0.0f;
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k) sum += (l[k] == kNegInf) ? 0.0f : exp_acc(l[k] - mx);
+            const float L = (mx == kNegInf) ? kNegInf : mx + logf(sum);
+            float acc[VE];
+#pragma unroll
+            for (int e = 0; e < VE; ++e) acc[e] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k) {
+                // an empty piece (or every piece empty: L = -inf) weighs 0
+                const float w = (l[k] == kNegInf) ? 0.0f : exp_acc(l[k] - L);
+                float v[VE];
+                if constexpr (sizeof(TI) == 2) {
+                    const uint32_t q[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[2 * e] = bf16_lo(q[e]);
+                        v[2 * e + 1] = bf16_hi(q[e]);
+                    }
+                } else {
+                    v[0] = __uint_as_float(x[k].x);
+                    v[1] = __uint_as_float(x[k].y);
+                    v[2] = __uint_as_float(x[k].z);
+                    v[3] = __uint_as_float(x[k].w);
+                }
+#pragma unroll
+                for (int e = 0; e < VE; ++e) acc[e] = (w == 0.0f) ? acc[e] : fmaf(w, v[e], acc[e]);
+            }
+            if (live) {
+                TO *orow = o + r * HD + part * VE;
+#pragma unroll
+                for (int e = 0; e < VE; e += 2) Elem<TO>::put2(orow + e, acc[e], acc[e + 1]);
+                if (lse && part == 0) lse[r] = L;
+            }
+            continue;
+        }
         // ---- pass 1: M = max lse_s, then L = M + log sum_s e^(lse_s - M) ----
         float mx = kNegInf;
         for (int s0 = 0; s0 < S; s0 += BATCH) {
@@ -182,7 +237,6 @@ merge_lse_rows(const TI *__restrict__ op, const float *__restrict__ lp, int64_t 
         float acc[VE];
 #pragma unroll
         for (int e = 0; e < VE; ++e) acc[e] = 0.0f;
-        const TI *base = op + rc * HD + part * VE;
         if (mx != kNegInf)
             for (int s0 = 0; s0 < S; s0 += BATCH) {
                 float w[BATCH];
@@ -191,7 +245,6 @@ merge_lse_rows(const TI *__restrict__ op, const float *__restrict__ lp, int64_t 
                 for (int k = 0; k < BATCH; ++k) {
                     const int sk = (s0 + k < S) ? s0 + k : S - 1;
                     // each piece is read once: nontemporal (streaming) loads, 5% faster
-                    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
                     const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + (int64_t)sk * part_stride));
                     x[k] = make_uint4(t[0], t[1], t[2], t[3]);
                 }
