@@ -287,15 +287,16 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[qb][i] = kNegInf;
-    float m[2], msub[2], l[2];
+    constexpr float kLazy = 8.0f;                 // allowed growth, base-2 units
+    const float lazy_raw = kLazy / scale_log2;    // the same in raw score units
+    float m[2], mlim[2], msub[2], l[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         m[qb] = kNegInf;     // reference maximum of raw scores q.k
+        mlim[qb] = kNegInf;  // m + lazy_raw: tile maxima up to it keep the reference
         msub[qb] = 0.0f;     // m * scale * log2(e) (0 while m = -inf)
         l[qb] = 0.0f;        // this lane's half of the running sum
     }
-    constexpr float kLazy = 8.0f;                 // allowed growth, base-2 units
-    const float lazy_raw = kLazy / scale_log2;    // the same in raw score units
 
     // ---- direct HBM -> LDS tile loads -----------------------------------
     // Load i of wave w fills LDS block 2 w + i (rows 4 (2 w + i) .. +3) of a
@@ -476,12 +477,23 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     // on which common reference was used.  When it moves, O~ and l are
     // rescaled by exp2(m_old - m_new) (0 when m_old is -inf: nothing
     // accumulated yet).
-    auto update_ref = [&](const float (&tm)[2]) __attribute__((always_inline)) {
-        if (!__all((tm[0] <= m[0] + lazy_raw) && (tm[1] <= m[1] + lazy_raw))) {
+    //
+    // th holds this lane's half of each query's tile maximum (lanes l and
+    // l ^ 32 hold the two halves of one query's scores).  Every lane being
+    // within its bound is the same test as every query's full maximum being
+    // within it, so the halves are only combined when the reference moves.
+    // mlim = m + kLazy in raw units, kept beside m.
+    auto update_ref = [&](const float (&th)[2]) __attribute__((always_inline)) {
+        // (one ballot per comparison: the compare writes the lane mask that
+        // the ballot reads, with no conversion to a value and back)
+        if ((__builtin_amdgcn_ballot_w64(th[0] > mlim[0]) | __builtin_amdgcn_ballot_w64(th[1] > mlim[1])) != 0) {
             acc_settle(oacc);
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
-                const float mn = fmaxf(m[qb], tm[qb]);
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(th[qb]), __float_as_uint(th[qb]),
+                                                                 false, false);
+                const float tm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+                const float mn = fmaxf(m[qb], tm);
                 const float alpha = (mn == kNegInf || m[qb] == mn) ? 1.0f
                                   : (m[qb] == kNegInf ? 0.0f : fast_exp2((m[qb] - mn) * scale_log2));
                 l[qb] *= alpha;
@@ -490,6 +502,7 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 #pragma unroll
                     for (int i = 0; i < 16; ++i) oacc[qb][dt][i] *= alpha;
                 m[qb] = mn;
+                mlim[qb] = mn + lazy_raw;
                 msub[qb] = (mn == kNegInf) ? 0.0f : mn * scale_log2;
             }
         }
@@ -644,16 +657,14 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
             l[qb] += (rs[qb][0] + rs[qb][1]) + (rs[qb][2] + rs[qb][3]);
             sacc[qb] = sn[qb];
         }
-        float tm[2];
+        float th[2];    // this lane's half of the tile maximum
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            const float t = fmaxf(px[qb][0], px[qb][3]);
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
-            tm[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            th[qb] = fmaxf(px[qb][0], px[qb][3]);
             // past the last tile the scores are of stale LDS data: unused
-            if (masked && j + 1 >= wtiles) tm[qb] = kNegInf;
+            if (masked && j + 1 >= wtiles) th[qb] = kNegInf;
         }
-        update_ref(tm);
+        update_ref(th);
     };
 
     // ---- prologue: tiles 0 .. AHEAD-1 in flight, S(0) and its maximum ----
@@ -677,6 +688,7 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
         for (int qb = 0; qb < 2; ++qb) {
             // nothing accumulated yet: take the tile maximum as reference
             m[qb] = tm[qb];
+            mlim[qb] = tm[qb] + lazy_raw;
             msub[qb] = (tm[qb] == kNegInf) ? 0.0f : tm[qb] * scale_log2;
         }
     }
