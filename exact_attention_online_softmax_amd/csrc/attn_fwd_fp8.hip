@@ -217,17 +217,18 @@ attn_fp8_body(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) acc_zero8(oacc[qb][dt], z8, unit_scale);
     }
-    float m[NQB], msub[NQB], l[NQB];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-        m[qb] = kNegInf;     // reference maximum of raw scores q.k
-        msub[qb] = 0.0f;     // m * scale * log2(e) (0 while m = -inf)
-        l[qb] = 0.0f;        // this lane's part of the running sum
-    }
     // The reference only moves when a tile's maximum exceeds it by more than
     // 2^8 in weight, so every P~ is at most 2^8 (E4M3 holds up to 448).
     constexpr float kLazy = 8.0f;
     const float lazy_raw = kLazy / scale_log2;
+    float m[NQB], mlim[NQB], msub[NQB], l[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        m[qb] = kNegInf;     // reference maximum of raw scores q.k
+        mlim[qb] = kNegInf;  // m + lazy_raw: tile maxima up to it keep the reference
+        msub[qb] = 0.0f;     // m * scale * log2(e) (0 while m = -inf)
+        l[qb] = 0.0f;        // this lane's part of the running sum
+    }
 
     // ---- tile DMA: load i of wave w fills LDS block LPW w + i (8 rows);
     // lane l row 8 blk + l/8, slot l%8, holding global chunk slot ^ swz8(row)
@@ -383,20 +384,27 @@ attn_fp8_body(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
             x = fmaxf(x, s[1][qb][1]);
 #pragma unroll
             for (int i = 2; i < 16; ++i) x = fmaxf(fmaxf(x, s[0][qb][i]), s[1][qb][i]);
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-            tm[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            tm[qb] = x;     // this lane's half; lane l ^ 32 holds the other
         }
     };
-    float tmc[NQB];     // tile maximum of the scores whose softmax is next
+    float tmc[NQB];     // this lane's half of the tile maximum of the scores whose softmax is next
     auto body = [&](const uint8_t *kn, const uint8_t *vb, int t, f32x16 (&s)[2][NQB], f32x16 (&sn)[2][NQB])
         __attribute__((always_inline)) {
-        float tm[NQB];
+        // tmc holds this lane's half of each query's tile maximum.  Every
+        // lane being within m + kLazy (mlim) is the same test as every full
+        // maximum being within it, so the halves are combined only when the
+        // reference moves (one ballot per comparison).
+        uint64_t over = 0;
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) tm[qb] = tmc[qb];
-        bool keep = true;
+        for (int qb = 0; qb < NQB; ++qb) over |= __builtin_amdgcn_ballot_w64(tmc[qb] > mlim[qb]);
+        if (over != 0) {
+            float tm[NQB];
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) keep = keep && (tm[qb] <= m[qb] + lazy_raw);
-        if (!__all(keep)) {
+            for (int qb = 0; qb < NQB; ++qb) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmc[qb]), __float_as_uint(tmc[qb]),
+                                                                 false, false);
+                tm[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            }
             acc_settle8(oacc);
 #pragma unroll
             for (int qb = 0; qb < NQB; ++qb) {
@@ -409,6 +417,7 @@ attn_fp8_body(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
 #pragma unroll
                     for (int i = 0; i < 16; ++i) oacc[qb][dt][i] *= alpha;
                 m[qb] = mn;
+                mlim[qb] = mn + lazy_raw;
                 msub[qb] = (mn == kNegInf) ? 0.0f : mn * scale_log2;
             }
         }
