@@ -200,3 +200,40 @@ def test_persistent_grid(orc, B, Hq, Hkv, Nq, Nk):
     rows = _sample_rows(np.random.default_rng(Nq + Nk), B, Hq, Nq, 300)
     o_ref, lse_ref = oracle(orc, inp, rows=rows)
     check_attn(host(o1).reshape(-1, 128)[rows], host(l1).reshape(-1)[rows], o_ref, lse_ref, "bf16")
+
+
+@pytest.mark.parametrize("persistent", [True, False])
+def test_lse_null(persistent):
+    """The C ABI lets lse be NULL: O is the same, bit for bit, as with an
+    lse buffer, for the bf16 and the FP8 forward, on the persistent grid
+    (full-length non-causal, 264 query blocks) and on one block per
+    workgroup (causal, ragged lengths)."""
+    announce(f"fwd lse NULL persistent={persistent}")
+    torch = torch_mod()
+    lib = osm.load_library()
+    if persistent:
+        B, Hq, Hkv, Nq, Nk, causal, lens = 1, 8, 4, 8448, 70, False, None
+    else:
+        B, Hq, Hkv, Nq, Nk, causal, lens = 2, 4, 2, 300, 300, True, np.array([300, 131], np.int32)
+    sl = None if lens is None else dev_i32(lens)
+    for dtype in ("bf16", "fp8"):
+        inp = inputs.attention_inputs(B, Hq, Hkv, Nq, Nk, 128, seed=91 + Nq, causal=causal, dtype=dtype,
+                                      seqlens_q=lens, seqlens_k=lens)
+        if dtype == "bf16":
+            q, k, v = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v)
+            o1, _ = osm.attn_fwd(q, k, v, scale=inp.scale, causal=causal, seqlens_q=sl, seqlens_k=sl)
+        else:
+            q, k, v = (torch.from_numpy(np.ascontiguousarray(t)).to("cuda") for t in (inp.q, inp.k, inp.v))
+            o1, _ = osm.attn_fwd_fp8(q, k, v, scale=inp.scale, causal=causal, seqlens_q=sl, seqlens_k=sl)
+        o2 = torch.full_like(o1, float("nan"))
+        if dtype == "bf16":
+            st = lib.osm_attn_fwd(osm._ptr(q), osm._ptr(k), osm._ptr(v), osm._ptr(o2), None, 1, B, Hq, Hkv, Nq,
+                                  Nk, 128, osm._ptr(sl), osm._ptr(sl), float(inp.scale), int(causal),
+                                  osm._stream())
+        else:
+            st = lib.osm_attn_fwd_fp8(osm._ptr(q), osm._ptr(k), osm._ptr(v), osm._ptr(o2), None, B, Hq, Hkv, Nq,
+                                      Nk, 128, osm._ptr(sl), osm._ptr(sl), float(inp.scale), 1.0, int(causal),
+                                      osm._stream())
+        assert st == 0, lib.osm_status_str(st)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(o1), host_bits(o2)), dtype
