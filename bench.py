@@ -150,9 +150,12 @@ def summarize(name, trace_dir, out):
                 avg_ns = sum(d) / len(d)
         lines.append("")
     counters = {}
+    pmc_ns = []    # kernel durations of the counter runs' dispatches
     for f in sorted(glob.glob(os.path.join(trace_dir, "pmc_*", "run_counter_collection.csv"))):
         per = {}
         for r in csv.DictReader(open(f)):
+            if kern in r["Kernel_Name"] and r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                pmc_ns.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
             # the calibration copy is torch's device-to-device copy_, which
             # runs the HIP runtime's buffer-copy kernel
             key = ("copy" if "copyBuffer" in r["Kernel_Name"]
@@ -167,7 +170,8 @@ def summarize(name, trace_dir, out):
             counters[k] = max(d.values()) if k[0] == "copy" else sum(d.values()) / len(d)
     cal = None
     if counters:
-        lines += ["## counters per dispatch (--pmc), KiB", "", "| kernel | counter | KiB |", "|---|---|---|"]
+        lines += ["## counters per dispatch (--pmc)", "", "| kernel | counter | value (FETCH_SIZE, WRITE_SIZE in KiB) |",
+                  "|---|---|---|"]
         for (k, c), v in sorted(counters.items()):
             lines.append(f"| {k} | {c} | {v:.0f} |")
         lines.append("")
@@ -182,6 +186,19 @@ def summarize(name, trace_dir, out):
                    + counters.get(("kernel", "WRITE_SIZE"), 0.0) * 1024 * w_scale)
         lines += [f"copy calibration: {copy_bytes:.0f} bytes read and written by the copy; "
                   f"FETCH_SIZE scale {f_scale:.4f}, WRITE_SIZE scale {w_scale:.4f}", ""]
+    if ("kernel", "SQ_VALU_MFMA_BUSY_CYCLES") in counters and ("kernel", "GRBM_GUI_ACTIVE") in counters and pmc_ns:
+        # GRBM_GUI_ACTIVE is summed over the 8 XCDs; SQ_VALU_MFMA_BUSY_CYCLES over
+        # the 1024 SIMDs, in cycles of the matrix pipe at its full issue rate
+        cycles = counters[("kernel", "GRBM_GUI_ACTIVE")] / 8
+        busy = counters[("kernel", "SQ_VALU_MFMA_BUSY_CYCLES")] / 1024
+        ns = sum(pmc_ns) / len(pmc_ns)
+        lines += [f"engine clock over the kernel: {cycles / ns:.2f} GHz (GRBM_GUI_ACTIVE per XCD / {ns / 1e3:.1f} us)",
+                  f"MFMA busy: {100 * busy / cycles:.1f}% of the kernel's cycles per SIMD "
+                  f"(SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / cycles)"]
+        if ("kernel", "SQ_INSTS_VALU_MFMA_MOPS_BF16") in counters:
+            lines.append(f"bf16 MFMA flops executed per launch: "
+                         f"{counters[('kernel', 'SQ_INSTS_VALU_MFMA_MOPS_BF16')] * 512:.4e} (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)")
+        lines.append("")
     lines += [f"kernel_source_sha256_16: {source_hash(name)}",
               f"avg_kernel_us: {avg_ns / 1e3:.2f}" if avg_ns else "avg_kernel_us: null",
               f"traffic_bytes_per_launch: {traffic:.0f}" if traffic else "traffic_bytes_per_launch: null", ""]
