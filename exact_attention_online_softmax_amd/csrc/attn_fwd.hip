@@ -225,537 +225,538 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     int L = blockIdx.x;
     bool first = true;
     for (;;) {
-    const Blk cur = decode(L);
-    const int Lnext = L + (int)gridDim.x;
-    const bool has_next = PERSIST && __builtin_amdgcn_readfirstlane(Lnext < nblocks ? 1 : 0) != 0;
-    const Blk nxt = decode(has_next ? Lnext : L);
-    const int b = cur.b, h = cur.h, kvh = cur.kvh, q0 = cur.q0;
-    // lengths and the wave index are uniform: keep them in scalar registers
-    // so that every tile-level decision is a scalar branch
-    const int Lq = __builtin_amdgcn_readfirstlane(seqlens_q ? clampi(seqlens_q[b], 0, Nq) : Nq);
-    const int Lk = __builtin_amdgcn_readfirstlane(seqlens_k ? clampi(seqlens_k[b], 0, Nk) : Nk);
+        const Blk cur = decode(L);
+        const int Lnext = L + (int)gridDim.x;
+        const bool has_next = PERSIST && __builtin_amdgcn_readfirstlane(Lnext < nblocks ? 1 : 0) != 0;
+        const Blk nxt = decode(has_next ? Lnext : L);
+        const int b = cur.b, h = cur.h, kvh = cur.kvh, q0 = cur.q0;
+        // lengths and the wave index are uniform: keep them in scalar registers
+        // so that every tile-level decision is a scalar branch
+        const int Lq = __builtin_amdgcn_readfirstlane(seqlens_q ? clampi(seqlens_q[b], 0, Nq) : Nq);
+        const int Lk = __builtin_amdgcn_readfirstlane(seqlens_k ? clampi(seqlens_k[b], 0, Nk) : Nk);
 
-    const int qw0 = q0 + QW * wave;         // first query of this wave
-    // this lane's queries: qw0 + c (block 0) and qw0 + 32 + c (block 1)
+        const int qw0 = q0 + QW * wave;         // first query of this wave
+        // this lane's queries: qw0 + c (block 0) and qw0 + 32 + c (block 1)
 
-    const size_t qhead = (size_t)(b * Hq + h) * Nq;
-    const uint16_t *Kh = K + (size_t)(b * Hkv + kvh) * Nk * D;
-    const uint16_t *Vh = V + (size_t)(b * Hkv + kvh) * Nk * D;
+        const size_t qhead = (size_t)(b * Hq + h) * Nq;
+        const uint16_t *Kh = K + (size_t)(b * Hkv + kvh) * Nk * D;
+        const uint16_t *Vh = V + (size_t)(b * Hkv + kvh) * Nk * D;
 
-    if (!PERSIST && q0 >= Lq) {
-        // every row of this block is padding: O = 0, LSE = -inf
-        const int rows = min(BQ, Nq - q0);
-        for (int i = tid; i < rows * (D / 8); i += NT) {
-            const int r = i / (D / 8), d8 = i % (D / 8);
-            *reinterpret_cast<uint4 *>(O + (qhead + q0 + r) * D + d8 * 8) = make_uint4(0, 0, 0, 0);
+        if (!PERSIST && q0 >= Lq) {
+            // every row of this block is padding: O = 0, LSE = -inf
+            const int rows = min(BQ, Nq - q0);
+            for (int i = tid; i < rows * (D / 8); i += NT) {
+                const int r = i / (D / 8), d8 = i % (D / 8);
+                *reinterpret_cast<uint4 *>(O + (qhead + q0 + r) * D + d8 * 8) = make_uint4(0, 0, 0, 0);
+            }
+            if (LSE)
+                for (int r = tid; r < rows; r += NT) LSE[qhead + q0 + r] = kNegInf;
+            return;
         }
-        if (LSE)
-            for (int r = tid; r < rows; r += NT) LSE[qhead + q0 + r] = kNegInf;
-        return;
-    }
 
-    // keys that can be visible to some query of this block
-    int kend = Lk;
-    if (causal) kend = min(kend, min(q0 + BQ, Lq));
-    const int ntiles = (kend + BK - 1) / BK;
-    // tiles this wave computes: none if all its queries are padding; with a
-    // causal mask only tiles starting at or below its last query
-    int wtiles = (qw0 >= Lq) ? 0 : ntiles;
-    if (causal) wtiles = min(wtiles, (qw0 + QW - 1) / BK + 1);
-    // first tile that needs a mask: the causal diagonal starts at the tile
-    // holding key qw0, the ragged end at the tile holding key Lk - 1
-    int wfirst_mask = wtiles;
-    if (causal) wfirst_mask = min(wfirst_mask, qw0 / BK);
-    if (Lk % BK) wfirst_mask = min(wfirst_mask, Lk / BK);
-    // iterations j whose next tile j + 1 is computed without a mask
-    const int nfast = max(0, wfirst_mask - 1);
-    // the loops run in whole groups of four iterations (see below)
-    const int wend = (wtiles + 3) & ~3, nend = (ntiles + 3) & ~3;
+        // keys that can be visible to some query of this block
+        int kend = Lk;
+        if (causal) kend = min(kend, min(q0 + BQ, Lq));
+        const int ntiles = (kend + BK - 1) / BK;
+        // tiles this wave computes: none if all its queries are padding; with a
+        // causal mask only tiles starting at or below its last query
+        int wtiles = (qw0 >= Lq) ? 0 : ntiles;
+        if (causal) wtiles = min(wtiles, (qw0 + QW - 1) / BK + 1);
+        // first tile that needs a mask: the causal diagonal starts at the tile
+        // holding key qw0, the ragged end at the tile holding key Lk - 1
+        int wfirst_mask = wtiles;
+        if (causal) wfirst_mask = min(wfirst_mask, qw0 / BK);
+        if (Lk % BK) wfirst_mask = min(wfirst_mask, Lk / BK);
+        // iterations j whose next tile j + 1 is computed without a mask
+        const int nfast = max(0, wfirst_mask - 1);
+        // the loops run in whole groups of four iterations (see below)
+        const int wend = (wtiles + 3) & ~3, nend = (ntiles + 3) & ~3;
 
-    // O~^T accumulators, zeroed in the AGPRs by an MFMA of zeros (so they
-    // never pass through VGPRs)
-    f32x16 oacc[2][4];
-    {
-        const bf16x8 z8 = {};
+        // O~^T accumulators, zeroed in the AGPRs by an MFMA of zeros (so they
+        // never pass through VGPRs)
+        f32x16 oacc[2][4];
+        {
+            const bf16x8 z8 = {};
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) acc_zero(oacc[qb][dt], z8);
+        }
+        f32x16 sacc[2];          // S^T of the tile whose softmax is next
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) acc_zero(oacc[qb][dt], z8);
-    }
-    f32x16 sacc[2];          // S^T of the tile whose softmax is next
+            for (int i = 0; i < 16; ++i) sacc[qb][i] = kNegInf;
+        constexpr float kLazy = 8.0f;                 // allowed growth, base-2 units
+        const float lazy_raw = kLazy / scale_log2;    // the same in raw score units
+        float m[2], mlim[2], msub[2], l[2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[qb][i] = kNegInf;
-    constexpr float kLazy = 8.0f;                 // allowed growth, base-2 units
-    const float lazy_raw = kLazy / scale_log2;    // the same in raw score units
-    float m[2], mlim[2], msub[2], l[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        m[qb] = kNegInf;     // reference maximum of raw scores q.k
-        mlim[qb] = kNegInf;  // m + lazy_raw: tile maxima up to it keep the reference
-        msub[qb] = 0.0f;     // m * scale * log2(e) (0 while m = -inf)
-        l[qb] = 0.0f;        // this lane's half of the running sum
-    }
-
-    // ---- direct HBM -> LDS tile loads -----------------------------------
-    // Load i of wave w fills LDS block 2 w + i (rows 4 (2 w + i) .. +3) of a
-    // slot; lane l fills row 4 (2 w + i) + l/16, slot l%16, which holds global
-    // 16-byte chunk (slot ^ swizzle(row)).  Offsets are in bytes within a tile.
-    // The loads go through a buffer resource that starts at the tile and
-    // spans its rows below Lk: the range check turns rows past Lk (and every
-    // row of a tile at or past Lk) into zeros without touching memory, so
-    // LDS only ever holds finite data, and a load needs no branch.  The
-    // buffer (MUBUF) form of the LDS DMA is used because with the global
-    // (FLAT) form in flight the compiler turns every LDS operand wait into a
-    // wait for all LDS reads.
-    uint32_t kld[LPW], vld[LPW];
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-        const int blk = LPW * wave + i;
-        const int row = 4 * blk + (lane >> 4);
-        const int s = lane & 15;
-        kld[i] = row * ROWB + ((s ^ (row & 15)) << 4);
-        vld[i] = row * ROWB + ((s ^ ((row & 3) << 2)) << 4);
-    }
-    struct TileRsrc {
-        __amdgpu_buffer_rsrc_t k, v;
-    };
-    auto rsrc_at = [&](const uint16_t *kb, const uint16_t *vb, int j0, int len) __attribute__((always_inline)) -> TileRsrc {
-        const int bytes = max(0, len - j0) * ROWB;   // < 2^31: the ABI bounds Nk * 256
-        return {__builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(kb) + (size_t)j0 * D, 0, bytes, kRsrcWord3),
-                __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(vb) + (size_t)j0 * D, 0, bytes, kRsrcWord3)};
-    };
-    // tile t of this block; the only kind the unmasked loop loads: it stops
-    // at least two iterations short of the padded end, so t < nend there
-    // (t may pass ntiles, where the range check loads zeros)
-    auto tile_rsrc_cur = [&](int t) __attribute__((always_inline)) -> TileRsrc {
-        return rsrc_at(Kh, Vh, t * BK, Lk);
-    };
-    // With PERSIST, tile nend + i (past this block's padded end, where the
-    // ring would load zeros) is tile i of the next block, if there is one;
-    // every block has the same Lk = Nk and the same nend.  The compiler
-    // evaluates the uniform selects of that case on the vector ALU;
-    // readfirstlane keeps the resource in scalar registers, without which
-    // every load would become a loop over lanes.
-    const uint16_t *Kn = K + (size_t)(nxt.b * Hkv + nxt.kvh) * Nk * D;
-    const uint16_t *Vn = V + (size_t)(nxt.b * Hkv + nxt.kvh) * Nk * D;
-    auto tile_rsrc = [&](int t) __attribute__((always_inline)) -> TileRsrc {
-        if constexpr (!PERSIST) {
-            return tile_rsrc_cur(t);
-        } else {
-            const bool next = t >= nend;
-            const uint16_t *kb = uniform_ptr(next ? Kn : Kh), *vb = uniform_ptr(next ? Vn : Vh);
-            const int j0 = __builtin_amdgcn_readfirstlane((next ? t - nend : t) * BK);
-            const int len = __builtin_amdgcn_readfirstlane((next && !has_next) ? 0 : Lk);
-            return rsrc_at(kb, vb, j0, len);
+        for (int qb = 0; qb < 2; ++qb) {
+            m[qb] = kNegInf;     // reference maximum of raw scores q.k
+            mlim[qb] = kNegInf;  // m + lazy_raw: tile maxima up to it keep the reference
+            msub[qb] = 0.0f;     // m * scale * log2(e) (0 while m = -inf)
+            l[qb] = 0.0f;        // this lane's half of the running sum
         }
-    };
-    // one of the four loads (K block 0, V block 0, K block 1, V block 1) of
-    // this wave's share of a tile
-    auto load1 = [&](const TileRsrc &r, uint8_t *kd, uint8_t *vd, int which) __attribute__((always_inline)) {
-        const int i = which >> 1, blk = LPW * wave + i;
-        if (which & 1)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r.v, (void __attribute__((address_space(3))) *)(vd + blk * 1024), 16,
-                                                     vld[i], 0, 0, 0);
-        else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r.k, (void __attribute__((address_space(3))) *)(kd + blk * 1024), 16,
-                                                     kld[i], 0, 0, 0);
-    };
-    auto issue = [&](uint8_t *kd, uint8_t *vd, int t) __attribute__((always_inline)) {
-        const TileRsrc r = tile_rsrc(t);
-#pragma unroll
-        for (int w = 0; w < 2 * LPW; ++w) load1(r, kd, vd, w);
-    };
 
-    // Q rows q0 .. q0 + BQ - 1 of block n into qs (PERSIST): wave w copies
-    // its own 64 rows, 16 loads of 1 KiB laid out like a K tile's; rows at
-    // or past Nq read as zeros
-    auto issue_q = [&](const Blk &n) __attribute__((always_inline)) {
-        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(Q) + ((size_t)(n.b * Hq + n.h) * Nq + n.q0) * D, 0,
-            max(0, Nq - n.q0) * ROWB, kRsrcWord3);
+        // ---- direct HBM -> LDS tile loads -----------------------------------
+        // Load i of wave w fills LDS block 2 w + i (rows 4 (2 w + i) .. +3) of a
+        // slot; lane l fills row 4 (2 w + i) + l/16, slot l%16, which holds global
+        // 16-byte chunk (slot ^ swizzle(row)).  Offsets are in bytes within a tile.
+        // The loads go through a buffer resource that starts at the tile and
+        // spans its rows below Lk: the range check turns rows past Lk (and every
+        // row of a tile at or past Lk) into zeros without touching memory, so
+        // LDS only ever holds finite data, and a load needs no branch.  The
+        // buffer (MUBUF) form of the LDS DMA is used because with the global
+        // (FLAT) form in flight the compiler turns every LDS operand wait into a
+        // wait for all LDS reads.
+        uint32_t kld[LPW], vld[LPW];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int blk = 16 * wave + i, row = 4 * blk + (lane >> 4), sl = lane & 15;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3))) *)(qs + blk * 1024), 16,
-                                                     row * ROWB + ((sl ^ (row & 15)) << 4), 0, 0, 0);
+        for (int i = 0; i < LPW; ++i) {
+            const int blk = LPW * wave + i;
+            const int row = 4 * blk + (lane >> 4);
+            const int s = lane & 15;
+            kld[i] = row * ROWB + ((s ^ (row & 15)) << 4);
+            vld[i] = row * ROWB + ((s ^ ((row & 3) << 2)) << 4);
         }
-    };
-    if (PERSIST && first) {
-        issue_q(cur);
-        issue(k0, v0, 0);
-        issue(k1, v1, 1);
-        issue(k2, v2, 2);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    }
-
-    // ---- Q fragments (B operands of S^T = K Q^T), kept in registers -----
-    // lane l holds Q[qw0 + 32 qb + c][64 g + 8 ks + 0..7] for ks = 0..7
-    bf16x8 qf[2][8];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int qi = qw0 + 32 * qb + c;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            if constexpr (PERSIST) {
-                // this wave's rows of qs: row 64 wave + 32 qb + c, chunk 8 g + ks
-                const int row = QW * wave + 32 * qb + c;
-                qf[qb][ks] = *reinterpret_cast<const bf16x8 *>(qs + row * ROWB + (((8 * g + ks) ^ (row & 15)) << 4));
+        struct TileRsrc {
+            __amdgpu_buffer_rsrc_t k, v;
+        };
+        auto rsrc_at = [&](const uint16_t *kb, const uint16_t *vb, int j0, int len)
+            __attribute__((always_inline)) -> TileRsrc {
+            const int bytes = max(0, len - j0) * ROWB;   // < 2^31: the ABI bounds Nk * 256
+            return {__builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(kb) + (size_t)j0 * D, 0, bytes, kRsrcWord3),
+                    __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(vb) + (size_t)j0 * D, 0, bytes, kRsrcWord3)};
+        };
+        // tile t of this block; the only kind the unmasked loop loads: it stops
+        // at least two iterations short of the padded end, so t < nend there
+        // (t may pass ntiles, where the range check loads zeros)
+        auto tile_rsrc_cur = [&](int t) __attribute__((always_inline)) -> TileRsrc {
+            return rsrc_at(Kh, Vh, t * BK, Lk);
+        };
+        // With PERSIST, tile nend + i (past this block's padded end, where the
+        // ring would load zeros) is tile i of the next block, if there is one;
+        // every block has the same Lk = Nk and the same nend.  The compiler
+        // evaluates the uniform selects of that case on the vector ALU;
+        // readfirstlane keeps the resource in scalar registers, without which
+        // every load would become a loop over lanes.
+        const uint16_t *Kn = K + (size_t)(nxt.b * Hkv + nxt.kvh) * Nk * D;
+        const uint16_t *Vn = V + (size_t)(nxt.b * Hkv + nxt.kvh) * Nk * D;
+        auto tile_rsrc = [&](int t) __attribute__((always_inline)) -> TileRsrc {
+            if constexpr (!PERSIST) {
+                return tile_rsrc_cur(t);
             } else {
-                uint4 w = make_uint4(0, 0, 0, 0);
-                if (qi < Lq) w = *reinterpret_cast<const uint4 *>(Q + (qhead + qi) * D + 64 * g + 8 * ks);
-                qf[qb][ks] = __builtin_bit_cast(bf16x8, w);
+                const bool next = t >= nend;
+                const uint16_t *kb = uniform_ptr(next ? Kn : Kh), *vb = uniform_ptr(next ? Vn : Vh);
+                const int j0 = __builtin_amdgcn_readfirstlane((next ? t - nend : t) * BK);
+                const int len = __builtin_amdgcn_readfirstlane((next && !has_next) ? 0 : Lk);
+                return rsrc_at(kb, vb, j0, len);
             }
+        };
+        // one of the four loads (K block 0, V block 0, K block 1, V block 1) of
+        // this wave's share of a tile
+        auto load1 = [&](const TileRsrc &r, uint8_t *kd, uint8_t *vd, int which) __attribute__((always_inline)) {
+            const int i = which >> 1, blk = LPW * wave + i;
+            if (which & 1)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    r.v, (void __attribute__((address_space(3))) *)(vd + blk * 1024), 16, vld[i], 0, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    r.k, (void __attribute__((address_space(3))) *)(kd + blk * 1024), 16, kld[i], 0, 0, 0);
+        };
+        auto issue = [&](uint8_t *kd, uint8_t *vd, int t) __attribute__((always_inline)) {
+            const TileRsrc r = tile_rsrc(t);
+#pragma unroll
+            for (int w = 0; w < 2 * LPW; ++w) load1(r, kd, vd, w);
+        };
+
+        // Q rows q0 .. q0 + BQ - 1 of block n into qs (PERSIST): wave w copies
+        // its own 64 rows, 16 loads of 1 KiB laid out like a K tile's; rows at
+        // or past Nq read as zeros
+        auto issue_q = [&](const Blk &n) __attribute__((always_inline)) {
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t *>(Q) + ((size_t)(n.b * Hq + n.h) * Nq + n.q0) * D, 0,
+                max(0, Nq - n.q0) * ROWB, kRsrcWord3);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int blk = 16 * wave + i, row = 4 * blk + (lane >> 4), sl = lane & 15;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3))) *)(qs + blk * 1024), 16,
+                                                         row * ROWB + ((sl ^ (row & 15)) << 4), 0, 0, 0);
+            }
+        };
+        if (PERSIST && first) {
+            issue_q(cur);
+            issue(k0, v0, 0);
+            issue(k1, v1, 1);
+            issue(k2, v2, 2);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
         }
-    }
 
-
-    // per-lane LDS byte offsets (within a tile) of the QK A operand: row c,
-    // chunk 8 g + ks -> slot (8 g + ks) ^ (c % 16)
-    uint32_t koff[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) koff[ks] = c * ROWB + ((((8 * g) ^ (c & 15)) ^ ks) << 4);
-    // transposing V read: 16-lane group q = lane/16, index i = lane%16:
-    // row kb + i/4 (kb a multiple of 4), dims 32 dt + 16 (q%2) + 4 (i%4) ..+3
-    const int trq = lane >> 4, tri = lane & 15;
-    const int tr_row = 4 * (trq >> 1) + (tri >> 2);
-    const int tr_sw = (tri >> 2) << 2;                  // 4 * (row % 4)
-    const int tr_half = (tri & 1) * 8;
-    uint32_t voff[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-        const int chunk = 4 * dt + 2 * (trq & 1) + ((tri & 3) >> 1);
-        voff[dt] = tr_row * ROWB + ((chunk ^ tr_sw) << 4) + tr_half;
-    }
-
-    // S^T = K Q^T (raw scores) of one tile: lane holds key 8 r + 4 g + u of
-    // the tile in s[qb][4 r + u], query qw0 + 32 qb + c
-    auto qk = [&](const uint8_t *kb, f32x16 (&s)[2]) __attribute__((always_inline)) {
-        const f32x16 zero = {};
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb + koff[ks]);
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-                s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], ks ? s[qb] : zero, 0, 0, 0);
-        }
-    };
-
-    // key 32 t + 8 r + 4 g + u is visible to query q iff it is <= min(Lk-1, q)
-    // (causal) or <= Lk - 1
-    auto mask = [&](f32x16 (&s)[2], int t) __attribute__((always_inline)) {
+        // ---- Q fragments (B operands of S^T = K Q^T), kept in registers -----
+        // lane l holds Q[qw0 + 32 qb + c][64 g + 8 ks + 0..7] for ks = 0..7
+        bf16x8 qf[2][8];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const int qi = qw0 + 32 * qb + c;
-            const int lim = (causal ? min(Lk - 1, qi) : Lk - 1) - t * BK - 4 * g;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    if (8 * r + u > lim) s[qb][4 * r + u] = kNegInf;
+            for (int ks = 0; ks < 8; ++ks) {
+                if constexpr (PERSIST) {
+                    // this wave's rows of qs: row 64 wave + 32 qb + c, chunk 8 g + ks
+                    const int row = QW * wave + 32 * qb + c;
+                    qf[qb][ks] = *reinterpret_cast<const bf16x8 *>(qs + row * ROWB + (((8 * g + ks) ^ (row & 15)) << 4));
+                } else {
+                    uint4 w = make_uint4(0, 0, 0, 0);
+                    if (qi < Lq) w = *reinterpret_cast<const uint4 *>(Q + (qhead + qi) * D + 64 * g + 8 * ks);
+                    qf[qb][ks] = __builtin_bit_cast(bf16x8, w);
+                }
+            }
         }
-    };
 
-    // tile maximum of each query (both halves of the tile)
-    auto tile_max = [&](const f32x16 (&s)[2], float (&tm)[2]) __attribute__((always_inline)) {
+
+        // per-lane LDS byte offsets (within a tile) of the QK A operand: row c,
+        // chunk 8 g + ks -> slot (8 g + ks) ^ (c % 16)
+        uint32_t koff[8];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            float t = fmaxf(fmaxf(s[qb][0], s[qb][1]), s[qb][2]);
+        for (int ks = 0; ks < 8; ++ks) koff[ks] = c * ROWB + ((((8 * g) ^ (c & 15)) ^ ks) << 4);
+        // transposing V read: 16-lane group q = lane/16, index i = lane%16:
+        // row kb + i/4 (kb a multiple of 4), dims 32 dt + 16 (q%2) + 4 (i%4) ..+3
+        const int trq = lane >> 4, tri = lane & 15;
+        const int tr_row = 4 * (trq >> 1) + (tri >> 2);
+        const int tr_sw = (tri >> 2) << 2;                  // 4 * (row % 4)
+        const int tr_half = (tri & 1) * 8;
+        uint32_t voff[4];
 #pragma unroll
-            for (int i = 3; i < 15; i += 2) t = fmaxf(fmaxf(t, s[qb][i]), s[qb][i + 1]);
-            t = fmaxf(t, s[qb][15]);
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
-            tm[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        for (int dt = 0; dt < 4; ++dt) {
+            const int chunk = 4 * dt + 2 * (trq & 1) + ((tri & 3) >> 1);
+            voff[dt] = tr_row * ROWB + ((chunk ^ tr_sw) << 4) + tr_half;
         }
-    };
 
-    // The reference m only moves when some lane's tile maximum exceeds it by
-    // more than kLazy (base-2 units): every weight is then at most 2^kLazy,
-    // far from fp32/bf16 overflow, and the final O~/l and LSE do not depend
-    // on which common reference was used.  When it moves, O~ and l are
-    // rescaled by exp2(m_old - m_new) (0 when m_old is -inf: nothing
-    // accumulated yet).
-    //
-    // th holds this lane's half of each query's tile maximum (lanes l and
-    // l ^ 32 hold the two halves of one query's scores).  Every lane being
-    // within its bound is the same test as every query's full maximum being
-    // within it, so the halves are only combined when the reference moves.
-    // mlim = m + kLazy in raw units, kept beside m.
-    auto update_ref = [&](const float (&th)[2]) __attribute__((always_inline)) {
-        // (one ballot per comparison: the compare writes the lane mask that
-        // the ballot reads, with no conversion to a value and back)
-        if ((__builtin_amdgcn_ballot_w64(th[0] > mlim[0]) | __builtin_amdgcn_ballot_w64(th[1] > mlim[1])) != 0) {
-            acc_settle(oacc);
+        // S^T = K Q^T (raw scores) of one tile: lane holds key 8 r + 4 g + u of
+        // the tile in s[qb][4 r + u], query qw0 + 32 qb + c
+        auto qk = [&](const uint8_t *kb, f32x16 (&s)[2]) __attribute__((always_inline)) {
+            const f32x16 zero = {};
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb + koff[ks]);
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+                    s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], ks ? s[qb] : zero, 0, 0, 0);
+            }
+        };
+
+        // key 32 t + 8 r + 4 g + u is visible to query q iff it is <= min(Lk-1, q)
+        // (causal) or <= Lk - 1
+        auto mask = [&](f32x16 (&s)[2], int t) __attribute__((always_inline)) {
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(th[qb]), __float_as_uint(th[qb]),
-                                                                 false, false);
-                const float tm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-                const float mn = fmaxf(m[qb], tm);
-                const float alpha = (mn == kNegInf || m[qb] == mn) ? 1.0f
-                                  : (m[qb] == kNegInf ? 0.0f : fast_exp2((m[qb] - mn) * scale_log2));
-                l[qb] *= alpha;
+                const int qi = qw0 + 32 * qb + c;
+                const int lim = (causal ? min(Lk - 1, qi) : Lk - 1) - t * BK - 4 * g;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (8 * r + u > lim) s[qb][4 * r + u] = kNegInf;
+            }
+        };
+
+        // tile maximum of each query (both halves of the tile)
+        auto tile_max = [&](const f32x16 (&s)[2], float (&tm)[2]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                float t = fmaxf(fmaxf(s[qb][0], s[qb][1]), s[qb][2]);
+#pragma unroll
+                for (int i = 3; i < 15; i += 2) t = fmaxf(fmaxf(t, s[qb][i]), s[qb][i + 1]);
+                t = fmaxf(t, s[qb][15]);
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+                tm[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            }
+        };
+
+        // The reference m only moves when some lane's tile maximum exceeds it by
+        // more than kLazy (base-2 units): every weight is then at most 2^kLazy,
+        // far from fp32/bf16 overflow, and the final O~/l and LSE do not depend
+        // on which common reference was used.  When it moves, O~ and l are
+        // rescaled by exp2(m_old - m_new) (0 when m_old is -inf: nothing
+        // accumulated yet).
+        //
+        // th holds this lane's half of each query's tile maximum (lanes l and
+        // l ^ 32 hold the two halves of one query's scores).  Every lane being
+        // within its bound is the same test as every query's full maximum being
+        // within it, so the halves are only combined when the reference moves.
+        // mlim = m + kLazy in raw units, kept beside m.
+        auto update_ref = [&](const float (&th)[2]) __attribute__((always_inline)) {
+            // (one ballot per comparison: the compare writes the lane mask that
+            // the ballot reads, with no conversion to a value and back)
+            if ((__builtin_amdgcn_ballot_w64(th[0] > mlim[0]) | __builtin_amdgcn_ballot_w64(th[1] > mlim[1])) != 0) {
+                acc_settle(oacc);
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(th[qb]), __float_as_uint(th[qb]),
+                                                                     false, false);
+                    const float tm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+                    const float mn = fmaxf(m[qb], tm);
+                    const float alpha = (mn == kNegInf || m[qb] == mn) ? 1.0f
+                                      : (m[qb] == kNegInf ? 0.0f : fast_exp2((m[qb] - mn) * scale_log2));
+                    l[qb] *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) oacc[qb][dt][i] *= alpha;
+                    m[qb] = mn;
+                    mlim[qb] = mn + lazy_raw;
+                    msub[qb] = (mn == kNegInf) ? 0.0f : mn * scale_log2;
+                }
+            }
+        };
+
+        // slot buffers by (compile-time) index
+        auto kslot = [&](auto S) __attribute__((always_inline)) -> uint8_t * {
+            constexpr int s = decltype(S)::value & 3;
+            return s == 0 ? k0 : s == 1 ? k1 : s == 2 ? k2 : k3;
+        };
+        auto vslot = [&](auto S) __attribute__((always_inline)) -> uint8_t * {
+            constexpr int s = decltype(S)::value & 3;
+            return s == 0 ? v0 : s == 1 ? v1 : s == 2 ? v2 : v3;
+        };
+
+        // top of iteration j: tile j + 1 resident for every wave, and every wave
+        // done with iteration j - 1, whose slot (j + 3) % 4 is refilled here
+        // Every iteration issues exactly four loads per wave (tiles past the end
+        // are zero fills of consumed slots), so at the top of iteration j the
+        // loads of tiles j+1 and j+2 are the ones in flight.
+        // With PERSIST and a next block, the 16 loads copying its Q are issued
+        // after S(0) (below), behind this block's tiles 1 and 2 and the previous
+        // block's O stores: tiles 1 and 2 are then followed by at least 20
+        // memory operations, and iterations 0 and 1 wait with vmcnt(20), so the
+        // copy and the stores are not waited for there.
+        auto enter = [&](int j) __attribute__((always_inline)) {
+            if (PERSIST && has_next && j < 2)
+                __builtin_amdgcn_s_waitcnt(kWaitVm20);
+            else
+                __builtin_amdgcn_s_waitcnt(kWaitVm4);
+            tile_barrier();
+        };
+        auto idle = [&](auto S, int j) __attribute__((always_inline)) {
+            enter(j);
+            issue(kslot(Slot<decltype(S)::value + 3>{}), vslot(Slot<decltype(S)::value + 3>{}), j + AHEAD);
+        };
+
+        // Iteration j, laid out as 32 MFMA steps: steps 0-15 compute
+        // S(j+1) = K(j+1) Q^T, steps 16-31 add P~(j) V(j) to O~.  The vector
+        // work rides between them, software-pipelined so that no step waits on
+        // a result produced in the same step: the 32 exponential items of tile j
+        // go through three stages (fma, exp2, sum/convert) in consecutive steps,
+        // each bf16 P~ operand ready before its P~V step; then the maximum of
+        // tile j+1 as a shallow tree.  Operand reads run four or five steps
+        // ahead of their MFMA.  sched_barrier keeps the compiler from regrouping
+        // the steps.  With MASKED, the scores of tile j+1 are masked first.
+        auto body = [&](auto S, auto MASKED, int j) __attribute__((always_inline)) {
+            constexpr bool masked = decltype(MASKED)::value != 0;
+            enter(j);
+            const uint8_t *kb = kslot(Slot<decltype(S)::value + 1>{});
+            const uint8_t *vb = vslot(S);
+            uint8_t *kd = kslot(Slot<decltype(S)::value + 3>{});
+            uint8_t *vd = vslot(Slot<decltype(S)::value + 3>{});
+            const TileRsrc lr = masked ? tile_rsrc(j + AHEAD) : tile_rsrc_cur(j + AHEAD);
+            const f32x16 zero = {};
+            float e[2][16];
+            float rs[2][4];      // four partial row sums per block, set by their first item
+            bf16x8 pb[2][2];
+            f32x16 sn[2];
+            bf16x8 ka[8];
+            bf16x8 va[2][4];
+            float px[2][6];
+
+            // stage 0 (fma), 1 (exp2) or 2 (sum, and the bf16 operand after the
+            // eighth item of an operand) of the items of group G
+            auto stage = [&](auto STAGE, auto G) __attribute__((always_inline)) {
+                constexpr int stg = decltype(STAGE)::value, grp = decltype(G)::value - 1;
+                static_for<item_lo(grp), item_lo(grp + 1)>([&](auto N) __attribute__((always_inline)) {
+                    constexpr int n = decltype(N)::value, qb = item_qb(n), i = item_i(n);
+                    if constexpr (stg == 0) {
+                        e[qb][i] = fmaf(sacc[qb][i], scale_log2, -msub[qb]);
+                    } else if constexpr (stg == 1) {
+                        e[qb][i] = fast_exp2(e[qb][i]);
+                    } else {
+                        // items n < 4 and 8 <= n < 12 are the first to reach rs[qb][n & 3]
+                        // (starting from 0.0f would cost an add: 0 + x is not x for x = -0)
+                        if constexpr (n < 16 && !(n & 4))
+                            rs[qb][i & 3] = e[qb][i];
+                        else
+                            rs[qb][i & 3] += e[qb][i];
+                        if constexpr ((n & 7) == 7) {
+                            constexpr int hh = n >> 4;
+                            f32x8 f;
+#pragma unroll
+                            for (int k = 0; k < 8; ++k) f[k] = e[qb][8 * hh + k];
+                            pb[qb][hh] = __builtin_convertvector(f, bf16x8);
+                        }
+                    }
+                });
+            };
+            auto rk = [&](int ks) __attribute__((always_inline)) {
+                ka[ks] = *reinterpret_cast<const bf16x8 *>(kb + koff[ks]);
+            };
+            auto rv = [&](int hh, int dt) __attribute__((always_inline)) {
+                const uint8_t *base = vb + 16 * hh * ROWB + voff[dt];
+                const bf16x4 lo4 = lds_read_tr(base);
+                const bf16x4 hi4 = lds_read_tr(base + 8 * ROWB);
+                va[hh][dt] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+            };
+
+            rk(0);
+            rk(1);
+            stage(Slot<0>{}, Slot<0>{});          // fma of group -1
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<0, 32>([&](auto ST) __attribute__((always_inline)) {
+                constexpr int st = decltype(ST)::value;
+                if constexpr (st < 16) {
+                    constexpr int ks = st >> 1, qb = st & 1;
+                    sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[qb][ks], ks ? sn[qb] : zero, 0, 0, 0);
+                } else {
+                    constexpr int t = st - 16, hh = t >> 3, dt = (t >> 1) & 3, qb = t & 1;
+                    mfma_acc(oacc[qb][dt], va[hh][dt], pb[qb][hh]);
+                }
+                // this wave's loads of tile j+3, one every eight steps
+                if constexpr ((st & 7) == 3) load1(lr, kd, vd, st >> 3);
+                // K operand of step 2 ks is read at step 2 ks - 4
+                if constexpr (st < 12 && !(st & 1)) rk((st + 4) >> 1);
+                // V operand of step 16 + 8 hh + 2 dt is read five steps earlier
+                if constexpr (st >= 11 && st < 27 && (st & 1)) rv((st - 11) >> 3, ((st - 11) >> 1) & 3);
+                // exponential pipeline: fma of group st, exp2 of st-1, sum of st-2
+                // (Slot<g + 1> names group g)
+                if constexpr (st < kGroups) stage(Slot<0>{}, Slot<st + 1>{});
+                if constexpr (st <= kGroups) stage(Slot<1>{}, Slot<st>{});
+                if constexpr (st >= 1 && st <= kGroups + 1) stage(Slot<2>{}, Slot<st - 1>{});
+                // masked iterations: mask S(j+1) once its MFMAs are done
+                if constexpr (masked && st >= 17 && st < 25) {
+                    constexpr int qb = (st - 17) >> 2, r = (st - 17) & 3;
+                    const int qi = qw0 + 32 * qb + c;
+                    const int lim = (causal ? min(Lk - 1, qi) : Lk - 1) - (j + 1) * BK - 4 * g;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (8 * r + u > lim) sn[qb][4 * r + u] = kNegInf;
+                }
+                // maximum of tile j+1: five independent max3 per block, then two
+                if constexpr (st >= 25 && st < 30) {
+                    constexpr int k = st - 25;
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb)
+                        px[qb][k] = fmaxf(fmaxf(sn[qb][3 * k], sn[qb][3 * k + 1]), sn[qb][3 * k + 2]);
+                }
+                if constexpr (st == 30) {
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb) {
+                        px[qb][0] = fmaxf(fmaxf(px[qb][0], px[qb][1]), px[qb][2]);
+                        px[qb][3] = fmaxf(fmaxf(px[qb][3], px[qb][4]), sn[qb][15]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                l[qb] += (rs[qb][0] + rs[qb][1]) + (rs[qb][2] + rs[qb][3]);
+                sacc[qb] = sn[qb];
+            }
+            float th[2];    // this lane's half of the tile maximum
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                th[qb] = fmaxf(px[qb][0], px[qb][3]);
+                // past the last tile the scores are of stale LDS data: unused
+                if (masked && j + 1 >= wtiles) th[qb] = kNegInf;
+            }
+            update_ref(th);
+        };
+
+        // ---- prologue: tiles 0 .. AHEAD-1 in flight, S(0) and its maximum ----
+        // tiles 0..2 (zero fills past the end); iteration 0 fills slot 3
+        // (with PERSIST the tiles were loaded before the Q fragments were read:
+        // by the block start above, or by the last iterations of the previous
+        // block, whose final wait and barrier leave tile 0 resident)
+        if (!PERSIST) {
+            issue(k0, v0, 0);
+            issue(k1, v1, 1);
+            issue(k2, v2, 2);
+            __builtin_amdgcn_s_waitcnt(0);   // nothing in flight (Q included)
+            __syncthreads();
+        }
+        if (wtiles > 0) {
+            qk(k0, sacc);
+            if (wfirst_mask == 0) mask(sacc, 0);
+            float tm[2];
+            tile_max(sacc, tm);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                // nothing accumulated yet: take the tile maximum as reference
+                m[qb] = tm[qb];
+                mlim[qb] = tm[qb] + lazy_raw;
+                msub[qb] = (tm[qb] == kNegInf) ? 0.0f : tm[qb] * scale_log2;
+            }
+        }
+        if (has_next) {
+            // this wave's reads of qs are complete (its own rows only): copy the
+            // next block's Q over them
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            issue_q(nxt);
+        }
+
+        // ---- main loop (unrolled by the ring size), then the masked tail -----
+        // Control flow never joins two versions of the accumulators that both
+        // came out of MFMAs (the compiler would copy all 128 of them through
+        // VGPRs): the masked loop also runs in whole groups of four, and its
+        // iterations past wtiles only load and pass the barrier.  Every wave
+        // passes the same barriers.
+        int j = 0;
+        for (; j + 4 <= nfast; j += 4) {
+            body(Slot<0>{}, Slot<0>{}, j);
+            body(Slot<1>{}, Slot<0>{}, j + 1);
+            body(Slot<2>{}, Slot<0>{}, j + 2);
+            body(Slot<3>{}, Slot<0>{}, j + 3);
+        }
+        for (; j < wend; j += 4) {
+            body(Slot<0>{}, Slot<1>{}, j);
+            if (j + 1 < wtiles) body(Slot<1>{}, Slot<1>{}, j + 1); else idle(Slot<1>{}, j + 1);
+            if (j + 2 < wtiles) body(Slot<2>{}, Slot<1>{}, j + 2); else idle(Slot<2>{}, j + 2);
+            if (j + 3 < wtiles) body(Slot<3>{}, Slot<1>{}, j + 3); else idle(Slot<3>{}, j + 3);
+        }
+        // this wave is done; keep loading and passing barriers with the others
+        for (; j < nend; j += 4) {
+            idle(Slot<0>{}, j);
+            idle(Slot<1>{}, j + 1);
+            idle(Slot<2>{}, j + 2);
+            idle(Slot<3>{}, j + 3);
+        }
+        // no load outlives the last block (the next block's tiles 1 and 2 stay
+        // in flight otherwise)
+        if (!has_next) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+
+        // ---- epilogue: O = O~ / l once, LSE = m + log l ------------------------
+        acc_settle(oacc);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int qi = qw0 + 32 * qb + c;
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l[qb]), __float_as_uint(l[qb]), false, false);
+            const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            const bool valid = (qi < Lq) && (lt > 0.0f);
+            const float inv = valid ? 1.0f / lt : 0.0f;
+            if (qi < Nq) {
+                uint16_t *orow = O + (qhead + qi) * D;
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[qb][dt][i] *= alpha;
-                m[qb] = mn;
-                mlim[qb] = mn + lazy_raw;
-                msub[qb] = (mn == kNegInf) ? 0.0f : mn * scale_log2;
-            }
-        }
-    };
-
-    // slot buffers by (compile-time) index
-    auto kslot = [&](auto S) __attribute__((always_inline)) -> uint8_t * {
-        constexpr int s = decltype(S)::value & 3;
-        return s == 0 ? k0 : s == 1 ? k1 : s == 2 ? k2 : k3;
-    };
-    auto vslot = [&](auto S) __attribute__((always_inline)) -> uint8_t * {
-        constexpr int s = decltype(S)::value & 3;
-        return s == 0 ? v0 : s == 1 ? v1 : s == 2 ? v2 : v3;
-    };
-
-    // top of iteration j: tile j + 1 resident for every wave, and every wave
-    // done with iteration j - 1, whose slot (j + 3) % 4 is refilled here
-    // Every iteration issues exactly four loads per wave (tiles past the end
-    // are zero fills of consumed slots), so at the top of iteration j the
-    // loads of tiles j+1 and j+2 are the ones in flight.
-    // With PERSIST and a next block, the 16 loads copying its Q are issued
-    // after S(0) (below), behind this block's tiles 1 and 2 and the previous
-    // block's O stores: tiles 1 and 2 are then followed by at least 20
-    // memory operations, and iterations 0 and 1 wait with vmcnt(20), so the
-    // copy and the stores are not waited for there.
-    auto enter = [&](int j) __attribute__((always_inline)) {
-        if (PERSIST && has_next && j < 2)
-            __builtin_amdgcn_s_waitcnt(kWaitVm20);
-        else
-            __builtin_amdgcn_s_waitcnt(kWaitVm4);
-        tile_barrier();
-    };
-    auto idle = [&](auto S, int j) __attribute__((always_inline)) {
-        enter(j);
-        issue(kslot(Slot<decltype(S)::value + 3>{}), vslot(Slot<decltype(S)::value + 3>{}), j + AHEAD);
-    };
-
-    // Iteration j, laid out as 32 MFMA steps: steps 0-15 compute
-    // S(j+1) = K(j+1) Q^T, steps 16-31 add P~(j) V(j) to O~.  The vector
-    // work rides between them, software-pipelined so that no step waits on
-    // a result produced in the same step: the 32 exponential items of tile j
-    // go through three stages (fma, exp2, sum/convert) in consecutive steps,
-    // each bf16 P~ operand ready before its P~V step; then the maximum of
-    // tile j+1 as a shallow tree.  Operand reads run four or five steps
-    // ahead of their MFMA.  sched_barrier keeps the compiler from regrouping
-    // the steps.  With MASKED, the scores of tile j+1 are masked first.
-    auto body = [&](auto S, auto MASKED, int j) __attribute__((always_inline)) {
-        constexpr bool masked = decltype(MASKED)::value != 0;
-        enter(j);
-        const uint8_t *kb = kslot(Slot<decltype(S)::value + 1>{});
-        const uint8_t *vb = vslot(S);
-        uint8_t *kd = kslot(Slot<decltype(S)::value + 3>{});
-        uint8_t *vd = vslot(Slot<decltype(S)::value + 3>{});
-        const TileRsrc lr = masked ? tile_rsrc(j + AHEAD) : tile_rsrc_cur(j + AHEAD);
-        const f32x16 zero = {};
-        float e[2][16];
-        float rs[2][4];      // four partial row sums per block, set by their first item
-        bf16x8 pb[2][2];
-        f32x16 sn[2];
-        bf16x8 ka[8];
-        bf16x8 va[2][4];
-        float px[2][6];
-
-        // stage 0 (fma), 1 (exp2) or 2 (sum, and the bf16 operand after the
-        // eighth item of an operand) of the items of group G
-        auto stage = [&](auto STAGE, auto G) __attribute__((always_inline)) {
-            constexpr int stg = decltype(STAGE)::value, grp = decltype(G)::value - 1;
-            static_for<item_lo(grp), item_lo(grp + 1)>([&](auto N) __attribute__((always_inline)) {
-                constexpr int n = decltype(N)::value, qb = item_qb(n), i = item_i(n);
-                if constexpr (stg == 0) {
-                    e[qb][i] = fmaf(sacc[qb][i], scale_log2, -msub[qb]);
-                } else if constexpr (stg == 1) {
-                    e[qb][i] = fast_exp2(e[qb][i]);
-                } else {
-                    // items n < 4 and 8 <= n < 12 are the first to reach rs[qb][n & 3]
-                    // (starting from 0.0f would cost an add: 0 + x is not x for x = -0)
-                    if constexpr (n < 16 && !(n & 4))
-                        rs[qb][i & 3] = e[qb][i];
-                    else
-                        rs[qb][i & 3] += e[qb][i];
-                    if constexpr ((n & 7) == 7) {
-                        constexpr int hh = n >> 4;
-                        f32x8 f;
-#pragma unroll
-                        for (int k = 0; k < 8; ++k) f[k] = e[qb][8 * hh + k];
-                        pb[qb][hh] = __builtin_convertvector(f, bf16x8);
+                    for (int r = 0; r < 4; ++r) {
+                        uint2 w;
+                        w.x = valid ? pack_bf16x2_hw(oacc[qb][dt][4 * r + 0] * inv, oacc[qb][dt][4 * r + 1] * inv) : 0u;
+                        w.y = valid ? pack_bf16x2_hw(oacc[qb][dt][4 * r + 2] * inv, oacc[qb][dt][4 * r + 3] * inv) : 0u;
+                        *reinterpret_cast<uint2 *>(orow + 32 * dt + 8 * r + 4 * g) = w;
                     }
-                }
-            });
-        };
-        auto rk = [&](int ks) __attribute__((always_inline)) {
-            ka[ks] = *reinterpret_cast<const bf16x8 *>(kb + koff[ks]);
-        };
-        auto rv = [&](int hh, int dt) __attribute__((always_inline)) {
-            const uint8_t *base = vb + 16 * hh * ROWB + voff[dt];
-            const bf16x4 lo4 = lds_read_tr(base);
-            const bf16x4 hi4 = lds_read_tr(base + 8 * ROWB);
-            va[hh][dt] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-        };
-
-        rk(0);
-        rk(1);
-        stage(Slot<0>{}, Slot<0>{});          // fma of group -1
-        __builtin_amdgcn_sched_barrier(0);
-        static_for<0, 32>([&](auto ST) __attribute__((always_inline)) {
-            constexpr int st = decltype(ST)::value;
-            if constexpr (st < 16) {
-                constexpr int ks = st >> 1, qb = st & 1;
-                sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[qb][ks], ks ? sn[qb] : zero, 0, 0, 0);
-            } else {
-                constexpr int t = st - 16, hh = t >> 3, dt = (t >> 1) & 3, qb = t & 1;
-                mfma_acc(oacc[qb][dt], va[hh][dt], pb[qb][hh]);
+                if (LSE && g == 0)
+                    LSE[qhead + qi] = valid ? (m[qb] * scale_log2 + __log2f(lt)) * kLn2 : kNegInf;
             }
-            // this wave's loads of tile j+3, one every eight steps
-            if constexpr ((st & 7) == 3) load1(lr, kd, vd, st >> 3);
-            // K operand of step 2 ks is read at step 2 ks - 4
-            if constexpr (st < 12 && !(st & 1)) rk((st + 4) >> 1);
-            // V operand of step 16 + 8 hh + 2 dt is read five steps earlier
-            if constexpr (st >= 11 && st < 27 && (st & 1)) rv((st - 11) >> 3, ((st - 11) >> 1) & 3);
-            // exponential pipeline: fma of group st, exp2 of st-1, sum of st-2
-            // (Slot<g + 1> names group g)
-            if constexpr (st < kGroups) stage(Slot<0>{}, Slot<st + 1>{});
-            if constexpr (st <= kGroups) stage(Slot<1>{}, Slot<st>{});
-            if constexpr (st >= 1 && st <= kGroups + 1) stage(Slot<2>{}, Slot<st - 1>{});
-            // masked iterations: mask S(j+1) once its MFMAs are done
-            if constexpr (masked && st >= 17 && st < 25) {
-                constexpr int qb = (st - 17) >> 2, r = (st - 17) & 3;
-                const int qi = qw0 + 32 * qb + c;
-                const int lim = (causal ? min(Lk - 1, qi) : Lk - 1) - (j + 1) * BK - 4 * g;
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    if (8 * r + u > lim) sn[qb][4 * r + u] = kNegInf;
-            }
-            // maximum of tile j+1: five independent max3 per block, then two
-            if constexpr (st >= 25 && st < 30) {
-                constexpr int k = st - 25;
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-                    px[qb][k] = fmaxf(fmaxf(sn[qb][3 * k], sn[qb][3 * k + 1]), sn[qb][3 * k + 2]);
-            }
-            if constexpr (st == 30) {
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    px[qb][0] = fmaxf(fmaxf(px[qb][0], px[qb][1]), px[qb][2]);
-                    px[qb][3] = fmaxf(fmaxf(px[qb][3], px[qb][4]), sn[qb][15]);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        });
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            l[qb] += (rs[qb][0] + rs[qb][1]) + (rs[qb][2] + rs[qb][3]);
-            sacc[qb] = sn[qb];
         }
-        float th[2];    // this lane's half of the tile maximum
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            th[qb] = fmaxf(px[qb][0], px[qb][3]);
-            // past the last tile the scores are of stale LDS data: unused
-            if (masked && j + 1 >= wtiles) th[qb] = kNegInf;
-        }
-        update_ref(th);
-    };
-
-    // ---- prologue: tiles 0 .. AHEAD-1 in flight, S(0) and its maximum ----
-    // tiles 0..2 (zero fills past the end); iteration 0 fills slot 3
-    // (with PERSIST the tiles were loaded before the Q fragments were read:
-    // by the block start above, or by the last iterations of the previous
-    // block, whose final wait and barrier leave tile 0 resident)
-    if (!PERSIST) {
-        issue(k0, v0, 0);
-        issue(k1, v1, 1);
-        issue(k2, v2, 2);
-        __builtin_amdgcn_s_waitcnt(0);   // nothing in flight (Q included)
-        __syncthreads();
-    }
-    if (wtiles > 0) {
-        qk(k0, sacc);
-        if (wfirst_mask == 0) mask(sacc, 0);
-        float tm[2];
-        tile_max(sacc, tm);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            // nothing accumulated yet: take the tile maximum as reference
-            m[qb] = tm[qb];
-            mlim[qb] = tm[qb] + lazy_raw;
-            msub[qb] = (tm[qb] == kNegInf) ? 0.0f : tm[qb] * scale_log2;
-        }
-    }
-    if (has_next) {
-        // this wave's reads of qs are complete (its own rows only): copy the
-        // next block's Q over them
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        issue_q(nxt);
-    }
-
-    // ---- main loop (unrolled by the ring size), then the masked tail -----
-    // Control flow never joins two versions of the accumulators that both
-    // came out of MFMAs (the compiler would copy all 128 of them through
-    // VGPRs): the masked loop also runs in whole groups of four, and its
-    // iterations past wtiles only load and pass the barrier.  Every wave
-    // passes the same barriers.
-    int j = 0;
-    for (; j + 4 <= nfast; j += 4) {
-        body(Slot<0>{}, Slot<0>{}, j);
-        body(Slot<1>{}, Slot<0>{}, j + 1);
-        body(Slot<2>{}, Slot<0>{}, j + 2);
-        body(Slot<3>{}, Slot<0>{}, j + 3);
-    }
-    for (; j < wend; j += 4) {
-        body(Slot<0>{}, Slot<1>{}, j);
-        if (j + 1 < wtiles) body(Slot<1>{}, Slot<1>{}, j + 1); else idle(Slot<1>{}, j + 1);
-        if (j + 2 < wtiles) body(Slot<2>{}, Slot<1>{}, j + 2); else idle(Slot<2>{}, j + 2);
-        if (j + 3 < wtiles) body(Slot<3>{}, Slot<1>{}, j + 3); else idle(Slot<3>{}, j + 3);
-    }
-    // this wave is done; keep loading and passing barriers with the others
-    for (; j < nend; j += 4) {
-        idle(Slot<0>{}, j);
-        idle(Slot<1>{}, j + 1);
-        idle(Slot<2>{}, j + 2);
-        idle(Slot<3>{}, j + 3);
-    }
-    // no load outlives the last block (the next block's tiles 1 and 2 stay
-    // in flight otherwise)
-    if (!has_next) __builtin_amdgcn_s_waitcnt(kWaitVm0);
-
-    // ---- epilogue: O = O~ / l once, LSE = m + log l ------------------------
-    acc_settle(oacc);
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int qi = qw0 + 32 * qb + c;
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l[qb]), __float_as_uint(l[qb]), false, false);
-        const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        const bool valid = (qi < Lq) && (lt > 0.0f);
-        const float inv = valid ? 1.0f / lt : 0.0f;
-        if (qi < Nq) {
-            uint16_t *orow = O + (qhead + qi) * D;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    uint2 w;
-                    w.x = valid ? pack_bf16x2_hw(oacc[qb][dt][4 * r + 0] * inv, oacc[qb][dt][4 * r + 1] * inv) : 0u;
-                    w.y = valid ? pack_bf16x2_hw(oacc[qb][dt][4 * r + 2] * inv, oacc[qb][dt][4 * r + 3] * inv) : 0u;
-                    *reinterpret_cast<uint2 *>(orow + 32 * dt + 8 * r + 4 * g) = w;
-                }
-            if (LSE && g == 0)
-                LSE[qhead + qi] = valid ? (m[qb] * scale_log2 + __log2f(lt)) * kLn2 : kNegInf;
-        }
-    }
-    if (!has_next) break;
-    L = Lnext;
-    first = false;
+        if (!has_next) break;
+        L = Lnext;
+        first = false;
     }   // blocks
 }
 

@@ -175,399 +175,399 @@ attn_fp8_body(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
     int L = blockIdx.x;
     bool first = true;
     for (;;) {
-    const Blk cur = decode(L);
-    const int Lnext = L + (int)gridDim.x;
-    const bool has_next = PERSIST && rfl(Lnext < nblocks ? 1 : 0) != 0;
-    const Blk nxt = decode(has_next ? Lnext : L);
-    const int b = cur.b, h = cur.h, kvh = cur.kvh, q0 = cur.q0;
-    const int Lq = rfl(seqlens_q ? clampi(seqlens_q[b], 0, Nq) : Nq);
-    const int Lk = rfl(seqlens_k ? clampi(seqlens_k[b], 0, Nk) : Nk);
+        const Blk cur = decode(L);
+        const int Lnext = L + (int)gridDim.x;
+        const bool has_next = PERSIST && rfl(Lnext < nblocks ? 1 : 0) != 0;
+        const Blk nxt = decode(has_next ? Lnext : L);
+        const int b = cur.b, h = cur.h, kvh = cur.kvh, q0 = cur.q0;
+        const int Lq = rfl(seqlens_q ? clampi(seqlens_q[b], 0, Nq) : Nq);
+        const int Lk = rfl(seqlens_k ? clampi(seqlens_k[b], 0, Nk) : Nk);
 
-    const int qw0 = q0 + QW * wave;             // queries qw0 + 32 qb + c
-    const size_t qrow0 = (size_t)(b * Hq + h) * Nq;
-    const uint8_t *Kh = K + (size_t)(b * Hkv + kvh) * Nk * D;
-    const uint8_t *Vh = V + (size_t)(b * Hkv + kvh) * Nk * D;
+        const int qw0 = q0 + QW * wave;             // queries qw0 + 32 qb + c
+        const size_t qrow0 = (size_t)(b * Hq + h) * Nq;
+        const uint8_t *Kh = K + (size_t)(b * Hkv + kvh) * Nk * D;
+        const uint8_t *Vh = V + (size_t)(b * Hkv + kvh) * Nk * D;
 
-    if (!PERSIST && q0 >= Lq) {
-        const int rows = min(BQ, Nq - q0);
-        for (int i = tid; i < rows * (D / 8); i += NT)
-            *reinterpret_cast<uint4 *>(O + (qrow0 + q0 + i / (D / 8)) * D + (i % (D / 8)) * 8) =
-                make_uint4(0, 0, 0, 0);
-        if (LSE)
-            for (int r = tid; r < rows; r += NT) LSE[qrow0 + q0 + r] = kNegInf;
-        return;
-    }
+        if (!PERSIST && q0 >= Lq) {
+            const int rows = min(BQ, Nq - q0);
+            for (int i = tid; i < rows * (D / 8); i += NT)
+                *reinterpret_cast<uint4 *>(O + (qrow0 + q0 + i / (D / 8)) * D + (i % (D / 8)) * 8) =
+                    make_uint4(0, 0, 0, 0);
+            if (LSE)
+                for (int r = tid; r < rows; r += NT) LSE[qrow0 + q0 + r] = kNegInf;
+            return;
+        }
 
-    int kend = Lk;
-    if (causal) kend = min(kend, min(q0 + BQ, Lq));
-    const int ntiles = (kend + BK - 1) / BK;
-    int wtiles = (qw0 >= Lq) ? 0 : ntiles;
-    if (causal) wtiles = min(wtiles, (qw0 + QW - 1) / BK + 1);
-    int wmask = wtiles;                           // first tile that needs a mask
-    if (causal) wmask = min(wmask, qw0 / BK);
-    if (Lk % BK) wmask = min(wmask, Lk / BK);
-    const int nend = ((ntiles + 3) / 4) * 4;
+        int kend = Lk;
+        if (causal) kend = min(kend, min(q0 + BQ, Lq));
+        const int ntiles = (kend + BK - 1) / BK;
+        int wtiles = (qw0 >= Lq) ? 0 : ntiles;
+        if (causal) wtiles = min(wtiles, (qw0 + QW - 1) / BK + 1);
+        int wmask = wtiles;                           // first tile that needs a mask
+        if (causal) wmask = min(wmask, qw0 / BK);
+        if (Lk % BK) wmask = min(wmask, Lk / BK);
+        const int nend = ((ntiles + 3) / 4) * 4;
 
-    const int unit_scale = kUnitScale;
-    f32x16 oacc[NQB][4];
-    {
-        const i32x8 z8 = {};
+        const int unit_scale = kUnitScale;
+        f32x16 oacc[NQB][4];
+        {
+            const i32x8 z8 = {};
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
+            for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) acc_zero8(oacc[qb][dt], z8, unit_scale);
-    }
-    // The reference only moves when a tile's maximum exceeds it by more than
-    // 2^8 in weight, so every P~ is at most 2^8 (E4M3 holds up to 448).
-    constexpr float kLazy = 8.0f;
-    const float lazy_raw = kLazy / scale_log2;
-    float m[NQB], mlim[NQB], msub[NQB], l[NQB];
+                for (int dt = 0; dt < 4; ++dt) acc_zero8(oacc[qb][dt], z8, unit_scale);
+        }
+        // The reference only moves when a tile's maximum exceeds it by more than
+        // 2^8 in weight, so every P~ is at most 2^8 (E4M3 holds up to 448).
+        constexpr float kLazy = 8.0f;
+        const float lazy_raw = kLazy / scale_log2;
+        float m[NQB], mlim[NQB], msub[NQB], l[NQB];
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-        m[qb] = kNegInf;     // reference maximum of raw scores q.k
-        mlim[qb] = kNegInf;  // m + lazy_raw: tile maxima up to it keep the reference
-        msub[qb] = 0.0f;     // m * scale * log2(e) (0 while m = -inf)
-        l[qb] = 0.0f;        // this lane's part of the running sum
-    }
+        for (int qb = 0; qb < NQB; ++qb) {
+            m[qb] = kNegInf;     // reference maximum of raw scores q.k
+            mlim[qb] = kNegInf;  // m + lazy_raw: tile maxima up to it keep the reference
+            msub[qb] = 0.0f;     // m * scale * log2(e) (0 while m = -inf)
+            l[qb] = 0.0f;        // this lane's part of the running sum
+        }
 
-    // ---- tile DMA: load i of wave w fills LDS block LPW w + i (8 rows);
-    // lane l row 8 blk + l/8, slot l%8, holding global chunk slot ^ swz8(row)
-    uint32_t dmo[LPW];
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-        const int row = 8 * (LPW * wave + i) + (lane >> 3);
-        dmo[i] = row * ROWB + (((lane & 7) ^ swz8(row)) << 4);
-    }
-    // loads of tile j0 / BK from K and V rows kb, vb of length len into slots kd, vd
-    auto issue_at = [&](uint8_t *kd, uint8_t *vd, const uint8_t *kb, const uint8_t *vb, int j0, int len)
-        __attribute__((always_inline)) {
-        const int bytes = max(0, len - j0) * ROWB;   // < 2^31: the ABI bounds Nk * 128
-        const __amdgpu_buffer_rsrc_t rk =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(kb) + (size_t)j0 * D, 0, bytes, kRsrcWord3);
-        const __amdgpu_buffer_rsrc_t rv =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(vb) + (size_t)j0 * D, 0, bytes, kRsrcWord3);
+        // ---- tile DMA: load i of wave w fills LDS block LPW w + i (8 rows);
+        // lane l row 8 blk + l/8, slot l%8, holding global chunk slot ^ swz8(row)
+        uint32_t dmo[LPW];
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (void __attribute__((address_space(3))) *)(kd + (LPW * wave + i) * 1024),
-                                                     16, dmo[i], 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (void __attribute__((address_space(3))) *)(vd + (LPW * wave + i) * 1024),
-                                                     16, dmo[i], 0, 0, 0);
+            const int row = 8 * (LPW * wave + i) + (lane >> 3);
+            dmo[i] = row * ROWB + (((lane & 7) ^ swz8(row)) << 4);
         }
-    };
-    // tile t of this block
-    auto issue = [&](uint8_t *kd, uint8_t *vd, int t) __attribute__((always_inline)) {
-        issue_at(kd, vd, Kh, Vh, t * BK, Lk);
-    };
-    // tile t of the ring in the last group of four iterations: with PERSIST,
-    // tile nend + i (past this block's padded end, where the ring would load
-    // zeros) is tile i of the next block, if there is one.  The selects are
-    // uniform, but the compiler evaluates them on the vector ALU; rfl keeps
-    // the resources in scalar registers (else every load loops over lanes).
-    const uint8_t *Kn = K + (size_t)(nxt.b * Hkv + nxt.kvh) * Nk * D;
-    const uint8_t *Vn = V + (size_t)(nxt.b * Hkv + nxt.kvh) * Nk * D;
-    auto issue_last = [&](uint8_t *kd, uint8_t *vd, int t) __attribute__((always_inline)) {
-        if constexpr (!PERSIST) {
-            issue(kd, vd, t);
-        } else {
-            const bool next = t >= nend;
-            issue_at(kd, vd, uniform_ptr(next ? Kn : Kh), uniform_ptr(next ? Vn : Vh),
-                     rfl((next ? t - nend : t) * BK), rfl((next && !has_next) ? 0 : Lk));
-        }
-    };
-    // Q rows q0 .. q0 + BQ - 1 of block n into qs (PERSIST): wave w copies its
-    // own 32 rows, 4 loads of 1 KiB laid out like a tile's; rows at or past
-    // Nq read as zeros
-    auto issue_q = [&](const Blk &n) __attribute__((always_inline)) {
-        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint8_t *>(Q) + ((size_t)(n.b * Hq + n.h) * Nq + n.q0) * D, 0,
-            max(0, Nq - n.q0) * ROWB, kRsrcWord3);
+        // loads of tile j0 / BK from K and V rows kb, vb of length len into slots kd, vd
+        auto issue_at = [&](uint8_t *kd, uint8_t *vd, const uint8_t *kb, const uint8_t *vb, int j0, int len)
+            __attribute__((always_inline)) {
+            const int bytes = max(0, len - j0) * ROWB;   // < 2^31: the ABI bounds Nk * 128
+            const __amdgpu_buffer_rsrc_t rk =
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(kb) + (size_t)j0 * D, 0, bytes, kRsrcWord3);
+            const __amdgpu_buffer_rsrc_t rv =
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(vb) + (size_t)j0 * D, 0, bytes, kRsrcWord3);
 #pragma unroll
-        for (int i = 0; i < QW * ROWB / 1024; ++i) {
-            const int blk = (QW * ROWB / 1024) * wave + i, row = 8 * blk + (lane >> 3);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3))) *)(qs + blk * 1024), 16,
-                                                     row * ROWB + (((lane & 7) ^ swz8(row)) << 4), 0, 0, 0);
-        }
-    };
-    if (PERSIST && first) {
-        issue_q(cur);
-        issue(k0, v0, 0);
-        issue(k1, v1, 1);
-        issue(k2, v2, 2);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    }
-
-    // ---- Q (B operands of S^T = K Q^T): lane (g, c) holds row qw0 + 32 qb + c,
-    // bytes 64 ks + 32 g .. + 31; rows at or past Lq are zero
-    i32x8 qf[NQB][2];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-        const int qi = qw0 + 32 * qb + c;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-            if constexpr (PERSIST) {
-                // this wave's rows of qs: row 32 wave + 32 qb + c, chunks 4 ks + 2 g, + 1
-                const int row = QW * wave + 32 * qb + c, ch = 4 * ks + 2 * g;
-                lo = *reinterpret_cast<const uint4 *>(qs + row * ROWB + ((ch ^ swz8(row)) << 4));
-                hi = *reinterpret_cast<const uint4 *>(qs + row * ROWB + (((ch + 1) ^ swz8(row)) << 4));
-            } else if (qi < Lq) {
-                const uint4 *src = reinterpret_cast<const uint4 *>(Q + (qrow0 + qi) * D + 64 * ks + 32 * g);
-                lo = src[0];
-                hi = src[1];
+            for (int i = 0; i < LPW; ++i) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rk, (void __attribute__((address_space(3))) *)(kd + (LPW * wave + i) * 1024), 16, dmo[i], 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rv, (void __attribute__((address_space(3))) *)(vd + (LPW * wave + i) * 1024), 16, dmo[i], 0, 0, 0);
             }
-            qf[qb][ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
-    }
-
-    // K operand (rows of a 32-key block, permuted): lane (g, c) with
-    // c = 8 r + 4 hh + u reads key row 16 hh + 4 r + u, chunks 4 ks + 2 g and + 1;
-    // the second 32-key block is the same offsets + 32 rows
-    uint32_t koff[2][2];
-    {
-        const int row = 16 * ((c >> 2) & 1) + 4 * (c >> 3) + (c & 3);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) koff[ks][hf] = row * ROWB + (((4 * ks + 2 * g + hf) ^ swz8(row)) << 4);
-    }
-    // V^T operand (dim rows 32 dt + c): bytes 8 e .. 8 e + 7 of lane half g are
-    // keys 32 (e/2) + 16 g + 8 (e%2) + 0..7.  16-lane group t = lane/16,
-    // index i = lane%16 points at key row 16 (t/2) + i/2 (+ 8 (e%2) + 32 (e/2),
-    // which leave the swizzle unchanged), dims 32 dt + 16 (t%2) + 8 (i%2)
-    uint32_t voff[4];
-    {
-        const int t = lane >> 4, i = lane & 15;
-        const int row = 16 * (t >> 1) + (i >> 1);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) voff[dt] = row * ROWB + (((2 * dt + (t & 1)) ^ swz8(row)) << 4) + 8 * (i & 1);
-    }
-
-    // S^T of one tile: s[kb][qb] element 4 r + u of lane (g, c) is key
-    // 32 kb + 16 g + 4 r + u of the tile, query qw0 + 32 qb + c
-    auto qk = [&](const uint8_t *kb, f32x16 (&s)[2][NQB]) __attribute__((always_inline)) {
-        const f32x16 zero = {};
-#pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const uint4 lo = *reinterpret_cast<const uint4 *>(kb + 32 * kbk * ROWB + koff[ks][0]);
-                const uint4 hi = *reinterpret_cast<const uint4 *>(kb + 32 * kbk * ROWB + koff[ks][1]);
-                const i32x8 a = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-#pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) s[kbk][qb] = mfma8(a, qf[qb][ks], ks ? s[kbk][qb] : zero);
+        };
+        // tile t of this block
+        auto issue = [&](uint8_t *kd, uint8_t *vd, int t) __attribute__((always_inline)) {
+            issue_at(kd, vd, Kh, Vh, t * BK, Lk);
+        };
+        // tile t of the ring in the last group of four iterations: with PERSIST,
+        // tile nend + i (past this block's padded end, where the ring would load
+        // zeros) is tile i of the next block, if there is one.  The selects are
+        // uniform, but the compiler evaluates them on the vector ALU; rfl keeps
+        // the resources in scalar registers (else every load loops over lanes).
+        const uint8_t *Kn = K + (size_t)(nxt.b * Hkv + nxt.kvh) * Nk * D;
+        const uint8_t *Vn = V + (size_t)(nxt.b * Hkv + nxt.kvh) * Nk * D;
+        auto issue_last = [&](uint8_t *kd, uint8_t *vd, int t) __attribute__((always_inline)) {
+            if constexpr (!PERSIST) {
+                issue(kd, vd, t);
+            } else {
+                const bool next = t >= nend;
+                issue_at(kd, vd, uniform_ptr(next ? Kn : Kh), uniform_ptr(next ? Vn : Vh),
+                         rfl((next ? t - nend : t) * BK), rfl((next && !has_next) ? 0 : Lk));
             }
-    };
+        };
+        // Q rows q0 .. q0 + BQ - 1 of block n into qs (PERSIST): wave w copies its
+        // own 32 rows, 4 loads of 1 KiB laid out like a tile's; rows at or past
+        // Nq read as zeros
+        auto issue_q = [&](const Blk &n) __attribute__((always_inline)) {
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t *>(Q) + ((size_t)(n.b * Hq + n.h) * Nq + n.q0) * D, 0,
+                max(0, Nq - n.q0) * ROWB, kRsrcWord3);
+#pragma unroll
+            for (int i = 0; i < QW * ROWB / 1024; ++i) {
+                const int blk = (QW * ROWB / 1024) * wave + i, row = 8 * blk + (lane >> 3);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3))) *)(qs + blk * 1024), 16,
+                                                         row * ROWB + (((lane & 7) ^ swz8(row)) << 4), 0, 0, 0);
+            }
+        };
+        if (PERSIST && first) {
+            issue_q(cur);
+            issue(k0, v0, 0);
+            issue(k1, v1, 1);
+            issue(k2, v2, 2);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
 
-    auto mask = [&](f32x16 (&s)[2][NQB], int t) __attribute__((always_inline)) {
+        // ---- Q (B operands of S^T = K Q^T): lane (g, c) holds row qw0 + 32 qb + c,
+        // bytes 64 ks + 32 g .. + 31; rows at or past Lq are zero
+        i32x8 qf[NQB][2];
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
             const int qi = qw0 + 32 * qb + c;
-            const int lim = (causal ? min(Lk - 1, qi) : Lk - 1) - t * BK - 16 * g;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+                if constexpr (PERSIST) {
+                    // this wave's rows of qs: row 32 wave + 32 qb + c, chunks 4 ks + 2 g, + 1
+                    const int row = QW * wave + 32 * qb + c, ch = 4 * ks + 2 * g;
+                    lo = *reinterpret_cast<const uint4 *>(qs + row * ROWB + ((ch ^ swz8(row)) << 4));
+                    hi = *reinterpret_cast<const uint4 *>(qs + row * ROWB + (((ch + 1) ^ swz8(row)) << 4));
+                } else if (qi < Lq) {
+                    const uint4 *src = reinterpret_cast<const uint4 *>(Q + (qrow0 + qi) * D + 64 * ks + 32 * g);
+                    lo = src[0];
+                    hi = src[1];
+                }
+                qf[qb][ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
+        }
+
+        // K operand (rows of a 32-key block, permuted): lane (g, c) with
+        // c = 8 r + 4 hh + u reads key row 16 hh + 4 r + u, chunks 4 ks + 2 g and + 1;
+        // the second 32-key block is the same offsets + 32 rows
+        uint32_t koff[2][2];
+        {
+            const int row = 16 * ((c >> 2) & 1) + 4 * (c >> 3) + (c & 3);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) koff[ks][hf] = row * ROWB + (((4 * ks + 2 * g + hf) ^ swz8(row)) << 4);
+        }
+        // V^T operand (dim rows 32 dt + c): bytes 8 e .. 8 e + 7 of lane half g are
+        // keys 32 (e/2) + 16 g + 8 (e%2) + 0..7.  16-lane group t = lane/16,
+        // index i = lane%16 points at key row 16 (t/2) + i/2 (+ 8 (e%2) + 32 (e/2),
+        // which leave the swizzle unchanged), dims 32 dt + 16 (t%2) + 8 (i%2)
+        uint32_t voff[4];
+        {
+            const int t = lane >> 4, i = lane & 15;
+            const int row = 16 * (t >> 1) + (i >> 1);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) voff[dt] = row * ROWB + (((2 * dt + (t & 1)) ^ swz8(row)) << 4) + 8 * (i & 1);
+        }
+
+        // S^T of one tile: s[kb][qb] element 4 r + u of lane (g, c) is key
+        // 32 kb + 16 g + 4 r + u of the tile, query qw0 + 32 qb + c
+        auto qk = [&](const uint8_t *kb, f32x16 (&s)[2][NQB]) __attribute__((always_inline)) {
+            const f32x16 zero = {};
 #pragma unroll
             for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (32 * kbk + i > lim) s[kbk][qb][i] = kNegInf;
-        }
-    };
+                for (int ks = 0; ks < 2; ++ks) {
+                    const uint4 lo = *reinterpret_cast<const uint4 *>(kb + 32 * kbk * ROWB + koff[ks][0]);
+                    const uint4 hi = *reinterpret_cast<const uint4 *>(kb + 32 * kbk * ROWB + koff[ks][1]);
+                    const i32x8 a = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb) s[kbk][qb] = mfma8(a, qf[qb][ks], ks ? s[kbk][qb] : zero);
+                }
+        };
 
-    // iteration body for tile t whose scores are in s: mask, lazy reference,
-    // then (one scheduling region) the scores of tile t + 1 into sn, the
-    // exponentials of tile t, and O~ += P~(t) V(t)
-    // mask (when tile t needs it) and tile maximum of scores s of tile t
-    auto tmax = [&](f32x16 (&s)[2][NQB], int t, float (&tm)[NQB]) __attribute__((always_inline)) {
-        if (t >= wmask) mask(s, t);
+        auto mask = [&](f32x16 (&s)[2][NQB], int t) __attribute__((always_inline)) {
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
+                const int qi = qw0 + 32 * qb + c;
+                const int lim = (causal ? min(Lk - 1, qi) : Lk - 1) - t * BK - 16 * g;
+#pragma unroll
+                for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (32 * kbk + i > lim) s[kbk][qb][i] = kNegInf;
+            }
+        };
+
+        // iteration body for tile t whose scores are in s: mask, lazy reference,
+        // then (one scheduling region) the scores of tile t + 1 into sn, the
+        // exponentials of tile t, and O~ += P~(t) V(t)
+        // mask (when tile t needs it) and tile maximum of scores s of tile t
+        auto tmax = [&](f32x16 (&s)[2][NQB], int t, float (&tm)[NQB]) __attribute__((always_inline)) {
+            if (t >= wmask) mask(s, t);
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
+                float x = fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), s[1][qb][0]);
+                x = fmaxf(x, s[1][qb][1]);
+#pragma unroll
+                for (int i = 2; i < 16; ++i) x = fmaxf(fmaxf(x, s[0][qb][i]), s[1][qb][i]);
+                tm[qb] = x;     // this lane's half; lane l ^ 32 holds the other
+            }
+        };
+        float tmc[NQB];     // this lane's half of the tile maximum of the scores whose softmax is next
+        auto body = [&](const uint8_t *kn, const uint8_t *vb, int t, f32x16 (&s)[2][NQB], f32x16 (&sn)[2][NQB])
+            __attribute__((always_inline)) {
+            // tmc holds this lane's half of each query's tile maximum.  Every
+            // lane being within m + kLazy (mlim) is the same test as every full
+            // maximum being within it, so the halves are combined only when the
+            // reference moves (one ballot per comparison).
+            uint64_t over = 0;
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) over |= __builtin_amdgcn_ballot_w64(tmc[qb] > mlim[qb]);
+            if (over != 0) {
+                float tm[NQB];
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmc[qb]), __float_as_uint(tmc[qb]),
+                                                                     false, false);
+                    tm[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+                }
+                acc_settle8(oacc);
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) {
+                    const float mn = fmaxf(m[qb], tm[qb]);
+                    const float alpha = (mn == kNegInf || m[qb] == mn) ? 1.0f
+                                      : (m[qb] == kNegInf ? 0.0f : fast_exp2((m[qb] - mn) * scale_log2));
+                    l[qb] *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) oacc[qb][dt][i] *= alpha;
+                    m[qb] = mn;
+                    mlim[qb] = mn + lazy_raw;
+                    msub[qb] = (mn == kNegInf) ? 0.0f : mn * scale_log2;
+                }
+            }
+            qk(kn, sn);
+            // P~ = exp2(S scale log2e - m scale log2e), l += row sums (four
+            // partial sums), E4M3 operands: dword 4 kb + r holds elements
+            // 4 r .. 4 r + 3 of block kb
+            i32x8 pf[NQB];
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
+                float rs[4];     // set by the first weight of each (0 + x would cost an add)
+#pragma unroll
+                for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float e[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            e[u] = fast_exp2(fmaf(s[kbk][qb][4 * r + u], scale_log2, -msub[qb]));
+                            rs[u] = (kbk == 0 && r == 0) ? e[u] : rs[u] + e[u];
+                        }
+                        int w = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+                        w = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], w, true);
+                        pf[qb][4 * kbk + r] = w;
+                    }
+                l[qb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+            }
+            // O~^T += V^T P~^T
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const uint8_t *base = vb + voff[dt];
+                const i32x2 r0 = lds_read_tr8(base);
+                const i32x2 r1 = lds_read_tr8(base + 8 * ROWB);
+                const i32x2 r2 = lds_read_tr8(base + 32 * ROWB);
+                const i32x2 r3 = lds_read_tr8(base + 40 * ROWB);
+                const i32x8 a = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) mfma8_acc(oacc[qb][dt], a, pf[qb], unit_scale);
+            }
+            // interleave the score MFMAs of tile t + 1 with the exponentials
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
+            }
+            tmax(sn, t + 1, tmc);
+        };
+
+        auto kslot = [&](auto S) __attribute__((always_inline)) -> uint8_t * {
+            constexpr int s = decltype(S)::value % 4;
+            return s == 0 ? k0 : s == 1 ? k1 : s == 2 ? k2 : k3;
+        };
+        auto vslot = [&](auto S) __attribute__((always_inline)) -> uint8_t * {
+            constexpr int s = decltype(S)::value % 4;
+            return s == 0 ? v0 : s == 1 ? v1 : s == 2 ? v2 : v3;
+        };
+        // iteration j (slot j % 4): this wave's loads of tile j + 1 are done (tile
+        // j + 2's may be in flight); the barrier publishes every wave's and frees
+        // slot (j + 3) % 4 (every wave is past iteration j - 1), which receives
+        // tile j + 3.  Every iteration issues exactly four loads per wave (tiles
+        // past the end are zero fills), so the wait count is the same everywhere.
+        // Two score buffers alternate: even iterations read sa and fill sb.
+        f32x16 sa[2][NQB], sb[2][NQB];
+        // With PERSIST and a next block, the 4 loads copying its Q are issued
+        // after S(0) (below), behind this block's tiles 1 and 2 and the previous
+        // block's O stores: tiles 1 and 2 are then followed by at least 6 memory
+        // operations, and iterations 0 and 1 wait with vmcnt(6).
+        auto iter = [&](auto S, auto LAST, int j) __attribute__((always_inline)) {
+            constexpr int si = decltype(S)::value;
+            if (PERSIST && has_next && j < 2)
+                __builtin_amdgcn_s_waitcnt(kWaitVm6);
+            else
+                __builtin_amdgcn_s_waitcnt(kWaitVm2);
+            tile_barrier();
+            if constexpr (decltype(LAST)::value)
+                issue_last(kslot(Slot<si + 3>{}), vslot(Slot<si + 3>{}), j + 3);
+            else
+                issue(kslot(Slot<si + 3>{}), vslot(Slot<si + 3>{}), j + 3);
+            if (j < wtiles) {
+                if constexpr (si % 2 == 0) body(kslot(Slot<si + 1>{}), vslot(S), j, sa, sb);
+                else body(kslot(Slot<si + 1>{}), vslot(S), j, sb, sa);
+            }
+        };
+
+        // (with PERSIST tile 0 is resident already: loaded at the start, or by
+        // the previous block's last iterations, whose final wait and barrier
+        // cover it)
+        if (!PERSIST) {
+            issue(k0, v0, 0);
+            issue(k1, v1, 1);
+            issue(k2, v2, 2);
+            __builtin_amdgcn_s_waitcnt(kWaitVm4);       // this wave's part of tile 0
+            tile_barrier();
+        }
+        if (wtiles > 0) {
+            qk(k0, sa);
+            tmax(sa, 0, tmc);
+        }
+        if (has_next) {
+            // this wave's reads of qs are complete (its own rows only): copy the
+            // next block's Q over them
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            issue_q(nxt);
+        }
+        // the last group of four iterations is the only one that loads past
+        // the padded end (tiles nend .. nend + 2)
+        int j = 0;
+        for (; j + 4 < nend; j += 4) {
+            iter(Slot<0>{}, Slot<0>{}, j);
+            iter(Slot<1>{}, Slot<0>{}, j + 1);
+            iter(Slot<2>{}, Slot<0>{}, j + 2);
+            iter(Slot<3>{}, Slot<0>{}, j + 3);
+        }
+        if (j < nend) {
+            iter(Slot<0>{}, Slot<1>{}, j);
+            iter(Slot<1>{}, Slot<1>{}, j + 1);
+            iter(Slot<2>{}, Slot<1>{}, j + 2);
+            iter(Slot<3>{}, Slot<1>{}, j + 3);
+        }
+        // no load outlives the last block (the next block's tiles 1 and 2 stay
+        // in flight otherwise)
+        if (!has_next) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+
+        // ---- epilogue: O = v_scale O~ / l, LSE = m + log l ------------------------
+        acc_settle8(oacc);
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
-            float x = fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), s[1][qb][0]);
-            x = fmaxf(x, s[1][qb][1]);
-#pragma unroll
-            for (int i = 2; i < 16; ++i) x = fmaxf(fmaxf(x, s[0][qb][i]), s[1][qb][i]);
-            tm[qb] = x;     // this lane's half; lane l ^ 32 holds the other
-        }
-    };
-    float tmc[NQB];     // this lane's half of the tile maximum of the scores whose softmax is next
-    auto body = [&](const uint8_t *kn, const uint8_t *vb, int t, f32x16 (&s)[2][NQB], f32x16 (&sn)[2][NQB])
-        __attribute__((always_inline)) {
-        // tmc holds this lane's half of each query's tile maximum.  Every
-        // lane being within m + kLazy (mlim) is the same test as every full
-        // maximum being within it, so the halves are combined only when the
-        // reference moves (one ballot per comparison).
-        uint64_t over = 0;
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) over |= __builtin_amdgcn_ballot_w64(tmc[qb] > mlim[qb]);
-        if (over != 0) {
-            float tm[NQB];
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) {
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmc[qb]), __float_as_uint(tmc[qb]),
-                                                                 false, false);
-                tm[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-            }
-            acc_settle8(oacc);
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) {
-                const float mn = fmaxf(m[qb], tm[qb]);
-                const float alpha = (mn == kNegInf || m[qb] == mn) ? 1.0f
-                                  : (m[qb] == kNegInf ? 0.0f : fast_exp2((m[qb] - mn) * scale_log2));
-                l[qb] *= alpha;
+            const int qi = qw0 + 32 * qb + c;
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l[qb]), __float_as_uint(l[qb]), false, false);
+            const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            const bool valid = (qi < Lq) && (lt > 0.0f);
+            const float inv = valid ? v_scale / lt : 0.0f;
+            if (qi < Nq) {
+                uint16_t *orow = O + (qrow0 + qi) * D;
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[qb][dt][i] *= alpha;
-                m[qb] = mn;
-                mlim[qb] = mn + lazy_raw;
-                msub[qb] = (mn == kNegInf) ? 0.0f : mn * scale_log2;
+                    for (int r = 0; r < 4; ++r) {
+                        uint2 w;
+                        w.x = valid ? pack_bf16x2_hw(oacc[qb][dt][4 * r + 0] * inv, oacc[qb][dt][4 * r + 1] * inv) : 0u;
+                        w.y = valid ? pack_bf16x2_hw(oacc[qb][dt][4 * r + 2] * inv, oacc[qb][dt][4 * r + 3] * inv) : 0u;
+                        *reinterpret_cast<uint2 *>(orow + 32 * dt + 8 * r + 4 * g) = w;
+                    }
+                if (LSE && g == 0)
+                    LSE[qrow0 + qi] = valid ? (m[qb] * scale_log2 + __log2f(lt)) * kLn2 : kNegInf;
             }
         }
-        qk(kn, sn);
-        // P~ = exp2(S scale log2e - m scale log2e), l += row sums (four
-        // partial sums), E4M3 operands: dword 4 kb + r holds elements
-        // 4 r .. 4 r + 3 of block kb
-        i32x8 pf[NQB];
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-            float rs[4];     // set by the first weight of each (0 + x would cost an add)
-#pragma unroll
-            for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float e[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        e[u] = fast_exp2(fmaf(s[kbk][qb][4 * r + u], scale_log2, -msub[qb]));
-                        rs[u] = (kbk == 0 && r == 0) ? e[u] : rs[u] + e[u];
-                    }
-                    int w = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
-                    w = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], w, true);
-                    pf[qb][4 * kbk + r] = w;
-                }
-            l[qb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-        }
-        // O~^T += V^T P~^T
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-            const uint8_t *base = vb + voff[dt];
-            const i32x2 r0 = lds_read_tr8(base);
-            const i32x2 r1 = lds_read_tr8(base + 8 * ROWB);
-            const i32x2 r2 = lds_read_tr8(base + 32 * ROWB);
-            const i32x2 r3 = lds_read_tr8(base + 40 * ROWB);
-            const i32x8 a = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) mfma8_acc(oacc[qb][dt], a, pf[qb], unit_scale);
-        }
-        // interleave the score MFMAs of tile t + 1 with the exponentials
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
-        }
-        tmax(sn, t + 1, tmc);
-    };
-
-    auto kslot = [&](auto S) __attribute__((always_inline)) -> uint8_t * {
-        constexpr int s = decltype(S)::value % 4;
-        return s == 0 ? k0 : s == 1 ? k1 : s == 2 ? k2 : k3;
-    };
-    auto vslot = [&](auto S) __attribute__((always_inline)) -> uint8_t * {
-        constexpr int s = decltype(S)::value % 4;
-        return s == 0 ? v0 : s == 1 ? v1 : s == 2 ? v2 : v3;
-    };
-    // iteration j (slot j % 4): this wave's loads of tile j + 1 are done (tile
-    // j + 2's may be in flight); the barrier publishes every wave's and frees
-    // slot (j + 3) % 4 (every wave is past iteration j - 1), which receives
-    // tile j + 3.  Every iteration issues exactly four loads per wave (tiles
-    // past the end are zero fills), so the wait count is the same everywhere.
-    // Two score buffers alternate: even iterations read sa and fill sb.
-    f32x16 sa[2][NQB], sb[2][NQB];
-    // With PERSIST and a next block, the 4 loads copying its Q are issued
-    // after S(0) (below), behind this block's tiles 1 and 2 and the previous
-    // block's O stores: tiles 1 and 2 are then followed by at least 6 memory
-    // operations, and iterations 0 and 1 wait with vmcnt(6).
-    auto iter = [&](auto S, auto LAST, int j) __attribute__((always_inline)) {
-        constexpr int si = decltype(S)::value;
-        if (PERSIST && has_next && j < 2)
-            __builtin_amdgcn_s_waitcnt(kWaitVm6);
-        else
-            __builtin_amdgcn_s_waitcnt(kWaitVm2);
-        tile_barrier();
-        if constexpr (decltype(LAST)::value)
-            issue_last(kslot(Slot<si + 3>{}), vslot(Slot<si + 3>{}), j + 3);
-        else
-            issue(kslot(Slot<si + 3>{}), vslot(Slot<si + 3>{}), j + 3);
-        if (j < wtiles) {
-            if constexpr (si % 2 == 0) body(kslot(Slot<si + 1>{}), vslot(S), j, sa, sb);
-            else body(kslot(Slot<si + 1>{}), vslot(S), j, sb, sa);
-        }
-    };
-
-    // (with PERSIST tile 0 is resident already: loaded at the start, or by
-    // the previous block's last iterations, whose final wait and barrier
-    // cover it)
-    if (!PERSIST) {
-        issue(k0, v0, 0);
-        issue(k1, v1, 1);
-        issue(k2, v2, 2);
-        __builtin_amdgcn_s_waitcnt(kWaitVm4);       // this wave's part of tile 0
-        tile_barrier();
-    }
-    if (wtiles > 0) {
-        qk(k0, sa);
-        tmax(sa, 0, tmc);
-    }
-    if (has_next) {
-        // this wave's reads of qs are complete (its own rows only): copy the
-        // next block's Q over them
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        issue_q(nxt);
-    }
-    // the last group of four iterations is the only one that loads past
-    // the padded end (tiles nend .. nend + 2)
-    int j = 0;
-    for (; j + 4 < nend; j += 4) {
-        iter(Slot<0>{}, Slot<0>{}, j);
-        iter(Slot<1>{}, Slot<0>{}, j + 1);
-        iter(Slot<2>{}, Slot<0>{}, j + 2);
-        iter(Slot<3>{}, Slot<0>{}, j + 3);
-    }
-    if (j < nend) {
-        iter(Slot<0>{}, Slot<1>{}, j);
-        iter(Slot<1>{}, Slot<1>{}, j + 1);
-        iter(Slot<2>{}, Slot<1>{}, j + 2);
-        iter(Slot<3>{}, Slot<1>{}, j + 3);
-    }
-    // no load outlives the last block (the next block's tiles 1 and 2 stay
-    // in flight otherwise)
-    if (!has_next) __builtin_amdgcn_s_waitcnt(kWaitVm0);
-
-    // ---- epilogue: O = v_scale O~ / l, LSE = m + log l ------------------------
-    acc_settle8(oacc);
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-        const int qi = qw0 + 32 * qb + c;
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l[qb]), __float_as_uint(l[qb]), false, false);
-        const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        const bool valid = (qi < Lq) && (lt > 0.0f);
-        const float inv = valid ? v_scale / lt : 0.0f;
-        if (qi < Nq) {
-            uint16_t *orow = O + (qrow0 + qi) * D;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    uint2 w;
-                    w.x = valid ? pack_bf16x2_hw(oacc[qb][dt][4 * r + 0] * inv, oacc[qb][dt][4 * r + 1] * inv) : 0u;
-                    w.y = valid ? pack_bf16x2_hw(oacc[qb][dt][4 * r + 2] * inv, oacc[qb][dt][4 * r + 3] * inv) : 0u;
-                    *reinterpret_cast<uint2 *>(orow + 32 * dt + 8 * r + 4 * g) = w;
-                }
-            if (LSE && g == 0)
-                LSE[qrow0 + qi] = valid ? (m[qb] * scale_log2 + __log2f(lt)) * kLn2 : kNegInf;
-        }
-    }
-    if (!has_next) break;
-    L = Lnext;
-    first = false;
+        if (!has_next) break;
+        L = Lnext;
+        first = false;
     }   // blocks
 }
 
