@@ -237,3 +237,29 @@ def test_lse_null(persistent):
         assert st == 0, lib.osm_status_str(st)
         torch.cuda.synchronize()
         assert np.array_equal(host_bits(o1), host_bits(o2)), dtype
+
+
+def test_no_keys_through_abi():
+    """seqlen_k == 0 with k = v = NULL: every query row sees no key, so
+    O = +0 and LSE = -inf, for the bf16 and the FP8 forward (300 query
+    blocks, causal and not)."""
+    torch = torch_mod()
+    lib = osm.load_library()
+    B, Hq, Hkv, Nq = 2, 6, 3, 12800
+    q8 = torch.zeros((B, Hq, Nq, 128), dtype=torch.uint8, device="cuda")
+    qb = torch.randn((B, Hq, Nq, 128), device="cuda").to(torch.bfloat16)
+    for causal in (0, 1):
+        announce(f"fwd no keys causal={causal}")
+        for fp8 in (False, True):
+            o = torch.full((B, Hq, Nq, 128), float("nan"), device="cuda").to(torch.bfloat16)
+            lse = torch.zeros((B, Hq, Nq), dtype=torch.float32, device="cuda")
+            if fp8:
+                st = lib.osm_attn_fwd_fp8(osm._ptr(q8), None, None, osm._ptr(o), osm._ptr(lse), B, Hq, Hkv, Nq, 0,
+                                          128, None, None, 0.1, 1.0, causal, osm._stream())
+            else:
+                st = lib.osm_attn_fwd(osm._ptr(qb), None, None, osm._ptr(o), osm._ptr(lse), 1, B, Hq, Hkv, Nq, 0,
+                                      128, None, None, 0.1, causal, osm._stream())
+            assert st == 0, lib.osm_status_str(st)
+            torch.cuda.synchronize()
+            assert np.all(host_bits(o) == 0), f"fp8={fp8}"
+            assert np.all(np.isneginf(host(lse))), f"fp8={fp8}"

@@ -116,3 +116,19 @@ def test_row_stride(orc, cols, ld_x, ld_y):
     y_ref, m_ref, l_ref = orc.softmax_rows(x)
     check_softmax(yb[:, :cols], host(md), host(sd), y_ref, m_ref, l_ref)
     assert np.all(yb[:, cols:] == sentinel)
+
+
+def test_zero_columns_through_abi():
+    """cols == 0 with x = y = NULL: each empty row's statistics are the
+    empty set's, m = -inf and l = 0 (nothing is read or written through
+    the NULL pointers)."""
+    announce("softmax cols=0, x = y = NULL")
+    torch = __import__("torch")
+    rows = 37
+    md = torch.full((rows,), float("nan"), dtype=torch.float32, device="cuda")
+    sd = torch.full((rows,), float("nan"), dtype=torch.float32, device="cuda")
+    lib = osm.load_library()
+    st = lib.osm_softmax_rows(None, None, rows, 0, 0, 0, osm._ptr(md), osm._ptr(sd), osm._stream())
+    assert st == 0, lib.osm_status_str(st)
+    torch.cuda.synchronize()
+    assert np.all(np.isneginf(host(md))) and np.all(host(sd) == 0.0)
