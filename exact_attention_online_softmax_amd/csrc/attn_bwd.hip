@@ -183,10 +183,15 @@ constexpr int KV_NW = 8;                       // wavefronts per workgroup (two 
 constexpr int KV_KW = 32;                      // keys per wavefront
 constexpr int KV_BK = KV_KW * KV_NW;           // keys per workgroup
 constexpr int KV_NT = 64 * KV_NW;
-constexpr int KV_QT = 128;                     // query rows per LDS stage
+// query rows per LDS stage: 64 keeps the four stage arrays (Q and dO, two
+// stages) within the first 64 KiB of LDS, where operand reads address them
+// with the 16-bit immediate offset; with 128 every read of the second
+// stage's arrays needed its address computed (an OR per read)
+constexpr int KV_QT = 64;
 constexpr int KV_STB = KV_QT * ROWB;           // bytes of Q (or dO) per stage
 constexpr int KV_BLK = KV_STB / 1024 / KV_NW;  // 1 KiB DMA blocks per wave per array per stage
-static_assert(KV_QT * 8 == 256 * 4, "waves 0-3 load a stage's (lse2, D), 256 bytes each");
+static_assert(KV_QT % 32 == 0 && KV_QT / 32 <= KV_NW,
+              "waves 0 .. KV_QT/32-1 load a stage's (lse2, D), 256 bytes each");
 
 template <bool CAUSAL>
 __global__ void __launch_bounds__(KV_NT, 1)
@@ -276,8 +281,8 @@ attn_bwd_dkdv(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 
     // DMA of one stage: wave w fills 1 KiB blocks KV_BLK w .. +KV_BLK-1 (four
     // rows each) of the Q and dO arrays, lane l row 4 blk + l/16, slot l%16
-    // (holding global chunk slot ^ swz(row)); waves 0-3 also load (lse2, D)
-    // of rows 32 w .. 32 w + 31.  Rows at or past Lq read as zeros: their Q
+    // (holding global chunk slot ^ swz(row)); waves 0 .. KV_QT/32-1 also load
+    // (lse2, D) of rows 32 w .. 32 w + 31.  Rows at or past Lq read as zeros: their Q
     // and dO are 0, so whatever their weight, they add nothing.
     uint32_t dmo[KV_BLK];
 #pragma unroll
@@ -297,7 +302,7 @@ attn_bwd_dkdv(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
         for (int i = 0; i < KV_BLK; ++i) dma16(rq, qd + (KV_BLK * wave + i) * 1024, dmo[i]);
 #pragma unroll
         for (int i = 0; i < KV_BLK; ++i) dma16(ro, od + (KV_BLK * wave + i) * 1024, dmo[i]);
-        if (wave < 4) dma4(rl, reinterpret_cast<uint8_t *>(ld) + 256 * wave, 256 * wave + 4 * lane);
+        if (wave < KV_QT / 32) dma4(rl, reinterpret_cast<uint8_t *>(ld) + 256 * wave, 256 * wave + 4 * lane);
     };
 
     // operand offsets within a 32-row block of a stage.  Row-wise A operand
