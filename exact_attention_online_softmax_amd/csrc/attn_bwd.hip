@@ -93,8 +93,17 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t *p) {
 // only at the end, fit only in the AGPRs, so their MFMAs are inline
 // assembly.  The hazard recognizer does not look into inline assembly: two
 // wait states let a VALU-written operand settle before the MFMA reads it.
+//
+// NOP: the two wait states, for the first MFMA that reads a P or dS operand
+// converted just before it.  Later uses of the same operand come after that
+// MFMA and the LDS reads of their own A operand, so they need none (checked
+// on the generated code by the test suite).
+template <bool NOP>
 __device__ __forceinline__ void mfma_acc(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
-    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    if constexpr (NOP)
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
 __device__ __forceinline__ void acc_zero(f32x16 &acc, const bf16x8 &z) {
@@ -370,8 +379,13 @@ attn_bwd_dkdv(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                                        lds_read_tr(ob + 16 * hh * ROWB + thi[dt]));
                 const bf16x8 aq = cat4(lds_read_tr(qb + 16 * hh * ROWB + tlo[dt]),
                                        lds_read_tr(qb + 16 * hh * ROWB + thi[dt]));
-                mfma_acc(dva[dt], ao, pb[hh]);
-                mfma_acc(dka[dt], aq, db[hh]);
+                if (dt == 0) {
+                    mfma_acc<true>(dva[dt], ao, pb[hh]);
+                    mfma_acc<true>(dka[dt], aq, db[hh]);
+                } else {
+                    mfma_acc<false>(dva[dt], ao, pb[hh]);
+                    mfma_acc<false>(dka[dt], aq, db[hh]);
+                }
             }
     };
 
@@ -610,7 +624,10 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                 const bf16x8 a = cat4(lds_read_tr(kb + 16 * hh * ROWB + tlo[dt]),
                                       lds_read_tr(kb + 16 * hh * ROWB + thi[dt]));
 #pragma unroll
-                for (int qb = 0; qb < DQ_NQB; ++qb) mfma_acc(dqa[qb][dt], a, db[qb][hh]);
+                for (int qb = 0; qb < DQ_NQB; ++qb) {
+                    if (dt == 0) mfma_acc<true>(dqa[qb][dt], a, db[qb][hh]);
+                    else mfma_acc<false>(dqa[qb][dt], a, db[qb][hh]);
+                }
             }
     };
 
