@@ -5,6 +5,9 @@ One step runs every operation of the path once on its standard workload,
 inputs already resident in HBM:
 
   softmax   osm_softmax_rows        4096 x 32000 fp32, N(0,9) + one spike/row in [20,90)
+                                    (rows held on chip between the passes: 8 B/elem)
+  softmax_2pass osm_softmax_rows_twopass  the same input, every row read twice from memory
+                                    (the pages' two-pass count: 12 B/elem)
   fwd       osm_attn_fwd            bf16 B=4 H=32 N=4096 d=128, non-causal   (the headline)
   fwd_causal osm_attn_fwd           bf16 B=8 H=16 N=8192 d=128, causal, lengths U[1024,8192]
   decode    osm_attn_decode_splitkv bf16 B=16 Hq=32 Hkv=8 d=128, L U[4096,32768], 256-key pieces
@@ -19,8 +22,11 @@ inputs already resident in HBM:
   bwd_causal osm_attn_bwd           backward of the fwd_causal workload
 
 Each call is timed with HIP events on the stream it runs on (torch's current
-stream); ``value`` is the headline forward's TFLOP/s.  The CPU oracle is timed
-on a bounded sample of the headline workload as a reported baseline.
+stream); ``value`` is the headline forward's TFLOP/s (mean over the timed
+steps; the median and minimum are reported beside it).  The CPU oracle is
+timed on a bounded sample of the headline workload as a reported baseline.
+After the timed steps, two reference kernels (libosm_probe.so: a streaming
+copy and a matrix-core loop) are timed once as "achievable" context.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
 """
@@ -54,10 +60,11 @@ def bf16_dev(bits, torch):
 
 
 KERNEL_SOURCES = {"fwd": "attn_fwd.hip", "fwd_causal": "attn_fwd.hip", "softmax": "softmax_rows.hip",
+                  "softmax_2pass": "softmax_rows.hip",
                   "decode": "decode.hip", "merge_lse": "merge_lse.hip", "extend": "decode.hip",
                   "bwd": "attn_bwd.hip", "bwd_causal": "attn_bwd.hip", "fwd_fp8": "attn_fwd_fp8.hip"}
-WORKLOADS = ["softmax", "fwd", "fwd_causal", "decode", "merge_lse", "extend", "bwd", "bwd_causal",
-             "fwd_fp8"]
+WORKLOADS = ["softmax", "softmax_2pass", "fwd", "fwd_causal", "decode", "merge_lse", "extend", "bwd",
+             "bwd_causal", "fwd_fp8"]
 
 
 def source_hash(name):
@@ -88,6 +95,61 @@ def traffic_from_profile(path, name):
         return None
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (or the platform string)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
+def achievable(torch):
+    """Rates of two reference kernels on this GPU (libosm_probe.so), each the
+    median of 20 back-to-back launches timed with HIP events: a streaming copy
+    of 1 GiB (GB/s of bytes read + written) and a bf16 matrix-core loop on
+    N(0, 1) operands (TFLOP/s) with one 256-thread workgroup per compute unit,
+    i.e. one wave per SIMD, as the attention forward runs."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "exact_attention_online_softmax_amd", "libosm_probe.so"))
+    vp = ctypes.c_void_p
+    lib.osmprobe_copy.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
+    lib.osmprobe_mfma_bf16.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp]
+    stream = vp(torch.cuda.current_stream().cuda_stream)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def timed(fn, reps=20):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        fn()
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs])) / 1e3
+
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: lib.osmprobe_copy(vp(src.data_ptr()), vp(dst.data_ptr()), nbytes, 8 * cus, stream))
+    del src, dst
+    grid, iters = cus, 4096
+    g = np.random.default_rng(12345)
+    ops = torch.from_numpy(g.standard_normal(grid * 256 * 128, dtype=np.float32)).to("cuda").to(torch.bfloat16)
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    t_mfma = timed(lambda: lib.osmprobe_mfma_bf16(vp(ops.data_ptr()), vp(out.data_ptr()), grid, iters, stream))
+    flops = grid * 4 * iters * 8 * 32768.0
+    return {"copy_GBps": round(2 * nbytes / t_copy / 1e9, 1),
+            "copy": "1 GiB streaming copy (nontemporal 16-byte loads and stores), bytes read + written",
+            "mfma_bf16_TFLOPs": round(flops / t_mfma / 1e12, 1),
+            "mfma": f"v_mfma_f32_32x32x16_bf16 chains on N(0,1) operands, {grid} workgroups x 4 waves, "
+                    f"no memory traffic in the loop"}
+
+
 def cpu_baseline(inp, seconds):
     """The oracle on the first rows of the headline workload, sized to take
     about `seconds` on the host's cores."""
@@ -106,7 +168,7 @@ def cpu_baseline(inp, seconds):
     dt = time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": round(n * flops_per_row / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"first {n} query rows (of {B * H * N}) of the B{B} H{H} N{N} d{d} "
                       f"non-causal forward, fp64, {dt:.1f} s"}
 
@@ -118,7 +180,8 @@ def summarize(name, trace_dir, out):
     size (the torch copy kernel run with --copy-calibration)."""
     import csv
     import glob
-    kern = {"fwd": "attn_fwd_bf16", "fwd_causal": "attn_fwd_bf16", "softmax": "softmax_rows",
+    kern = {"fwd": "attn_fwd_bf16", "fwd_causal": "attn_fwd_bf16", "softmax": "softmax_rows_resident",
+            "softmax_2pass": "softmax_rows_streaming",
             "decode": "decode_split", "merge_lse": "merge_lse", "extend": "decode_split",
             "bwd": "attn_bwd_dkdv", "bwd_causal": "attn_bwd_dkdv", "fwd_fp8": "attn_fwd_fp8"}[name]
     lines = [f"# rocprofv3 summary: {name}", ""]
@@ -141,7 +204,8 @@ def summarize(name, trace_dir, out):
         # the non-causal forward runs on the persistent grid (one workgroup per
         # compute unit); the causal one on one workgroup per query block
         want = {"fwd": ("attn_fwd_bf16_d128_persist", None), "fwd_causal": ("attn_fwd_bf16", 4096),
-                "softmax": ("softmax_rows", None), "decode": ("decode_split", None),
+                "softmax": ("softmax_rows_resident", None), "softmax_2pass": ("softmax_rows_streaming", None),
+                "decode": ("decode_split", None),
                 "merge_lse": ("merge_lse", None), "extend": ("decode_split", None),
                 "bwd": ("attn_bwd_dkdv", None), "bwd_causal": ("attn_bwd_dkdv", None),
                 "fwd_fp8": ("attn_fwd_fp8", None)}[name]
@@ -219,6 +283,8 @@ def main():
     ap.add_argument("--only", choices=WORKLOADS, default=None,
                     help="run one operation only (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the reference copy and matrix-core kernels")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB per step (scales rocprof "
@@ -250,6 +316,14 @@ def main():
         calls["softmax"] = lambda: osm.softmax_rows(x, out=y)
         # one HBM read + one HBM write per element: the row stays in registers
         work["softmax"] = ("hbm", 8.0 * x.numel(), "4096 x 32000 fp32, 8 B/elem")
+    if "softmax_2pass" in names:
+        if "softmax" not in names:
+            log("inputs: softmax 4096 x 32000")
+            x = torch.from_numpy(inputs.config2()).to("cuda")
+        y2 = torch.empty_like(x)
+        calls["softmax_2pass"] = lambda: osm.softmax_rows(x, out=y2, two_pass=True)
+        # the pages' count: two loads and one store per element
+        work["softmax_2pass"] = ("hbm", 12.0 * x.numel(), "4096 x 32000 fp32, two passes, 12 B/elem")
     if "fwd" in names or "bwd" in names or args.only is None:
         log("inputs: fwd B4 H32 N4096 d128")
         inp3 = inputs.config3()
@@ -385,7 +459,8 @@ def main():
             b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in names}
+    times = {n: [a.elapsed_time(b) for a, b in ev[n]] for n in names}
+    ms = {n: float(np.mean(times[n])) for n in names}
 
     comps = {}
     for n in names:
@@ -397,7 +472,8 @@ def main():
             ach, peak, unit = amount / t / 1e12, PEAK_FP8_TFLOPS, "TFLOP/s"
         else:
             ach, peak, unit = amount / t / 1e9, PEAK_HBM_GBS, "GB/s"
-        comps[n] = {"workload": desc, "ms": round(ms[n], 4), "achieved": round(ach, 2),
+        comps[n] = {"workload": desc, "ms": round(ms[n], 4), "ms_median": round(float(np.median(times[n])), 4),
+                    "ms_min": round(float(np.min(times[n])), 4), "achieved": round(ach, 2),
                     "unit": unit, "bound": "hbm" if bound == "hbm" else "mfma",
                     "peak": round(peak, 1), "frac": round(ach / peak, 4),
                     "algorithmic": amount}
@@ -413,12 +489,15 @@ def main():
            "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": f"attn_fwd {hc['workload']}" if head == "fwd" else hc["workload"],
-                      "step": "softmax_rows + attn_fwd (non-causal) + attn_fwd (causal varlen) "
+                      "step": "softmax_rows + softmax_rows_twopass + attn_fwd (non-causal) + attn_fwd (causal varlen) "
                               "+ attn_decode_splitkv + merge_lse + attn_extend + attn_bwd (non-causal) "
                               "+ attn_bwd (causal varlen) + attn_fwd_fp8" if args.only is None
                               else args.only,
                       "global_batch": 4, "seq_len": 4096, "parallelism": "none (1 GPU)"},
            "roofline": roofline, "components": comps}
+    if not args.no_context and args.only is None:
+        log("context: reference copy and matrix-core kernels")
+        out["achievable"] = achievable(torch)
     if not args.no_cpu_baseline and args.only is None:
         log("cpu baseline: oracle on a sample of the headline workload")
         out["cpu_baseline"] = cpu_baseline(inp3, args.cpu_seconds)

@@ -8,7 +8,7 @@ or a call fails, an exception is raised.
 
 Entry points (same names as the C ABI, without the ``osm_`` prefix):
 
-* ``softmax_rows(x, return_stats=False)``
+* ``softmax_rows(x, return_stats=False, two_pass=False)``
 * ``attn_fwd(q, k, v, *, scale=None, causal=False, seqlens_q=None, seqlens_k=None)``
 * ``attn_decode_splitkv(q, k_cache, v_cache, seqlens_k, *, scale=None, split_size=256)``
 * ``merge_partials(part_m, part_l, part_o, out_dtype=torch.float32)``
@@ -27,7 +27,7 @@ OSM_F32 = 0
 OSM_BF16 = 1
 STATUS = {0: "OSM_OK", 1: "OSM_ERR_NULL", 2: "OSM_ERR_SHAPE", 3: "OSM_ERR_UNSUPPORTED",
           4: "OSM_ERR_WORKSPACE", 5: "OSM_ERR_HIP"}
-EXPORTS = ("osm_status_str", "osm_softmax_rows", "osm_attn_fwd", "osm_decode_workspace_bytes",
+EXPORTS = ("osm_status_str", "osm_softmax_rows", "osm_softmax_rows_twopass", "osm_attn_fwd", "osm_decode_workspace_bytes",
            "osm_attn_decode_splitkv", "osm_merge_partials", "osm_merge_lse", "osm_attn_extend",
            "osm_attn_bwd_workspace_bytes", "osm_attn_bwd", "osm_attn_fwd_fp8")
 
@@ -54,6 +54,7 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.osm_status_str.argtypes = [ctypes.c_int]
     lib.osm_status_str.restype = ctypes.c_char_p
     lib.osm_softmax_rows.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp]
+    lib.osm_softmax_rows_twopass.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp]
     lib.osm_attn_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32, i32,
                                  vp, vp, f32, i32, vp]
     lib.osm_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
@@ -70,7 +71,7 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.osm_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.osm_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, i32, i32, i32,
                                  i32, i32, vp, vp, f32, i32, vp, ctypes.c_size_t, vp]
-    for name in ("osm_softmax_rows", "osm_attn_fwd", "osm_attn_decode_splitkv",
+    for name in ("osm_softmax_rows", "osm_softmax_rows_twopass", "osm_attn_fwd", "osm_attn_decode_splitkv",
                  "osm_merge_partials", "osm_merge_lse", "osm_attn_extend", "osm_attn_bwd",
                  "osm_attn_fwd_fp8"):
         getattr(lib, name).restype = ctypes.c_int
@@ -136,9 +137,12 @@ def _lengths(t, name, batch, device):
 # ---------------------------------------------------------------------------
 # entry points
 # ---------------------------------------------------------------------------
-def softmax_rows(x, return_stats: bool = False, out=None):
+def softmax_rows(x, return_stats: bool = False, out=None, two_pass: bool = False):
     """Row softmax of a 2-D fp32 GPU tensor (two-pass online normalizer).
-    Returns y, or (y, row_max, row_sum) with ``return_stats``."""
+    Returns y, or (y, row_max, row_sum) with ``return_stats``.  With
+    ``two_pass`` every row is read twice from memory
+    (``osm_softmax_rows_twopass``); otherwise rows of up to 65536 columns stay
+    on chip between the passes."""
     torch = _torch()
     lib = load_library()
     _device_tensor(x, "x", (torch.float32,))
@@ -152,8 +156,8 @@ def softmax_rows(x, return_stats: bool = False, out=None):
     if return_stats:
         mx = torch.empty(rows, dtype=torch.float32, device=x.device)
         sm = torch.empty(rows, dtype=torch.float32, device=x.device)
-    _check(lib.osm_softmax_rows(_ptr(x), _ptr(y), rows, cols, cols, cols, _ptr(mx), _ptr(sm),
-                                _stream()))
+    fn = lib.osm_softmax_rows_twopass if two_pass else lib.osm_softmax_rows
+    _check(fn(_ptr(x), _ptr(y), rows, cols, cols, cols, _ptr(mx), _ptr(sm), _stream()))
     return (y, mx, sm) if return_stats else y
 
 

@@ -1,4 +1,5 @@
-"""Build libosm.so (the gfx950 kernels and the C ABI) in-tree with hipcc.
+"""Build libosm.so (the gfx950 kernels and the C ABI) in-tree with hipcc, and
+libosm_probe.so (the benchmark's reference copy and matrix-core kernels).
 
 Usage: python -m exact_attention_online_softmax_amd.build
 """
@@ -14,8 +15,10 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIBRARY = os.path.join(HERE, "libosm.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["abi.cpp", "softmax_rows.hip", "attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "decode.hip", "merge_lse.hip"]
+SOURCES = ["abi.cpp", "layout.cpp", "softmax_rows.hip", "attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "decode.hip", "merge_lse.hip"]
 ARCH = "gfx950"
+PROBE_SOURCE = "probe.hip"
+PROBE_LIBRARY = os.path.join(HERE, "libosm_probe.so")
 
 # -packed-fp32-ops: no packed fp32 VALU instructions are generated.
 FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -61,8 +64,16 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIBRARY)
+    # the benchmark's reference kernels (copy, matrix-core loop): their own library
+    obj = _compile(PROBE_SOURCE)
+    tmp = PROBE_LIBRARY + ".tmp"
+    r = subprocess.run(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, PROBE_LIBRARY)
     if verbose:
-        print(f"built {LIBRARY}")
+        print(f"built {LIBRARY} and {PROBE_LIBRARY}")
     return LIBRARY
 
 

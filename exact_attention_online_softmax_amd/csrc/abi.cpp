@@ -48,6 +48,17 @@ osm_status osm_softmax_rows(const float *x, float *y, int64_t rows, int64_t cols
     return hip_status(osm::launch_softmax_rows(a, p, static_cast<hipStream_t>(stream)));
 }
 
+osm_status osm_softmax_rows_twopass(const float *x, float *y, int64_t rows, int64_t cols, int64_t ld_x,
+                                    int64_t ld_y, float *row_max, float *row_sum, osm_stream stream) {
+    if (rows < 0 || cols < 0 || ld_x < cols || ld_y < cols) return OSM_ERR_SHAPE;
+    if (rows == 0) return OSM_OK;
+    if ((!x || !y) && cols > 0) return OSM_ERR_NULL;
+    if (cols == 0 && !row_max && !row_sum) return OSM_OK;
+    osm::SoftmaxArgs a{x, y, rows, cols, ld_x, ld_y, row_max, row_sum};
+    const osm::SoftmaxPlan p = osm::plan_softmax_rows(cols, 1);
+    return hip_status(osm::launch_softmax_rows(a, p, static_cast<hipStream_t>(stream)));
+}
+
 osm_status osm_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                         osm_dtype dtype, int32_t batch, int32_t heads_q, int32_t heads_kv,
                         int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
@@ -149,6 +160,7 @@ osm_status osm_attn_decode_splitkv(const void *q, const void *k_cache, const voi
     // rows are read 16 bytes at a time
     if (misaligned16(q) || misaligned16(k_cache) || misaligned16(v_cache)) return OSM_ERR_UNSUPPORTED;
     const osm::DecodeLayout lay = osm::decode_layout(batch, heads_q, max_seqlen_k, head_dim, split_size);
+    if (lay.total == 0) return OSM_ERR_UNSUPPORTED;   // a workspace past 2^62 bytes
     if (!workspace || workspace_bytes < lay.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
         return OSM_ERR_WORKSPACE;
     osm::DecodeArgs a{q, k_cache, v_cache, o, lse, dtype == OSM_BF16 ? 1 : 0, batch, heads_q,
@@ -196,6 +208,7 @@ osm_status osm_attn_extend(const void *q, const void *k_new, const void *v_new, 
     // rows are read 16 bytes at a time
     if (misaligned16(q) || misaligned16(k_new) || misaligned16(v_new)) return OSM_ERR_UNSUPPORTED;
     const osm::DecodeLayout lay = osm::decode_layout(batch, heads_q, n_new, head_dim, split_size);
+    if (lay.total == 0) return OSM_ERR_UNSUPPORTED;   // a workspace past 2^62 bytes
     if (!workspace || workspace_bytes < lay.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
         return OSM_ERR_WORKSPACE;
     // the new keys' pieces, summarized as in the split decode (every key valid)
@@ -225,6 +238,8 @@ osm_status osm_merge_lse(const void *o_parts, const float *lse_parts, int64_t ro
         return OSM_ERR_UNSUPPORTED;
     if (rows == 0) return OSM_OK;
     if (!o_parts || !lse_parts || !o) return OSM_ERR_NULL;
+    // pieces and output are read and written in vectors of up to 16 bytes
+    if (misaligned16(o_parts) || misaligned16(o)) return OSM_ERR_UNSUPPORTED;
     osm::MergeLseArgs m{o_parts, lse_parts, rows, num_parts, head_dim,
                         in_dtype == OSM_BF16 ? 1 : 0, out_dtype == OSM_BF16 ? 1 : 0, o, lse};
     return hip_status(osm::launch_merge_lse(m, static_cast<hipStream_t>(stream)));

@@ -22,7 +22,7 @@
 //    K and V stay in registers as MFMA operands and its dK, dV accumulators
 //    in the AGPRs.
 //    Every query row that can see those keys -- all query heads that read
-//    the key/value head -- streams through LDS, 128 rows of Q and dO per
+//    the key/value head -- streams through LDS, 64 rows of Q and dO per
 //    stage, double-buffered.  Per 32-query block: S = Q K^T and dP = dO V^T
 //    on the matrix cores (one key per lane column), P = exp2(S scale log2e
 //    - lse2), dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS, the
@@ -684,10 +684,6 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 }
 
 }  // namespace
-
-size_t attn_bwd_workspace_bytes(int64_t batch, int64_t heads_q, int64_t seqlen_q) {
-    return (size_t)(batch * heads_q * seqlen_q) * sizeof(float2);
-}
 
 hipError_t launch_attn_bwd(const AttnBwdArgs &a, hipStream_t s) {
     const int64_t rows = (int64_t)a.batch * a.heads_q * a.seqlen_q;

@@ -43,15 +43,20 @@
 //    (ds_read_b64_tr_b16): in each 16-lane group, lane i points at
 //    V[k0 + i/4][d0 + 4 (i%4) .. +3] and lane j receives V[k0 + e][d0 + j],
 //    e = 0..3 -- four consecutive keys of one dim, the operand layout.
-//  * rows at or past the valid length are never loaded: their loads are
-//    clamped to the last valid row, so LDS only ever holds finite valid data
-//    and NaN padding cannot reach an MFMA (0 * NaN = NaN); their scores are
-//    masked to -inf, so they add exactly zero.
-//  * the reference maximum is only raised (and O~, l rescaled) when a score
-//    exceeds it by more than 2^8 in weight ([P3] "Precision, and what can
-//    still go wrong": any reference that keeps the weights bounded works;
-//    the running maximum is the tightest one), so after the first tiles the
-//    rescale is skipped by a wave-uniform branch.
+//  * rows at or past the valid length are never read from memory: each
+//    tile's loads go through a buffer resource that ends at the valid
+//    length, and its range check fills those rows of LDS with zeros, so LDS
+//    only ever holds finite data and NaN padding cannot reach an MFMA
+//    (0 * NaN = NaN); their scores are masked to -inf, so they add exactly
+//    zero.
+//  * the reference is only raised (and O~, l rescaled) when a score exceeds
+//    it by more than 8 in base-2 units, so every weight stays at most 2^8 and
+//    the reference may sit up to that far below the running maximum.  The
+//    result does not depend on the reference: a common factor cancels
+//    between O~ and l ([P3] "Merging partial results": summaries relative to
+//    any common reference combine exactly), and l <= 2^8 N_k keeps clear of
+//    fp32 overflow.  After the first tiles the rescale is skipped by a
+//    wave-uniform branch.
 //  * tiles that need a mask (the causal diagonal, the ragged end) are the
 //    last ones each wave visits; they run in a separate, branchy loop so the
 //    main loop carries no mask code.

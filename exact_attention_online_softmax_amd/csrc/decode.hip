@@ -25,9 +25,10 @@
 // Pieces wholly past the valid length write the identity (m = -inf, l = 0).
 //
 // merge_partials: one workgroup per row; the row's largest piece maximum is
-// the common reference, every piece is weighted by exp(m_c - m) and added,
-// empty pieces skipped (their l and O~ are never read).  Then o = O~ / l
-// once and LSE = m + log l ([P3] "From weights to outputs").
+// the common reference, every piece is weighted by exp(m_c - m) and added;
+// an empty piece's l and O~ are loaded with the others but dropped by a
+// select, so whatever they hold (NaN included) never reaches a sum.  Then
+// o = O~ / l once and LSE = m + log l ([P3] "From weights to outputs").
 #include "osm_device.h"
 #include "osm_internal.h"
 
@@ -253,8 +254,8 @@ decode_split(const T *__restrict__ Q, const T *__restrict__ K, const T *__restri
 // found first, so every piece's weight exp(m_c - m) is final and the pieces
 // can be accumulated in any order with no rescaling; waves take pieces
 // c = wave, wave + 4, ..., lanes own NDL dims each, and the four partial sums
-// are added through LDS.  Empty pieces (m_c = -inf) are skipped without
-// reading their l or O~.
+// are added through LDS.  Empty pieces (m_c = -inf) get weight 0 through a
+// select (their l and O~ are loaded, so their memory must be valid).
 constexpr int MRG_THREADS = 256;
 constexpr int MRG_WAVES = MRG_THREADS / 64;
 
@@ -395,21 +396,6 @@ hipError_t launch_split_g(const DecodeArgs &a, const DecodeLayout &lay, hipStrea
 }
 
 }  // namespace
-
-static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-DecodeLayout decode_layout(int64_t batch, int64_t heads_q, int64_t max_seqlen_k, int64_t head_dim,
-                           int64_t split) {
-    DecodeLayout lay{};
-    lay.rows = batch * heads_q;
-    lay.chunks = (int32_t)((max_seqlen_k + split - 1) / split);
-    const size_t n = (size_t)lay.rows * (size_t)lay.chunks;
-    lay.off_m = 0;
-    lay.off_l = align256(n * sizeof(float));
-    lay.off_o = lay.off_l + align256(n * sizeof(float));
-    lay.total = lay.off_o + align256(n * (size_t)head_dim * sizeof(float));
-    return lay;
-}
 
 hipError_t launch_decode_split(const DecodeArgs &a, const DecodeLayout &lay, hipStream_t s) {
     if (a.dtype == 1)

@@ -1,5 +1,7 @@
 // osm_internal.h -- host-side launch interfaces between the C ABI layer and
 // the kernel translation units of libosm (not installed, not part of the ABI).
+// The sizes and plans (layout.cpp) are plain host code; the launchers live
+// beside their kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,6 +22,8 @@ struct SoftmaxPlan {
     int nv;          // float4 vectors per lane (resident)
     int threads;     // workgroup size
 };
+// float4 vectors per lane whose loads the streaming kernel issues together
+constexpr int kSoftmaxStreamBatch = 4;
 // force_variant: 0 = automatic, 1 = streaming
 SoftmaxPlan plan_softmax_rows(int64_t cols, int force_variant);
 hipError_t launch_softmax_rows(const SoftmaxArgs &a, const SoftmaxPlan &p, hipStream_t s);
@@ -59,6 +63,7 @@ struct AttnBwdArgs {
     int causal;
     void *workspace;     // attn_bwd_workspace_bytes(): (lse2, D) per query row
 };
+// 0 when the size does not fit in 2^62 bytes
 size_t attn_bwd_workspace_bytes(int64_t batch, int64_t heads_q, int64_t seqlen_q);
 hipError_t launch_attn_bwd(const AttnBwdArgs &a, hipStream_t s);
 
@@ -66,7 +71,7 @@ hipError_t launch_attn_bwd(const AttnBwdArgs &a, hipStream_t s);
 struct DecodeLayout {
     int64_t rows;        // batch * heads_q
     int32_t chunks;      // C = ceil(max_seqlen_k / split)
-    size_t off_m, off_l, off_o, total;
+    size_t off_m, off_l, off_o, total;   // total = 0: the workspace would exceed 2^62 bytes
 };
 DecodeLayout decode_layout(int64_t batch, int64_t heads_q, int64_t max_seqlen_k, int64_t head_dim,
                            int64_t split);

@@ -18,9 +18,11 @@
 //    m) / l.  HBM traffic: one load and one store per element (8 B).
 //
 //  * streaming (any cols): pass 1 reads the row and runs the recurrence per
-//    lane, one rescale per float4 vector; lane summaries are merged as above;
-//    pass 2 reads the row again and writes y = exp(x - m) / l.  HBM traffic:
-//    two loads and one store per element (12 B), the pages' count.
+//    lane, one rescale per batch of four float4 vectors; lane summaries are
+//    merged as above; pass 2 reads the row again and writes
+//    y = exp(x - m) / l.  Memory accesses: two loads and one store per
+//    element (12 B), the pages' count.  Used for rows too long to hold, and
+//    for every row through osm_softmax_rows_twopass.
 #include "osm_device.h"
 #include "osm_internal.h"
 
@@ -211,6 +213,34 @@ softmax_rows_resident_whole(const float *x, float *y, int64_t rows, int64_t cols
     }
 }
 
+// ---- the streaming two-pass kernel (any width) ------------------------------
+// Pass 1 runs the recurrence of [P3] "The recurrence, and a proof that it is
+// right" per lane, one batch of kStreamU vectors (4 kStreamU elements) per
+// step: the batch maximum bm moves the lane's reference once, l is rescaled
+// by e^(m - bm) and the batch's e^(x - bm) are added (the rescale is paid
+// once per batch, not per element).  Every exponential is exp_acc of an fp32
+// difference: the difference is the only rounding before the exponent, so l
+// keeps about one fp32 rounding per term.  No branch is needed around an
+// empty batch or a lane that has seen nothing: exp_acc maps -inf, and the
+// NaN of -inf - (-inf), to 0, so such a step leaves (m, l) = (-inf, 0).
+// Pass 2 reads the row again and writes y = e^(x - m) / l.
+constexpr int kStreamU = kSoftmaxStreamBatch;
+
+__device__ __forceinline__ void fold_batch(float &m, float &l, const float4 (&v)[kStreamU]) {
+    float bm = m;
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u) bm = fmaxf(bm, max4(v[u]));
+    float s = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u)
+        s += (exp_acc(v[u].x - bm) + exp_acc(v[u].y - bm)) + (exp_acc(v[u].z - bm) + exp_acc(v[u].w - bm));
+    l = fmaf(l, exp_acc(m - bm), s);
+    m = bm;
+}
+
+// Rows of any width and alignment (ALIGNED: 16-byte aligned rows).  Vectors
+// past the row read as -inf.  Pass 1 loads are cached, so that pass 2 may
+// find the row still on chip; pass 2 loads and the stores are nontemporal.
 template <bool ALIGNED>
 __global__ void __launch_bounds__(1024)
 softmax_rows_streaming(const float *x, float *y, int64_t rows,
@@ -218,37 +248,95 @@ softmax_rows_streaming(const float *x, float *y, int64_t rows,
                        float *__restrict__ row_sum) {
     __shared__ float sm[kMaxWaves], sl[kMaxWaves];
     const int64_t nvec = (cols + 3) / 4;
+    const int64_t step = (int64_t)blockDim.x * kStreamU;
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
         const float *xr = x + r * ld_x;
-        // pass 1: the recurrence over this lane's vectors, one rescale per vector
         float m = kNegInf, l = 0.0f;
-        for (int64_t vec = threadIdx.x; vec < nvec; vec += blockDim.x) {
-            float4 v = load_vec<ALIGNED>(xr, vec, cols);
-            float mn = fmaxf(m, max4(v));
-            if (mn == kNegInf) continue;          // nothing visible yet
-            float alpha = (m == kNegInf) ? 0.0f : exp_acc(m - mn);
-            float ms = mn * kLog2e;
-            float s = fast_exp2(fmaf(v.x, kLog2e, -ms)) + fast_exp2(fmaf(v.y, kLog2e, -ms)) +
-                      fast_exp2(fmaf(v.z, kLog2e, -ms)) + fast_exp2(fmaf(v.w, kLog2e, -ms));
-            l = fmaf(l, alpha, s);
-            m = mn;
+        for (int64_t v0 = threadIdx.x; v0 < nvec; v0 += step) {
+            float4 v[kStreamU];
+#pragma unroll
+            for (int u = 0; u < kStreamU; ++u) {
+                const int64_t vec = v0 + (int64_t)u * blockDim.x;
+                v[u] = (vec < nvec) ? load_vec<ALIGNED>(xr, vec, cols)
+                                    : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+            }
+            fold_batch(m, l, v);
         }
         block_merge_ml(m, l, sm, sl);
-        // pass 2: read again, write y = exp(x - m) / l
         const float inv_l = (m == kNegInf) ? 0.0f : 1.0f / l;
         float *yr = y + r * ld_y;
-        for (int64_t vec = threadIdx.x; vec < nvec; vec += blockDim.x) {
-            float4 v = load_vec<ALIGNED>(xr, vec, cols);
-            float4 o;
-            if (m == kNegInf) {
-                o = make_float4(0.f, 0.f, 0.f, 0.f);
-            } else {
-                o.x = exp_acc(v.x - m) * inv_l;
-                o.y = exp_acc(v.y - m) * inv_l;
-                o.z = exp_acc(v.z - m) * inv_l;
-                o.w = exp_acc(v.w - m) * inv_l;
+        for (int64_t v0 = threadIdx.x; v0 < nvec; v0 += step) {
+            float4 v[kStreamU];
+#pragma unroll
+            for (int u = 0; u < kStreamU; ++u) {
+                const int64_t vec = v0 + (int64_t)u * blockDim.x;
+                if (vec < nvec) v[u] = load_vec_once<ALIGNED>(xr, vec, cols);
             }
-            store_vec<ALIGNED>(yr, vec, cols, o);
+#pragma unroll
+            for (int u = 0; u < kStreamU; ++u) {
+                const int64_t vec = v0 + (int64_t)u * blockDim.x;
+                if (vec < nvec) {
+                    const float4 o = make_float4(exp_acc(v[u].x - m) * inv_l, exp_acc(v[u].y - m) * inv_l,
+                                                 exp_acc(v[u].z - m) * inv_l, exp_acc(v[u].w - m) * inv_l);
+                    store_vec<ALIGNED>(yr, vec, cols, o);
+                }
+            }
+        }
+        if (threadIdx.x == 0) {
+            if (row_max) row_max[r] = m;
+            if (row_sum) row_sum[r] = l;
+        }
+    }
+}
+
+// The streaming kernel for 16-byte aligned rows whose width is a multiple
+// of four (and below 2^29 elements): loads and stores go through a buffer
+// resource spanning exactly the row, so a vector past the end loads zeros
+// (set to -inf by a select) and its store is dropped, with no per-vector
+// branch.  Each access carries its whole byte offset in the VGPR offset,
+// which is what the range check covers.
+__global__ void __launch_bounds__(1024)
+softmax_rows_streaming_whole(const float *x, float *y, int64_t rows, int64_t cols, int64_t ld_x,
+                             int64_t ld_y, float *__restrict__ row_max, float *__restrict__ row_sum) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    __shared__ float sm[kMaxWaves], sl[kMaxWaves];
+    const uint32_t bytes = (uint32_t)(cols * 4);
+    const uint32_t stride = blockDim.x * 16u, step = stride * kStreamU;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const __amdgpu_buffer_rsrc_t xr =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(x + r * ld_x), 0, (int)bytes, kRsrcWord3);
+        float m = kNegInf, l = 0.0f;
+        for (uint32_t o0 = threadIdx.x * 16u; o0 < bytes; o0 += step) {
+            float4 v[kStreamU];
+#pragma unroll
+            for (int u = 0; u < kStreamU; ++u) {
+                const uint32_t off = o0 + u * stride;
+                const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+                const bool in = off < bytes;
+                v[u].x = in ? __uint_as_float(w[0]) : kNegInf;
+                v[u].y = in ? __uint_as_float(w[1]) : kNegInf;
+                v[u].z = in ? __uint_as_float(w[2]) : kNegInf;
+                v[u].w = in ? __uint_as_float(w[3]) : kNegInf;
+            }
+            fold_batch(m, l, v);
+        }
+        block_merge_ml(m, l, sm, sl);
+        const float inv_l = (m == kNegInf) ? 0.0f : 1.0f / l;
+        const __amdgpu_buffer_rsrc_t yr =
+            __builtin_amdgcn_make_buffer_rsrc(y + r * ld_y, 0, (int)bytes, kRsrcWord3);
+        for (uint32_t o0 = threadIdx.x * 16u; o0 < bytes; o0 += step) {
+            u32x4 w[kStreamU];
+#pragma unroll
+            for (int u = 0; u < kStreamU; ++u)
+                w[u] = __builtin_amdgcn_raw_buffer_load_b128(xr, o0 + u * stride, 0, kAuxNontemporal);
+#pragma unroll
+            for (int u = 0; u < kStreamU; ++u) {
+                const u32x4 o = {__float_as_uint(exp_acc(__uint_as_float(w[u][0]) - m) * inv_l),
+                                 __float_as_uint(exp_acc(__uint_as_float(w[u][1]) - m) * inv_l),
+                                 __float_as_uint(exp_acc(__uint_as_float(w[u][2]) - m) * inv_l),
+                                 __float_as_uint(exp_acc(__uint_as_float(w[u][3]) - m) * inv_l)};
+                __builtin_amdgcn_raw_buffer_store_b128(o, yr, o0 + u * stride, 0, kAuxNontemporal);
+            }
         }
         if (threadIdx.x == 0) {
             if (row_max) row_max[r] = m;
@@ -278,39 +366,6 @@ hipError_t launch_resident_mode(const SoftmaxArgs &a, int mode, int threads, int
 
 }  // namespace
 
-// Plan: the row lives in registers when it fits in 16 float4 per lane of a
-// workgroup of at most 1024 threads.  Rows of more than 4096 vectors take 16
-// vectors per lane and the fewest threads (measured on MI355X for 32000
-// columns: 512 threads x 16 vectors reaches 69% of HBM peak, 1024 x 8 59%);
-// shorter rows take the smallest power-of-two workgroup that holds them.
-// Longer rows take the streaming two-pass kernel.
-SoftmaxPlan plan_softmax_rows(int64_t cols, int force_variant) {
-    SoftmaxPlan p{};
-    const int64_t nvec = (cols + 3) / 4;
-    if (force_variant != 1 && nvec <= 16 * 1024) {
-        p.resident = true;
-        if (nvec > 4096) {
-            p.nv = 16;
-            p.threads = 256;
-            while ((int64_t)p.threads * 16 < nvec) p.threads *= 2;
-            return p;
-        }
-        for (int nv : {4, 8, 16}) {
-            for (int t = 64; t <= 1024; t *= 2) {
-                if ((int64_t)t * nv >= nvec) {
-                    p.nv = nv;
-                    p.threads = t;
-                    return p;
-                }
-            }
-        }
-    }
-    p.resident = false;
-    p.nv = 0;
-    p.threads = 1024;
-    return p;
-}
-
 hipError_t launch_softmax_rows(const SoftmaxArgs &a, const SoftmaxPlan &p, hipStream_t s) {
     if (a.rows == 0) return hipSuccess;
     const bool aligned = ((reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.y)) % 16 == 0) &&
@@ -325,7 +380,11 @@ hipError_t launch_softmax_rows(const SoftmaxArgs &a, const SoftmaxPlan &p, hipSt
             default: return launch_resident_mode<16>(a, mode, p.threads, grid, s);
         }
     }
-    if (aligned)
+    // whole-vector rows whose byte offsets (plus one batch) stay below 2^31
+    if (aligned && a.cols % 4 == 0 && a.cols < ((int64_t)1 << 28))
+        hipLaunchKernelGGL(softmax_rows_streaming_whole, dim3(grid), dim3(p.threads), 0, s, a.x, a.y,
+                           a.rows, a.cols, a.ld_x, a.ld_y, a.row_max, a.row_sum);
+    else if (aligned)
         hipLaunchKernelGGL((softmax_rows_streaming<true>), dim3(grid), dim3(p.threads), 0, s, a.x,
                            a.y, a.rows, a.cols, a.ld_x, a.ld_y, a.row_max, a.row_sum);
     else

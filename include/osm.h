@@ -90,6 +90,24 @@ osm_status osm_softmax_rows(const float *x, float *y, int64_t rows, int64_t cols
                             osm_stream stream);
 
 /*
+ * osm_softmax_rows_twopass -- osm_softmax_rows computed exactly as the
+ * pages count it: two passes over the row in memory.
+ *
+ * [P3] "Three passes, and why that is a problem" and "The recurrence, and a
+ * proof that it is right": pass 1 reads the row once and keeps the running
+ * (m, l), pass 2 reads it again and writes y, three memory accesses per
+ * element (against four for the three-pass safe softmax).  osm_softmax_rows
+ * holds rows of up to 65536 columns on chip and reads them once; this entry
+ * point always re-reads, for any width.  Within a row each lane runs the
+ * recurrence over its share of the elements and the lanes' (m, l) are
+ * merged ([P3] "Merging partial results").
+ * Arguments, results, special cases and errors: as osm_softmax_rows.
+ */
+osm_status osm_softmax_rows_twopass(const float *x, float *y, int64_t rows, int64_t cols,
+                                    int64_t ld_x, int64_t ld_y, float *row_max, float *row_sum,
+                                    osm_stream stream);
+
+/*
  * osm_attn_fwd -- fused exact attention forward, O = softmax(scale * Q K^T) V,
  * plus the per-query log-sum-exp.
  *
@@ -269,9 +287,10 @@ osm_status osm_attn_decode_splitkv(const void *q, const void *k_cache, const voi
  *
  * [P3] "Merging partial results": with m = max(m_A, m_B),
  * l = l_A exp(m_A - m) + l_B exp(m_B - m) and O~ likewise; the empty set
- * (-inf, 0, 0) is the identity and is skipped (its l and O~ are not read,
- * so they may hold any bits).  Then o = O~ / l and LSE = m + log l
- * ([P3] "From weights to outputs").
+ * (-inf, 0, 0) is the identity and drops out: its l and O~ are loaded with
+ * the other pieces but weighted out by a select, so they may hold any bits
+ * (NaN included), though their memory must be valid.  Then o = O~ / l and
+ * LSE = m + log l ([P3] "From weights to outputs").
  *
  *   part_m  fp32 [rows][num_splits]  piece maxima (natural-log units of the
  *           scaled scores); -inf marks an empty piece
@@ -346,9 +365,12 @@ osm_status osm_attn_extend(const void *q, const void *k_new, const void *v_new, 
  *   lse        fp32 [rows] (written; may be NULL)
  * A row whose pieces are all empty gives o = 0, LSE = -inf.
  * Supported: in_dtype and out_dtype OSM_F32 or OSM_BF16; head_dim 1..1024
- * (even) or 1..511 (odd); num_parts >= 1.  fp32 accumulation.
+ * (even) or 1..511 (odd); num_parts >= 1; o_parts and o 16-byte aligned
+ * (they are read and written in vectors of up to 16 bytes).  fp32
+ * accumulation.
  * Errors: OSM_ERR_NULL, OSM_ERR_SHAPE (rows < 0, num_parts < 1,
- * head_dim < 1), OSM_ERR_UNSUPPORTED, OSM_ERR_HIP.
+ * head_dim < 1), OSM_ERR_UNSUPPORTED (other dtype or head_dim, o_parts or o
+ * not 16-byte aligned), OSM_ERR_HIP.
  */
 osm_status osm_merge_lse(const void *o_parts, const float *lse_parts, int64_t rows,
                          int32_t num_parts, int32_t head_dim, osm_dtype in_dtype, void *o,

@@ -14,7 +14,23 @@ HEADER = os.path.join(ROOT, "include", "osm.h")
 FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation
 
 
+def _hip_device_count():
+    """Devices the HIP runtime itself sees (0 when it reports none, or on any
+    error: libosm.so links the same runtime, so a launch fails there too)."""
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return 0
+    n = ctypes.c_int(0)
+    err = hip.hipGetDeviceCount(ctypes.byref(n))
+    return n.value if err == 0 else 0
+
+
 def _has_gpu():
+    """True when either the HIP runtime or torch sees a device: the
+    fake-pointer tests below must never reach a launch on a real GPU."""
+    if _hip_device_count() > 0:
+        return True
     try:
         import torch
         return torch.cuda.device_count() > 0
@@ -64,6 +80,14 @@ def test_softmax_validation(lib):
     assert lib.osm_softmax_rows(None, FAKE, 2, 4, 4, 4, None, None, s) == 1
     assert lib.osm_softmax_rows(FAKE, None, 2, 4, 4, 4, None, None, s) == 1
     assert lib.osm_softmax_rows(None, None, 0, 4, 4, 4, None, None, s) == 0     # nothing to do
+    f = lib.osm_softmax_rows_twopass
+    assert f(FAKE, FAKE, -1, 4, 4, 4, None, None, s) == 2
+    assert f(FAKE, FAKE, 2, 4, 3, 4, None, None, s) == 2
+    assert f(FAKE, FAKE, 2, 4, 4, 3, None, None, s) == 2
+    assert f(None, FAKE, 2, 4, 4, 4, None, None, s) == 1
+    assert f(FAKE, None, 2, 4, 4, 4, None, None, s) == 1
+    assert f(None, None, 0, 4, 4, 4, None, None, s) == 0
+    assert f(None, None, 3, 0, 0, 0, None, None, s) == 0                       # no columns, no stats
 
 
 @no_gpu_only
@@ -85,7 +109,9 @@ def test_attn_fwd_validation(lib):
     assert call(q=None) == 1
     assert call(o=None) == 1
     assert call(k=None) == 1
-    assert call(k=None, v=None, Nk=0) != 1          # no keys: k/v may be NULL
+    # no keys: k and v may be NULL (the request then fails only at the
+    # alignment check that follows the NULL check, before any launch)
+    assert call(k=None, v=None, Nk=0, o=ctypes.c_void_p(0x10008)) == 3
     assert call(q=None, Nq=0) == 0                  # nothing to compute
     assert call(q=ctypes.c_void_p(0x10002)) == 3    # not 16-byte aligned
     assert call(o=ctypes.c_void_p(0x10008)) == 3
@@ -148,6 +174,8 @@ def test_merge_lse_validation(lib):
     assert call(lp=None) == 1
     assert call(o=None) == 1
     assert call(op=None, rows=0) == 0
+    assert call(op=ctypes.c_void_p(0x10008)) == 3    # pieces not 16-byte aligned
+    assert call(o=ctypes.c_void_p(0x10004)) == 3     # output not 16-byte aligned
 
 
 @no_gpu_only

@@ -108,3 +108,38 @@ def test_merge_bf16_out(orc):
     o_ref, lse_ref = orc.merge(pm, pl, po)
     assert np.abs(host(o) - o_ref).max() <= 2e-2
     assert np.abs(host(lse) - lse_ref).max() <= 1e-3
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_every_split_instantiation(orc, dtype, d, group):
+    """Each (element type, head_dim, heads per KV head) instantiation of the
+    piece kernel, through decode (ragged lengths, NaN past them, an empty
+    sequence, 192-key pieces so the last piece of a row is partial) and
+    through extend (two chunks into a fresh state, 128-key pieces)."""
+    announce(f"decode/extend instantiation {dtype} d={d} group={group}")
+    hkv = 2
+    hq = hkv * group
+    lens = np.array([0, 1, 333, 700], np.int32)
+    inp = inputs.attention_inputs(4, hq, hkv, 1, 700, d, seed=900 + 10 * d + group + (dtype == "f32"),
+                                  dtype=dtype, seqlens_k=lens, poison=True)
+    o, lse = run_decode(inp, 192)
+    o_ref, lse_ref = oracle_decode(orc, inp)
+    check_attn(host(o), host(lse), o_ref, lse_ref, dtype)
+
+    torch = __import__("torch")
+    e_inp = inputs.attention_inputs(2, hq, hkv, 1, 450, d, seed=950 + 10 * d + group, dtype=dtype)
+    q = dev_input(e_inp.q[:, :, 0, :], dtype)
+    k = dev_input(e_inp.k, dtype)
+    v = dev_input(e_inp.v, dtype)
+    state = osm.attn_state(2, hq, d)
+    osm.attn_extend(q, k[:, :, :130].contiguous(), v[:, :, :130].contiguous(), state, scale=e_inp.scale,
+                    split_size=128)
+    osm.attn_extend(q, k[:, :, 130:].contiguous(), v[:, :, 130:].contiguous(), state, scale=e_inp.scale,
+                    split_size=128)
+    oe, le = osm.attn_state_finalize(state)
+    torch.cuda.synchronize()
+    qw, kw, vw = e_inp.widened()
+    oe_ref, le_ref = orc.attention(qw, kw, vw, scale=e_inp.scale)
+    check_attn(host(oe), host(le), oe_ref.reshape(-1, d), le_ref.reshape(-1), dtype)
