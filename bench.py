@@ -117,8 +117,8 @@ def achievable(torch):
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "exact_attention_online_softmax_amd", "libosm_probe.so"))
     vp = ctypes.c_void_p
-    lib.osmprobe_copy.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
-    lib.osmprobe_mfma_bf16.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp]
+    lib.osmprobe_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+    lib.osmprobe_mfma_bf16.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     stream = vp(torch.cuda.current_stream().cuda_stream)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
 
@@ -135,19 +135,23 @@ def achievable(torch):
     nbytes = 1 << 30
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    t_copy = timed(lambda: lib.osmprobe_copy(vp(src.data_ptr()), vp(dst.data_ptr()), nbytes, 8 * cus, stream))
+    t_copy = timed(lambda: lib.osmprobe_copy(vp(src.data_ptr()), vp(dst.data_ptr()), nbytes, stream))
     del src, dst
-    grid, iters = cus, 4096
+    res = {"copy_GBps": round(2 * nbytes / t_copy / 1e9, 1),
+           "copy": "1 GiB streaming copy (nontemporal 16-byte loads and stores, 32 KiB per workgroup), "
+                   "bytes read + written"}
     g = np.random.default_rng(12345)
-    ops = torch.from_numpy(g.standard_normal(grid * 256 * 128, dtype=np.float32)).to("cuda").to(torch.bfloat16)
-    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
-    t_mfma = timed(lambda: lib.osmprobe_mfma_bf16(vp(ops.data_ptr()), vp(out.data_ptr()), grid, iters, stream))
-    flops = grid * 4 * iters * 8 * 32768.0
-    return {"copy_GBps": round(2 * nbytes / t_copy / 1e9, 1),
-            "copy": "1 GiB streaming copy (nontemporal 16-byte loads and stores), bytes read + written",
-            "mfma_bf16_TFLOPs": round(flops / t_mfma / 1e12, 1),
-            "mfma": f"v_mfma_f32_32x32x16_bf16 chains on N(0,1) operands, {grid} workgroups x 4 waves, "
-                    f"no memory traffic in the loop"}
+    grid, iters = cus, 4096
+    ops = torch.from_numpy(g.standard_normal(grid * 512 * 128, dtype=np.float32)).to("cuda").to(torch.bfloat16)
+    out = torch.empty(grid * 512, dtype=torch.float32, device="cuda")
+    for threads in (256, 512):
+        t = timed(lambda: lib.osmprobe_mfma_bf16(vp(ops.data_ptr()), vp(out.data_ptr()), grid, threads, iters,
+                                                 stream))
+        res[f"mfma_bf16_TFLOPs_{threads // 256}wave_per_simd"] = round(grid * threads // 64 * iters * 8 * 32768.0
+                                                                       / t / 1e12, 1)
+    res["mfma"] = (f"v_mfma_f32_32x32x16_bf16 chains (4 accumulators per wave) on N(0,1) operands, {grid} "
+                   f"workgroups of 4 or 8 waves, no memory traffic in the loop")
+    return res
 
 
 def cpu_baseline(inp, seconds):

@@ -49,6 +49,12 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with "
                           "`python -m exact_attention_online_softmax_amd.build`")
+    # torch first: its HIP runtime then satisfies libosm.so's dependency on
+    # libamdhip64.so.7, so the library and the tensors and streams it is given
+    # share one runtime.  Loaded the other way round, the process would hold
+    # two runtime instances, and the library's would not see torch's device
+    # memory or streams.
+    _torch()
     lib = ctypes.CDLL(path)
     vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
     lib.osm_status_str.argtypes = [ctypes.c_int]

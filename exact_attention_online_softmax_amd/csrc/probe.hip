@@ -4,7 +4,7 @@
 // osm C ABI, used by the benchmark only):
 //
 //  * osmprobe_copy: a streaming device copy, 16 bytes per lane per access,
-//    nontemporal loads and stores, grid-stride over the buffer.  Its
+//    nontemporal loads and stores, one sweep of 32 KiB per workgroup.  Its
 //    GB/s (bytes read + bytes written per second) is the practical HBM
 //    ceiling of a read-and-write stream.
 //  * osmprobe_mfma_bf16: independent chains of v_mfma_f32_32x32x16_bf16 on
@@ -22,29 +22,26 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Workgroup w copies vectors [2048 w, 2048 (w + 1)) of the buffer: eight
+// 16-byte vectors per lane, all loads issued before the stores, so each
+// workgroup makes one sweep with 32 KiB in flight.
 __global__ void __launch_bounds__(256) copy_nt(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
                                                size_t n) {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    // four independent vectors per lane per step
-    for (; i + 3 * stride < n; i += 4 * stride) {
-        const u32x4 a = __builtin_nontemporal_load(src + i);
-        const u32x4 b = __builtin_nontemporal_load(src + i + stride);
-        const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
-        const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
-        __builtin_nontemporal_store(a, dst + i);
-        __builtin_nontemporal_store(b, dst + i + stride);
-        __builtin_nontemporal_store(c, dst + i + 2 * stride);
-        __builtin_nontemporal_store(d, dst + i + 3 * stride);
-    }
-    for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+    const size_t base = (size_t)blockIdx.x * 2048 + threadIdx.x;
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+        if (base + 256 * u < n) v[u] = __builtin_nontemporal_load(src + base + 256 * u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+        if (base + 256 * u < n) __builtin_nontemporal_store(v[u], dst + base + 256 * u);
 }
 
 // Each lane loads eight A and eight B operand fragments (16 bf16 vectors);
 // iteration i of the inner loop multiplies A fragment i with B fragment
 // (i + 3) % 8 into accumulator i % 4.  The sum of the accumulators is stored
 // so that nothing is optimized away.
-__global__ void __launch_bounds__(256) mfma_loop(const bf16x8 *__restrict__ ops, float *__restrict__ out,
+__global__ void __launch_bounds__(512) mfma_loop(const bf16x8 *__restrict__ ops, float *__restrict__ out,
                                                  int iters) {
     const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     bf16x8 a[8], b[8];
@@ -72,22 +69,28 @@ __global__ void __launch_bounds__(256) mfma_loop(const bf16x8 *__restrict__ ops,
 extern "C" {
 
 // Copy `bytes` (a multiple of 16; both pointers 16-byte aligned) from src to
-// dst on `stream` with `grid` workgroups of 256 threads.  Returns a
+// dst on `stream`, 32 KiB per workgroup of 256 threads.  Returns a
 // hipError_t value (0 = launched).
-int osmprobe_copy(const void *src, void *dst, size_t bytes, int grid, void *stream) {
-    if (bytes % 16 || (reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 || grid < 1)
+int osmprobe_copy(const void *src, void *dst, size_t bytes, void *stream) {
+    if (bytes % 16 || (reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 ||
+        bytes / 32768 >= (size_t)1 << 31)
         return (int)hipErrorInvalidValue;
+    const size_t n = bytes / 16;
+    const unsigned grid = (unsigned)((n + 2047) / 2048);
+    if (grid == 0) return 0;
     hipLaunchKernelGGL(copy_nt, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
-                       static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), bytes / 16);
+                       static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), n);
     return (int)hipGetLastError();
 }
 
-// `grid` workgroups of 256 threads, each thread running `iters` x 8 MFMAs of
-// 32x32x16 (32768 flops per wave each).  `ops` holds grid * 256 * 16 bf16x8
-// fragments (grid * 256 * 256 bytes); `out` grid * 256 floats.
-int osmprobe_mfma_bf16(const void *ops, float *out, int grid, int iters, void *stream) {
-    if (grid < 1 || iters < 1 || (reinterpret_cast<uintptr_t>(ops) % 16)) return (int)hipErrorInvalidValue;
-    hipLaunchKernelGGL(mfma_loop, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+// `grid` workgroups of `threads` (256 or 512: one or two waves per SIMD)
+// threads, each thread running `iters` x 8 MFMAs of 32x32x16 (32768 flops per
+// wave each).  `ops` holds grid * threads * 16 bf16x8 fragments
+// (grid * threads * 256 bytes); `out` grid * threads floats.
+int osmprobe_mfma_bf16(const void *ops, float *out, int grid, int threads, int iters, void *stream) {
+    if (grid < 1 || iters < 1 || (threads != 256 && threads != 512) || (reinterpret_cast<uintptr_t>(ops) % 16))
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(mfma_loop, dim3(grid), dim3(threads), 0, static_cast<hipStream_t>(stream),
                        static_cast<const bf16x8 *>(ops), out, iters);
     return (int)hipGetLastError();
 }

@@ -15,10 +15,16 @@ FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails v
 
 
 def _hip_device_count():
-    """Devices the HIP runtime itself sees (0 when it reports none, or on any
-    error: libosm.so links the same runtime, so a launch fails there too)."""
+    """Devices that the HIP runtime libosm.so is bound to sees (0 when it
+    reports none, or on any error).  The runtime is the instance already
+    mapped into this process (loading the library loads it), so no second
+    instance is started."""
     try:
-        hip = ctypes.CDLL("libamdhip64.so")
+        osm.load_library()
+        path = next((ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln), None)
+        if path is None:
+            return 0
+        hip = ctypes.CDLL(path)
     except OSError:
         return 0
     n = ctypes.c_int(0)
