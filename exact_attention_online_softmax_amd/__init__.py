@@ -29,7 +29,8 @@ STATUS = {0: "OSM_OK", 1: "OSM_ERR_NULL", 2: "OSM_ERR_SHAPE", 3: "OSM_ERR_UNSUPP
           4: "OSM_ERR_WORKSPACE", 5: "OSM_ERR_HIP"}
 EXPORTS = ("osm_status_str", "osm_softmax_rows", "osm_softmax_rows_twopass", "osm_attn_fwd", "osm_decode_workspace_bytes",
            "osm_attn_decode_splitkv", "osm_merge_partials", "osm_merge_lse", "osm_attn_extend",
-           "osm_attn_bwd_workspace_bytes", "osm_attn_bwd", "osm_attn_fwd_fp8")
+           "osm_attn_bwd_workspace_bytes", "osm_attn_bwd", "osm_attn_fwd_fp8",
+           "osm_attn_decode_splitkv_noalloc")
 
 
 class OsmError(RuntimeError):
@@ -67,6 +68,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.osm_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.osm_attn_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i32, i32, i32, i32,
                                             i32, vp, f32, i32, vp, ctypes.c_size_t, vp]
+    lib.osm_attn_decode_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i32, i32, i32, i32,
+                                                    i32, vp, f32, i32, vp]
     lib.osm_merge_partials.argtypes = [vp, vp, vp, i64, i32, i32, vp, ctypes.c_int, vp, vp]
     lib.osm_merge_lse.argtypes = [vp, vp, i64, i32, i32, ctypes.c_int, vp, ctypes.c_int, vp, vp]
     lib.osm_attn_extend.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32, f32, vp, vp, vp,
@@ -79,7 +82,7 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
                                  i32, i32, vp, vp, f32, i32, vp, ctypes.c_size_t, vp]
     for name in ("osm_softmax_rows", "osm_softmax_rows_twopass", "osm_attn_fwd", "osm_attn_decode_splitkv",
                  "osm_merge_partials", "osm_merge_lse", "osm_attn_extend", "osm_attn_bwd",
-                 "osm_attn_fwd_fp8"):
+                 "osm_attn_fwd_fp8", "osm_attn_decode_splitkv_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

@@ -176,6 +176,39 @@ osm_status osm_attn_decode_splitkv(const void *q, const void *k_cache, const voi
     return hip_status(osm::launch_merge_partials(m, s));
 }
 
+osm_status osm_attn_decode_splitkv_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                           void *o, float *lse, osm_dtype dtype, int32_t batch,
+                                           int32_t heads_q, int32_t heads_kv, int32_t max_seqlen_k,
+                                           int32_t head_dim, const int32_t *seqlens_k, float scale,
+                                           int32_t split_size, osm_stream stream) {
+    if (batch < 1 || heads_q < 1 || heads_kv < 1 || max_seqlen_k < 1 || head_dim < 1 ||
+        heads_q % heads_kv != 0 || !(scale > 0.0f) || !isfinite(scale) || split_size < 1)
+        return OSM_ERR_SHAPE;
+    const int group = heads_q / heads_kv;
+    if ((dtype != OSM_F32 && dtype != OSM_BF16) || (head_dim != 64 && head_dim != 128) ||
+        (group != 1 && group != 2 && group != 4 && group != 8) || split_size % 64 != 0 ||
+        split_size > 8192 || (int64_t)group * split_size > kMaxDecodeScores ||
+        too_many_heads(batch, heads_q))
+        return OSM_ERR_UNSUPPORTED;
+    if (!q || !k_cache || !v_cache || !o || !seqlens_k) return OSM_ERR_NULL;
+    if (misaligned16(q) || misaligned16(k_cache) || misaligned16(v_cache)) return OSM_ERR_UNSUPPORTED;
+    const osm::DecodeLayout lay = osm::decode_layout(batch, heads_q, max_seqlen_k, head_dim, split_size);
+    // the partials must fit the library's scratch array (OSM_DECODE_SCRATCH_BYTES)
+    if (lay.total == 0 || lay.total > osm::kDecodeScratchBytes) return OSM_ERR_WORKSPACE;
+    void *workspace = nullptr;
+    if (osm::decode_scratch(&workspace) != hipSuccess) return OSM_ERR_HIP;
+    osm::DecodeArgs a{q, k_cache, v_cache, o, lse, dtype == OSM_BF16 ? 1 : 0, batch, heads_q,
+                      heads_kv, max_seqlen_k, head_dim, seqlens_k, scale, split_size, workspace};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (osm::launch_decode_split(a, lay, s) != hipSuccess) return OSM_ERR_HIP;
+    const char *ws = static_cast<const char *>(workspace);
+    osm::MergeArgs m{reinterpret_cast<const float *>(ws + lay.off_m),
+                     reinterpret_cast<const float *>(ws + lay.off_l),
+                     reinterpret_cast<const float *>(ws + lay.off_o),
+                     lay.rows, lay.chunks, head_dim, o, a.dtype, lse};
+    return hip_status(osm::launch_merge_partials(m, s));
+}
+
 osm_status osm_merge_partials(const float *part_m, const float *part_l, const float *part_o,
                               int64_t rows, int32_t num_splits, int32_t head_dim, void *o,
                               osm_dtype out_dtype, float *lse, osm_stream stream) {

@@ -29,10 +29,19 @@
 // an empty piece's l and O~ are loaded with the others but dropped by a
 // select, so whatever they hold (NaN included) never reaches a sum.  Then
 // o = O~ / l once and LSE = m + log l ([P3] "From weights to outputs").
+#include <mutex>
+
 #include "osm_device.h"
 #include "osm_internal.h"
 
 namespace osm {
+
+// The decode workspace of osm_attn_decode_splitkv_noalloc: one copy per GPU,
+// allocated by the runtime when the library's code object is loaded there and
+// held until the process ends.  Host code never passes `scratch` itself to a
+// kernel (on the host the name is only a stand-in): decode_scratch() looks up
+// each device's own address once and every launch uses that.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
 
 namespace {
 
@@ -396,6 +405,26 @@ hipError_t launch_split_g(const DecodeArgs &a, const DecodeLayout &lay, hipStrea
 }
 
 }  // namespace
+
+hipError_t decode_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        // with `dev` current: this device's copy of the array
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_decode_split(const DecodeArgs &a, const DecodeLayout &lay, hipStream_t s) {
     if (a.dtype == 1)

@@ -89,6 +89,13 @@ struct DecodeArgs {
 };
 hipError_t launch_decode_split(const DecodeArgs &a, const DecodeLayout &lay, hipStream_t s);
 
+// The decode workspace held by the library for callers that cannot allocate:
+// kDecodeScratchBytes of device memory per GPU (a file-scope device array in
+// decode.hip), shared by every call on that GPU.  decode_scratch() returns its
+// address on the current device, looked up once per device.
+constexpr size_t kDecodeScratchBytes = (size_t)64 << 20;
+hipError_t decode_scratch(void **ptr);
+
 struct MergeArgs {
     const float *part_m, *part_l, *part_o;
     int64_t rows;

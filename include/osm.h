@@ -11,8 +11,10 @@
  * ---------------------------------------
  * - Every data pointer is DEVICE memory owned by the caller (for example a
  *   PyTorch tensor's data_ptr()).  The library never allocates, frees or
- *   retains memory, keeps no global mutable state and is safe to call from
- *   several host threads.
+ *   retains memory and is safe to call from several host threads.  Its only
+ *   global state is the per-GPU scratch array of
+ *   osm_attn_decode_splitkv_noalloc (reserved with the library's code, see
+ *   there) and the table of its addresses.
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *   runs asynchronously.  Outputs are valid after the stream is synchronized.
  *   Faults inside a kernel surface at the caller's next synchronization.
@@ -280,6 +282,38 @@ osm_status osm_attn_decode_splitkv(const void *q, const void *k_cache, const voi
                                    int32_t head_dim, const int32_t *seqlens_k, float scale,
                                    int32_t split_size, void *workspace, size_t workspace_bytes,
                                    osm_stream stream);
+
+/*
+ * osm_attn_decode_splitkv_noalloc -- osm_attn_decode_splitkv without a
+ * caller-supplied workspace, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, and harnesses that
+ * forbid allocation.  Neither this call nor anything it calls allocates or
+ * frees memory.
+ *
+ * The piece summaries go to a scratch array the library holds on each GPU:
+ * OSM_DECODE_SCRATCH_BYTES (64 MiB) of device memory, reserved when the
+ * library's code is loaded on that GPU and kept until the process ends.  Its
+ * address on the current device is looked up on the first call there.  Every
+ * call on one GPU shares that array, so calls that overlap on one GPU (on
+ * different streams, or from different host threads without ordering) race
+ * and give wrong results: order them on one stream.  No part of the array
+ * needs clearing between calls: every summary the merge reads is written by
+ * the same call first (empty pieces' vectors included, which are weighted
+ * out).
+ *
+ * Arguments, semantics, results and errors: as osm_attn_decode_splitkv,
+ * except that there is no workspace, and OSM_ERR_WORKSPACE means that
+ * osm_decode_workspace_bytes() for these sizes exceeds
+ * OSM_DECODE_SCRATCH_BYTES (nothing is launched); OSM_ERR_HIP also covers a
+ * failed lookup of the array's address.  The kernels are the same, so the
+ * result is bit-identical to osm_attn_decode_splitkv's.
+ */
+#define OSM_DECODE_SCRATCH_BYTES ((size_t)64 << 20)
+osm_status osm_attn_decode_splitkv_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                           void *o, float *lse, osm_dtype dtype, int32_t batch,
+                                           int32_t heads_q, int32_t heads_kv, int32_t max_seqlen_k,
+                                           int32_t head_dim, const int32_t *seqlens_k, float scale,
+                                           int32_t split_size, osm_stream stream);
 
 /*
  * osm_merge_partials -- merge per-piece summaries of each row into the

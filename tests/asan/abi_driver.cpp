@@ -105,6 +105,20 @@ int main() {
     EXPECT(po + (size_t)512 * 128 * 128 * 4 <= w0 + dws);
     EXPECT(osm::g_merge.num_splits == 128 && osm::g_merge.head_dim == 128);
 
+    // ---- decode without a workspace: the library's scratch -----------------------
+    EXPECT(osm_attn_decode_splitkv_noalloc(P, P, P, P, F, OSM_BF16, 16, 32, 8, 32768, 128, LEN, 0.1f, 256,
+                                           nullptr) == OSM_OK);
+    EXPECT(reinterpret_cast<uintptr_t>(osm::g_merge.part_m) == 0x7000000);
+    EXPECT(reinterpret_cast<uintptr_t>(osm::g_merge.part_o) + (size_t)512 * 128 * 128 * 4 <=
+           0x7000000 + OSM_DECODE_SCRATCH_BYTES);
+    // 4 x the workspace above (136 MiB) does not fit the 64 MiB scratch
+    EXPECT(osm_attn_decode_splitkv_noalloc(P, P, P, P, F, OSM_BF16, 64, 32, 8, 32768, 128, LEN, 0.1f, 256,
+                                           nullptr) == OSM_ERR_WORKSPACE);
+    EXPECT(osm_attn_decode_splitkv_noalloc(P, P, P, P, F, OSM_BF16, 16, 32, 8, 32768, 128, nullptr, 0.1f, 256,
+                                           nullptr) == OSM_ERR_NULL);
+    EXPECT(osm_attn_decode_splitkv_noalloc(P, P, P, P, F, OSM_BF16, 16, 32, 8, 32768, 128, LEN, 0.1f, 100,
+                                           nullptr) == OSM_ERR_UNSUPPORTED);
+
     // ---- extend ------------------------------------------------------------------
     const size_t ews = osm_decode_workspace_bytes(16, 32, 4096, 128, 512);
     EXPECT(osm_attn_extend(P, P, P, OSM_BF16, 16, 32, 8, 4096, 128, 0.1f, F, F, F, 512, W, ews, nullptr) == OSM_OK);

@@ -152,6 +152,26 @@ def test_decode_validation(lib):
 
 
 @no_gpu_only
+def test_decode_noalloc_validation(lib):
+    """The allocation-free decode checks its arguments like the workspace
+    entry point, and rejects partials larger than the library's 64 MiB
+    scratch array with OSM_ERR_WORKSPACE, before any HIP call."""
+    def call(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, dtype=osm.OSM_BF16, B=16, Hq=32, Hkv=8, L=32768,
+             d=128, sk=FAKE, scale=0.1, split=256):
+        return lib.osm_attn_decode_splitkv_noalloc(q, kc, vc, o, None, dtype, B, Hq, Hkv, L, d, sk, scale,
+                                                   split, None)
+    assert call(B=0) == 2
+    assert call(split=0) == 2
+    assert call(d=96) == 3
+    assert call(split=100) == 3
+    assert call(sk=None) == 1
+    assert call(kc=ctypes.c_void_p(0x10008)) == 3
+    assert lib.osm_decode_workspace_bytes(64, 32, 32768, 128, 256) > (64 << 20)
+    assert call(B=64) == 4                          # 136 MiB of partials
+    assert call(B=16, L=131072) == 4
+
+
+@no_gpu_only
 def test_merge_validation(lib):
     def call(pm=FAKE, pl=FAKE, po=FAKE, rows=4, C=3, d=64, o=FAKE, dt=osm.OSM_F32):
         return lib.osm_merge_partials(pm, pl, po, rows, C, d, o, dt, None, None)
