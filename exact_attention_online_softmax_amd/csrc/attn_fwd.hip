@@ -171,18 +171,35 @@ constexpr int kWaitVm20 = 0x4F74;  // vmcnt(20)
 constexpr int kWaitLgkm0 = 0xC07F; // lgkmcnt(0)
 static_assert(2 * LPW == 4, "kWaitVm4 assumes four loads per wave per tile");
 
-// (batch, head, KV head, first query) of a query block
+// (batch, head, KV head, first query, valid query and key lengths) of a
+// query block
 struct Blk {
-    int b, h, kvh, q0;
+    int b, h, kvh, q0, Lq, Lk;
 };
 
-// PERSIST: one workgroup per CU walks the blocks L = blockIdx.x, + gridDim.x,
-// ...  Used for full-length non-causal inputs, where every block has the same
-// work.  The Q of the next block is copied into LDS (qs) while the current
-// block runs, and the last ring loads of a block fetch the first tiles of
-// the next one, so a block starts with its Q and first tiles on chip and
-// the Q reads and O writes of all CUs no longer fall in the same interval.
-template <bool PERSIST>
+// Persistent grid with a static schedule (causal or varlen inputs): the
+// schedule of one XCD's blocks is a list in LDS of entries (t << 16) | i, head
+// 8 t + XCD and query block i, at most kSchedMax of them.
+constexpr int kSchedMax = 2048;
+constexpr int kSchedFixed = 10;     // per-block cost outside the tile loop, in tiles (measured)
+
+// MODE 0: one query block per workgroup.
+// MODE 1 and 2 (PERSIST): one workgroup per CU walks several blocks.  The Q of
+// the next block is copied into LDS (qs) while the current block runs, and
+// the last ring loads of a block fetch the first tiles of the next one, so a
+// block starts with its Q and first tiles on chip, and no CU waits for a new
+// workgroup to be dispatched between blocks.
+//  * MODE 1: full-length non-causal inputs, where every block has the same
+//    work: workgroup L takes blocks L, L + gridDim.x, ...
+//  * MODE 2: causal or varlen inputs.  Every workgroup first builds its list
+//    of blocks from the lengths: the XCD's heads in decreasing order of
+//    their largest block; a head's blocks, heaviest first, go to the
+//    least-loaded slots of the XCD (longest-processing-time-first list
+//    scheduling, with costs in tiles plus a fixed cost per block), so the
+//    XCD's workgroups run one or two heads at a time and share their K and V
+//    in L2.  Blocks with no visible key or no valid query only write O = 0,
+//    LSE = -inf; they come last, round robin over the slots.
+template <int MODE>
 __device__ __forceinline__ void
 attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
               const uint16_t *__restrict__ V, uint16_t *__restrict__ O,
@@ -195,8 +212,13 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     // Q of the block (PERSIST), rows swizzled like K
     // (less aligned than the slots, so that it is laid out after them and the
     // slots stay within reach of the 16-bit immediate offset of LDS reads)
+    constexpr bool PERSIST = MODE != 0;
+    constexpr bool SCHED = MODE == 2;
     __shared__ __attribute__((aligned(256))) uint8_t qs[PERSIST ? BQ * ROWB : 256];
-    const int causal = PERSIST ? 0 : causal_arg;
+    // the workgroup's block list (SCHED): entries, then (compute items, items)
+    __shared__ int sched[SCHED ? kSchedMax : 1];
+    __shared__ int sched_n[2];
+    const int causal = MODE == 1 ? 0 : causal_arg;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -224,21 +246,121 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
         qrev = __builtin_amdgcn_readfirstlane(qrev);
         const int qb0 = causal ? (nqb - 1 - qrev) : qrev;
         const int b = head / Hq, h = head % Hq;
-        return {b, h, h / (Hq / Hkv), qb0 * BQ};
+        return {b, h, h / (Hq / Hkv), qb0 * BQ, 0, 0};   // lengths: read in the block loop
+    };
+    // block of a schedule entry (SCHED)
+    auto item_blk = [&](int e) __attribute__((always_inline)) -> Blk {
+        e = __builtin_amdgcn_readfirstlane(e);
+        const int head = 8 * (e >> 16) + (int)(blockIdx.x & 7);
+        // the integer divisions run on the vector ALU; the results are uniform,
+        // so move them back to scalar registers (a buffer resource built from
+        // a vector register makes every load a loop over lanes)
+        const int b = __builtin_amdgcn_readfirstlane(head / Hq), h = __builtin_amdgcn_readfirstlane(head % Hq);
+        const int kvh = __builtin_amdgcn_readfirstlane(h / (Hq / Hkv));
+        const int lq = __builtin_amdgcn_readfirstlane(seqlens_q ? clampi(seqlens_q[b], 0, Nq) : Nq);
+        const int lk = __builtin_amdgcn_readfirstlane(seqlens_k ? clampi(seqlens_k[b], 0, Nk) : Nk);
+        return {b, h, kvh, (e & 0xffff) * BQ, lq, lk};
+    };
+    // every row of a block that sees no key is written O = 0, LSE = -inf
+    auto zero_fill = [&](const Blk &z) __attribute__((always_inline)) {
+        const size_t zhead = (size_t)(z.b * Hq + z.h) * Nq;
+        const int rows = min(BQ, Nq - z.q0);
+        for (int i = tid; i < rows * (D / 8); i += NT) {
+            const int r = i / (D / 8), d8 = i % (D / 8);
+            *reinterpret_cast<uint4 *>(O + (zhead + z.q0 + r) * D + d8 * 8) = make_uint4(0, 0, 0, 0);
+        }
+        if (LSE)
+            for (int r = tid; r < rows; r += NT) LSE[zhead + z.q0 + r] = kNegInf;
     };
 
+    // ---- the static schedule (SCHED), built by wave 0 -------------------------
+    int n_compute = 0, n_items = 0;
+    if constexpr (SCHED) {
+        if (wave == 0) {
+            const int xcd = blockIdx.x & 7, myslot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
+            const int nh = xcd_heads;
+            // tiles of query block i of a head with lengths (lq, lk)
+            auto tiles_of = [&](int i, int lq, int lk) __attribute__((always_inline)) -> int {
+                const int kend = causal ? min(lk, min((i + 1) * BQ, lq)) : lk;
+                return (kend + BK - 1) / BK;
+            };
+            // lane t < nh: head 8 t + xcd, its lengths and its number of blocks
+            // with work (none when it has no key)
+            int hlq = 0, hlk = 0, hnb = 0, hcost = -1;
+            if (lane < nh) {
+                const int bb = (8 * lane + xcd) / Hq;
+                hlq = seqlens_q ? clampi(seqlens_q[bb], 0, Nq) : Nq;
+                hlk = seqlens_k ? clampi(seqlens_k[bb], 0, Nk) : Nk;
+                hnb = hlk > 0 ? (hlq + BQ - 1) / BQ : 0;
+                hcost = hnb > 0 ? tiles_of(hnb - 1, hlq, hlk) : 0;
+            }
+            // rank of each head: decreasing cost of its largest block, ties by t
+            int hrank = 0;
+            for (int j = 0; j < nh; ++j) {
+                const int cj = __builtin_amdgcn_readlane(hcost, j);
+                hrank += (cj > hcost || (cj == hcost && j < lane)) ? 1 : 0;
+            }
+            int load = 0;   // lane s < nslots: tiles given to slot s so far
+            int n = 0;      // entries of this workgroup's list
+            for (int r = 0; r < nh; ++r) {
+                const int t = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(lane < nh && hrank == r));
+                const int nb = __builtin_amdgcn_readlane(hnb, t);
+                const int lq = __builtin_amdgcn_readlane(hlq, t), lk = __builtin_amdgcn_readlane(hlk, t);
+                // the head's blocks, heaviest first (causal: the last), in rounds
+                // of nslots: the least-loaded slot (ties by slot) takes the
+                // heaviest block of the round, the next one the next, ...
+                for (int i0 = 0; i0 < nb; i0 += nslots) {
+                    const int take = min(nslots, nb - i0);
+                    const int key = lane < nslots ? load * 64 + lane : 0x7fffffff;
+                    int rk = 0;
+                    for (int j = 0; j < nslots; ++j) rk += (__builtin_amdgcn_readlane(key, j) < key) ? 1 : 0;
+                    if (lane < nslots && rk < take) load += tiles_of(nb - 1 - (i0 + rk), lq, lk) + kSchedFixed;
+                    const int mrk = __builtin_amdgcn_readlane(rk, myslot);
+                    if (mrk < take) {
+                        if (lane == 0) sched[n] = (t << 16) | (nb - 1 - (i0 + mrk));
+                        ++n;
+                    }
+                }
+            }
+            const int ncomp = n;
+            // blocks without work, numbered over the heads in rank order; the
+            // slot of block number j is j % nslots
+            int pj = 0;
+            for (int r = 0; r < nh; ++r) {
+                const int t = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(lane < nh && hrank == r));
+                const int nb = __builtin_amdgcn_readlane(hnb, t);
+                const int np = nqb - nb;
+                for (int i = nb + ((myslot - pj) % nslots + nslots) % nslots; i < nqb; i += nslots) {
+                    if (lane == 0) sched[n] = (t << 16) | i;
+                    ++n;
+                }
+                pj += np;
+            }
+            if (lane == 0) {
+                sched_n[0] = ncomp;
+                sched_n[1] = n;
+            }
+        }
+        __syncthreads();
+        n_compute = __builtin_amdgcn_readfirstlane(sched_n[0]);
+        n_items = __builtin_amdgcn_readfirstlane(sched_n[1]);
+    }
+
     int L = blockIdx.x;
+    int item = 0;
     bool first = true;
     for (;;) {
-        const Blk cur = decode(L);
+        if (SCHED && item >= n_compute) break;
+        const Blk cur = SCHED ? item_blk(sched[item]) : decode(L);
         const int Lnext = L + (int)gridDim.x;
-        const bool has_next = PERSIST && __builtin_amdgcn_readfirstlane(Lnext < nblocks ? 1 : 0) != 0;
-        const Blk nxt = decode(has_next ? Lnext : L);
+        const bool has_next = SCHED ? (item + 1 < n_compute)
+                                    : (PERSIST && __builtin_amdgcn_readfirstlane(Lnext < nblocks ? 1 : 0) != 0);
+        const Blk nxt = SCHED ? (has_next ? item_blk(sched[item + 1]) : cur) : decode(has_next ? Lnext : L);
         const int b = cur.b, h = cur.h, kvh = cur.kvh, q0 = cur.q0;
         // lengths and the wave index are uniform: keep them in scalar registers
         // so that every tile-level decision is a scalar branch
-        const int Lq = __builtin_amdgcn_readfirstlane(seqlens_q ? clampi(seqlens_q[b], 0, Nq) : Nq);
-        const int Lk = __builtin_amdgcn_readfirstlane(seqlens_k ? clampi(seqlens_k[b], 0, Nk) : Nk);
+        const int Lq = SCHED ? cur.Lq : __builtin_amdgcn_readfirstlane(seqlens_q ? clampi(seqlens_q[b], 0, Nq) : Nq);
+        const int Lk = SCHED ? cur.Lk : __builtin_amdgcn_readfirstlane(seqlens_k ? clampi(seqlens_k[b], 0, Nk) : Nk);
 
         const int qw0 = q0 + QW * wave;         // first query of this wave
         // this lane's queries: qw0 + c (block 0) and qw0 + 32 + c (block 1)
@@ -249,13 +371,7 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 
         if (!PERSIST && q0 >= Lq) {
             // every row of this block is padding: O = 0, LSE = -inf
-            const int rows = min(BQ, Nq - q0);
-            for (int i = tid; i < rows * (D / 8); i += NT) {
-                const int r = i / (D / 8), d8 = i % (D / 8);
-                *reinterpret_cast<uint4 *>(O + (qhead + q0 + r) * D + d8 * 8) = make_uint4(0, 0, 0, 0);
-            }
-            if (LSE)
-                for (int r = tid; r < rows; r += NT) LSE[qhead + q0 + r] = kNegInf;
+            zero_fill(cur);
             return;
         }
 
@@ -339,8 +455,8 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
             return rsrc_at(Kh, Vh, t * BK, Lk);
         };
         // With PERSIST, tile nend + i (past this block's padded end, where the
-        // ring would load zeros) is tile i of the next block, if there is one;
-        // every block has the same Lk = Nk and the same nend.  The compiler
+        // ring would load zeros) is tile i of the next block, if there is one,
+        // with the next block's key length.  The compiler
         // evaluates the uniform selects of that case on the vector ALU;
         // readfirstlane keeps the resource in scalar registers, without which
         // every load would become a loop over lanes.
@@ -353,7 +469,8 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                 const bool next = t >= nend;
                 const uint16_t *kb = uniform_ptr(next ? Kn : Kh), *vb = uniform_ptr(next ? Vn : Vh);
                 const int j0 = __builtin_amdgcn_readfirstlane((next ? t - nend : t) * BK);
-                const int len = __builtin_amdgcn_readfirstlane((next && !has_next) ? 0 : Lk);
+                // (MODE 1: every block has the same key length)
+                const int len = __builtin_amdgcn_readfirstlane((next && !has_next) ? 0 : (next && SCHED) ? nxt.Lk : Lk);
                 return rsrc_at(kb, vb, j0, len);
             }
         };
@@ -376,11 +493,11 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 
         // Q rows q0 .. q0 + BQ - 1 of block n into qs (PERSIST): wave w copies
         // its own 64 rows, 16 loads of 1 KiB laid out like a K tile's; rows at
-        // or past Nq read as zeros
+        // or past the block's valid length read as zeros
         auto issue_q = [&](const Blk &n) __attribute__((always_inline)) {
             const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<uint16_t *>(Q) + ((size_t)(n.b * Hq + n.h) * Nq + n.q0) * D, 0,
-                max(0, Nq - n.q0) * ROWB, kRsrcWord3);
+                max(0, (SCHED ? n.Lq : Nq) - n.q0) * ROWB, kRsrcWord3);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int blk = 16 * wave + i, row = 4 * blk + (lane >> 4), sl = lane & 15;
@@ -761,8 +878,12 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
         }
         if (!has_next) break;
         L = Lnext;
+        ++item;
         first = false;
     }   // blocks
+    // blocks without work (SCHED): O = 0, LSE = -inf
+    if constexpr (SCHED)
+        for (int k = n_compute; k < n_items; ++k) zero_fill(item_blk(sched[k]));
 }
 
 #define OSM_ATTN_FWD_PARAMS                                                                          \
@@ -773,14 +894,20 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 
 // one query block per workgroup
 __global__ void __launch_bounds__(NT, 1) attn_fwd_bf16_d128(OSM_ATTN_FWD_PARAMS) {
-    attn_fwd_body<false>(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, seqlens_q, seqlens_k, scale_log2, causal, nqb,
-                         xcd_heads, nblocks);
+    attn_fwd_body<0>(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, seqlens_q, seqlens_k, scale_log2, causal, nqb,
+                     xcd_heads, nblocks);
 }
 
-// one workgroup per compute unit walking several query blocks
+// one workgroup per compute unit walking several equal query blocks
 __global__ void __launch_bounds__(NT, 1) attn_fwd_bf16_d128_persist(OSM_ATTN_FWD_PARAMS) {
-    attn_fwd_body<true>(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, seqlens_q, seqlens_k, scale_log2, causal, nqb,
-                        xcd_heads, nblocks);
+    attn_fwd_body<1>(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, seqlens_q, seqlens_k, scale_log2, causal, nqb,
+                     xcd_heads, nblocks);
+}
+
+// one workgroup per compute unit walking a static schedule of unequal blocks
+__global__ void __launch_bounds__(NT, 1) attn_fwd_bf16_d128_sched(OSM_ATTN_FWD_PARAMS) {
+    attn_fwd_body<2>(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, seqlens_q, seqlens_k, scale_log2, causal, nqb,
+                     xcd_heads, nblocks);
 }
 #undef OSM_ATTN_FWD_PARAMS
 
@@ -792,29 +919,42 @@ hipError_t launch_attn_fwd(const AttnFwdArgs &a, hipStream_t s) {
     const int64_t blocks = (int64_t)nqb * nheads;
     if (blocks == 0) return hipSuccess;
     const int xcd_heads = (nheads % 8 == 0) ? nheads / 8 : 0;
-    // full-length non-causal inputs with more blocks than compute units run
-    // on a persistent grid of one workgroup per compute unit
     int cus = 0;
-    if (!a.causal && !a.seqlens_q && !a.seqlens_k && a.seqlen_k > 0) {
+    {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             cus = 0;
         cus &= ~7;   // whole XCDs' worth, so block L keeps running on XCD L % 8
     }
-    const bool persist = cus > 0 && blocks > cus;
-    const unsigned grid = persist ? (unsigned)cus : (unsigned)blocks;
+    // Full-length non-causal inputs with more blocks than compute units run on
+    // a persistent grid of one workgroup per compute unit (MODE 1); causal or
+    // varlen inputs on the scheduled persistent grid (MODE 2) when each XCD's
+    // heads and its list fit the schedule's limits (heads per XCD and slots
+    // per XCD at most 64, at most kSchedMax blocks per XCD, slot loads below
+    // 2^24 tiles); everything else one block per workgroup (MODE 0).
+    const bool uniform = !a.causal && !a.seqlens_q && !a.seqlens_k && a.seqlen_k > 0;
+    const int64_t per_xcd = xcd_heads ? (int64_t)xcd_heads * nqb : 0;
+    const int64_t max_tiles = per_xcd * ((a.seqlen_k + BK - 1) / BK + kSchedFixed);
+    int mode = 0;
+    if (cus > 0 && blocks > cus) {
+        if (uniform) mode = 1;
+        else if (xcd_heads > 0 && xcd_heads <= 64 && cus / 8 <= 64 && per_xcd <= kSchedMax &&
+                 max_tiles < ((int64_t)1 << 24))
+            mode = 2;
+    }
+    const unsigned grid = mode ? (unsigned)cus : (unsigned)blocks;
     const uint16_t *q = static_cast<const uint16_t *>(a.q), *k = static_cast<const uint16_t *>(a.k),
                    *v = static_cast<const uint16_t *>(a.v);
     uint16_t *o = static_cast<uint16_t *>(a.o);
-    if (persist)
-        hipLaunchKernelGGL(attn_fwd_bf16_d128_persist, dim3(grid), dim3(NT), 0, s, q, k, v, o, a.lse, a.batch,
-                           a.heads_q, a.heads_kv, a.seqlen_q, a.seqlen_k, a.seqlens_q, a.seqlens_k,
-                           a.scale * kLog2e, a.causal, nqb, xcd_heads, (int)blocks);
-    else
-        hipLaunchKernelGGL(attn_fwd_bf16_d128, dim3(grid), dim3(NT), 0, s, q, k, v, o, a.lse, a.batch,
-                           a.heads_q, a.heads_kv, a.seqlen_q, a.seqlen_k, a.seqlens_q, a.seqlens_k,
-                           a.scale * kLog2e, a.causal, nqb, xcd_heads, (int)blocks);
+#define OSM_FWD_LAUNCH(KERNEL)                                                                         \
+    hipLaunchKernelGGL(KERNEL, dim3(grid), dim3(NT), 0, s, q, k, v, o, a.lse, a.batch, a.heads_q,     \
+                       a.heads_kv, a.seqlen_q, a.seqlen_k, a.seqlens_q, a.seqlens_k, a.scale * kLog2e, \
+                       a.causal, nqb, xcd_heads, (int)blocks)
+    if (mode == 1) OSM_FWD_LAUNCH(attn_fwd_bf16_d128_persist);
+    else if (mode == 2) OSM_FWD_LAUNCH(attn_fwd_bf16_d128_sched);
+    else OSM_FWD_LAUNCH(attn_fwd_bf16_d128);
+#undef OSM_FWD_LAUNCH
     return hipGetLastError();
 }
 

@@ -183,9 +183,10 @@ def test_persistent_grid(orc, B, Hq, Hkv, Nq, Nk):
     """Full-length non-causal inputs with more query blocks than compute
     units run on a persistent grid (each workgroup walks several blocks,
     prefetching the next block's Q and first key tiles).  The same inputs
-    with explicit full lengths take the one-block-per-workgroup kernel; the
-    per-block arithmetic is the same, so the outputs must agree bit for bit.
-    Sampled rows are also checked against the oracle."""
+    with explicit full lengths take the scheduled persistent grid (head
+    counts divisible by 8) or the one-block-per-workgroup kernel (9 heads);
+    the per-block arithmetic is the same, so the outputs must agree bit for
+    bit.  Sampled rows are also checked against the oracle."""
     announce(f"fwd persistent grid B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk}")
     torch = torch_mod()
     assert B * Hq * ((Nq + 255) // 256) > torch.cuda.get_device_properties(0).multi_processor_count
@@ -263,3 +264,62 @@ def test_no_keys_through_abi():
             torch.cuda.synchronize()
             assert np.all(host_bits(o) == 0), f"fp8={fp8}"
             assert np.all(np.isneginf(host(lse))), f"fp8={fp8}"
+
+
+def _run_in_groups(inp):
+    """The same attention, one call per (batch, group of 8 query heads): at
+    most 256 query blocks per call (N <= 8192), so every call runs one block
+    per workgroup."""
+    torch = torch_mod()
+    B, Hq, Nq, d = inp.q.shape
+    Hkv = inp.k.shape[1]
+    g = Hq // Hkv
+    q, k, v = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device="cuda")
+    for b in range(B):
+        for h0 in range(0, Hq, 8):
+            kv0, kv1 = h0 // g, (h0 + 8 + g - 1) // g
+            sq = None if inp.seqlens_q is None else dev_i32(inp.seqlens_q[b:b + 1])
+            sk = None if inp.seqlens_k is None else dev_i32(inp.seqlens_k[b:b + 1])
+            ob, lb = osm.attn_fwd(q[b:b + 1, h0:h0 + 8].contiguous(), k[b:b + 1, kv0:kv1].contiguous(),
+                                  v[b:b + 1, kv0:kv1].contiguous(), scale=inp.scale, causal=inp.causal,
+                                  seqlens_q=sq, seqlens_k=sk)
+            o[b:b + 1, h0:h0 + 8] = ob
+            lse[b:b + 1, h0:h0 + 8] = lb
+    return o, lse
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,causal,lq,lk", [
+    (4, 16, 16, 4096, 4096, True, [1, 1000, 2049, 4096], None),       # causal, ragged, one 1-row sequence
+    (4, 16, 8, 3000, 2000, False, [3000, 17, 2999, 0], [0, 2000, 1234, 5]),   # no keys / no queries
+    (2, 32, 8, 5000, 5000, True, [5000, 3333], None),                  # GQA 4:1, causal
+    (2, 8, 8, 8192, 8192, True, [8192, 7777], None),                   # 1 head per XCD, 32-block heads
+])
+def test_scheduled_grid(orc, B, Hq, Hkv, Nq, Nk, causal, lq, lk):
+    """Causal or varlen inputs with more query blocks than compute units run
+    on the scheduled persistent grid (each workgroup walks a list of blocks
+    built in-kernel from the lengths, prefetching the next block's Q and
+    first tiles).  One call per group of 8 query heads of one sequence runs
+    the same blocks one per workgroup; the per-block arithmetic is the same,
+    so the outputs must agree bit for bit.  NaN past the lengths; padded
+    rows exactly 0 / -inf; sampled rows against the oracle."""
+    announce(f"fwd scheduled grid B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} causal={causal} lq={lq} lk={lk}")
+    torch = torch_mod()
+    assert B * Hq * ((Nq + 255) // 256) > torch.cuda.get_device_properties(0).multi_processor_count
+    lq = np.array(lq, np.int32)
+    lk = lq.copy() if lk is None else np.array(lk, np.int32)
+    inp = inputs.attention_inputs(B, Hq, Hkv, Nq, Nk, 128, seed=B * 11 + Hq + Nq + Nk, causal=causal,
+                                  seqlens_q=lq, seqlens_k=lk, poison=True)
+    o1, l1 = run(inp)
+    o2, l2 = _run_in_groups(inp)
+    assert np.array_equal(host_bits(o1), host_bits(o2))
+    assert np.array_equal(host_bits(l1), host_bits(l2))
+    oh, lh = host(o1), host(l1)
+    assert not np.isnan(oh).any()
+    for b in range(B):
+        dead_from = int(lq[b]) if lk[b] > 0 else 0
+        assert np.all(oh[b, :, dead_from:] == 0.0) and np.all(np.isneginf(lh[b, :, dead_from:]))
+    rows = _sample_rows(np.random.default_rng(Nq + B), B, Hq, Nq, 300, np.maximum(lq, 1))
+    o_ref, lse_ref = oracle(orc, inp, rows=rows)
+    check_attn(oh.reshape(-1, 128)[rows], lh.reshape(-1)[rows], o_ref, lse_ref, "bf16")
