@@ -205,9 +205,10 @@ def summarize(name, trace_dir, out):
         for (short, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
             lines.append(f"| {short} | {wg} | {len(d)} | {sum(d) / len(d) / 1e3:.1f} | "
                          f"{min(d) / 1e3:.1f} | {max(d) / 1e3:.1f} |")
-        # the non-causal forward runs on the persistent grid (one workgroup per
-        # compute unit); the causal one on one workgroup per query block
-        want = {"fwd": ("attn_fwd_bf16_d128_persist", None), "fwd_causal": ("attn_fwd_bf16", 4096),
+        # both forwards run on persistent grids (one workgroup per compute
+        # unit): the full-length one walks equal blocks, the causal varlen one
+        # a schedule built from the lengths
+        want = {"fwd": ("attn_fwd_bf16_d128_persist", None), "fwd_causal": ("attn_fwd_bf16_d128_sched", None),
                 "softmax": ("softmax_rows_resident", None), "softmax_2pass": ("softmax_rows_streaming", None),
                 "decode": ("decode_split", None),
                 "merge_lse": ("merge_lse", None), "extend": ("decode_split", None),

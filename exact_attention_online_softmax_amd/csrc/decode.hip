@@ -380,6 +380,95 @@ merge_partials_kernel(const float *__restrict__ pm, const float *__restrict__ pl
     }
 }
 
+// Rows of at most kSmallC pieces (the streaming extend's chunks, short
+// decodes): one wave per row, four rows per workgroup, and every load of a
+// row (the pieces' m, l and O~, and the persisted summary) issued before any
+// is used, so a row costs one memory round trip.  Empty pieces get weight 0
+// through a select, as in merge_partials_kernel; the pieces are summed in
+// order, then the persisted summary.
+constexpr int kSmallC = 8;
+
+template <int NDL, bool STATE>
+__global__ void __launch_bounds__(MRG_THREADS)
+merge_partials_small(const float *__restrict__ pm, const float *__restrict__ pl,
+                     const float *__restrict__ po, int64_t rows, int C, int HD,
+                     void *__restrict__ out, int out_bf16, float *__restrict__ lse,
+                     float *state_m, float *state_l, float *state_o) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * MRG_WAVES + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    float mc[kSmallC], lc[kSmallC], oc[kSmallC][NDL];
+#pragma unroll
+    for (int c = 0; c < kSmallC; ++c) {
+        mc[c] = kNegInf;
+        lc[c] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NDL; ++k) oc[c][k] = 0.0f;
+        if (c < C) {
+            mc[c] = pm[r * C + c];
+            lc[c] = pl[r * C + c];
+#pragma unroll
+            for (int k = 0; k < NDL; ++k)
+                if (lane + 64 * k < HD) oc[c][k] = po[(r * C + c) * HD + lane + 64 * k];
+        }
+    }
+    float ms = kNegInf, ls = 0.0f, os[NDL];
+#pragma unroll
+    for (int k = 0; k < NDL; ++k) os[k] = 0.0f;
+    if (STATE) {
+        ms = state_m[r];
+        ls = state_l[r];
+#pragma unroll
+        for (int k = 0; k < NDL; ++k)
+            if (lane + 64 * k < HD) os[k] = state_o[r * HD + lane + 64 * k];
+    }
+    float m = ms;
+#pragma unroll
+    for (int c = 0; c < kSmallC; ++c) m = fmaxf(m, mc[c]);
+    float acc[NDL], lsum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NDL; ++k) acc[k] = 0.0f;
+    if (m != kNegInf) {
+#pragma unroll
+        for (int c = 0; c < kSmallC; ++c) {
+            const bool live = mc[c] != kNegInf;
+            const float w = live ? exp_acc(mc[c] - m) : 0.0f;
+            lsum = live ? fmaf(w, lc[c], lsum) : lsum;
+#pragma unroll
+            for (int k = 0; k < NDL; ++k) acc[k] = live ? fmaf(w, oc[c][k], acc[k]) : acc[k];
+        }
+        if (STATE && ms != kNegInf) {
+            const float w = exp_acc(ms - m);
+            lsum = fmaf(w, ls, lsum);
+#pragma unroll
+            for (int k = 0; k < NDL; ++k) acc[k] = fmaf(w, os[k], acc[k]);
+        }
+    }
+    if (STATE) {
+        // every read of this row's summary above precedes these writes
+#pragma unroll
+        for (int k = 0; k < NDL; ++k)
+            if (lane + 64 * k < HD) state_o[r * HD + lane + 64 * k] = (m == kNegInf) ? 0.0f : acc[k];
+        if (lane == 0) {
+            state_m[r] = m;
+            state_l[r] = (m == kNegInf) ? 0.0f : lsum;
+        }
+        return;
+    }
+    const bool valid = (m != kNegInf) && (lsum > 0.0f);
+    const float inv = valid ? 1.0f / lsum : 0.0f;
+#pragma unroll
+    for (int k = 0; k < NDL; ++k) {
+        const int d = lane + 64 * k;
+        if (d < HD) {
+            const float o = acc[k] * inv;
+            if (out_bf16) static_cast<uint16_t *>(out)[r * HD + d] = f32_to_bf16(o);
+            else static_cast<float *>(out)[r * HD + d] = o;
+        }
+    }
+    if (lse && lane == 0) lse[r] = valid ? m + logf(lsum) : kNegInf;
+}
+
 template <typename T, int HD, int G>
 hipError_t launch_split(const DecodeArgs &a, const DecodeLayout &lay, hipStream_t s) {
     char *ws = static_cast<char *>(a.workspace);
@@ -436,9 +525,23 @@ hipError_t launch_decode_split(const DecodeArgs &a, const DecodeLayout &lay, hip
 
 hipError_t launch_merge_partials(const MergeArgs &a, hipStream_t s) {
     if (a.rows == 0) return hipSuccess;
-    const int grid = (int)(a.rows < 1048576 ? a.rows : 1048576);
     const int ndl = (a.head_dim + 63) / 64;
     const bool st = a.state_m != nullptr;
+    if (a.num_splits <= kSmallC && ndl <= 2) {
+        const unsigned g = (unsigned)((a.rows + MRG_WAVES - 1) / MRG_WAVES);
+#define OSM_MERGE_SMALL(N, ST)                                                                           \
+    hipLaunchKernelGGL((merge_partials_small<N, ST>), dim3(g), dim3(MRG_THREADS), 0, s, a.part_m, a.part_l, \
+                       a.part_o, a.rows, a.num_splits, a.head_dim, a.o, a.out_dtype, a.lse, a.state_m,     \
+                       a.state_l, a.state_o)
+        if (st) {
+            if (ndl <= 1) OSM_MERGE_SMALL(1, true);
+            else OSM_MERGE_SMALL(2, true);
+        } else if (ndl <= 1) OSM_MERGE_SMALL(1, false);
+        else OSM_MERGE_SMALL(2, false);
+#undef OSM_MERGE_SMALL
+        return hipGetLastError();
+    }
+    const int grid = (int)(a.rows < 1048576 ? a.rows : 1048576);
 #define OSM_MERGE_LAUNCH(N, ST)                                                                        \
     hipLaunchKernelGGL((merge_partials_kernel<N, ST>), dim3(grid), dim3(MRG_THREADS), 0, s, a.part_m,  \
                        a.part_l, a.part_o, a.rows, a.num_splits, a.head_dim, a.o, a.out_dtype, a.lse, \
