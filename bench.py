@@ -110,7 +110,7 @@ def cpu_model():
 
 def achievable(torch):
     """Rates of two reference kernels on this GPU (libosm_probe.so), each the
-    median of 20 back-to-back launches timed with HIP events: a streaming copy
+    median of 20 launches, each timed with HIP events on its own: a streaming copy
     of 1 GiB (GB/s of bytes read + written) and a bf16 matrix-core loop on
     N(0, 1) operands (TFLOP/s) with one 256-thread workgroup per compute unit,
     i.e. one wave per SIMD, as the attention forward runs."""
@@ -123,14 +123,18 @@ def achievable(torch):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
 
     def timed(fn, reps=20):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        # each launch timed on its own (the stream drained before it)
         fn()
-        for a, b in evs:
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
             a.record()
             fn()
             b.record()
-        torch.cuda.synchronize()
-        return float(np.median([a.elapsed_time(b) for a, b in evs])) / 1e3
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts)) / 1e3
 
     nbytes = 1 << 30
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
@@ -138,7 +142,7 @@ def achievable(torch):
     t_copy = timed(lambda: lib.osmprobe_copy(vp(src.data_ptr()), vp(dst.data_ptr()), nbytes, stream))
     del src, dst
     res = {"copy_GBps": round(2 * nbytes / t_copy / 1e9, 1),
-           "copy": "1 GiB streaming copy (nontemporal 16-byte loads and stores, 32 KiB per workgroup), "
+           "copy": "1 GiB streaming copy (nontemporal 16-byte buffer loads and stores, 32 KiB per workgroup), "
                    "bytes read + written"}
     g = np.random.default_rng(12345)
     grid, iters = cus, 4096
@@ -208,11 +212,14 @@ def summarize(name, trace_dir, out):
         # both forwards run on persistent grids (one workgroup per compute
         # unit): the full-length one walks equal blocks, the causal varlen one
         # a schedule built from the lengths
+        # (the piece kernel's grid is (pieces, kv heads, batch): 128 pieces
+        # for decode, 8 for extend; the backward's key-major kernel is
+        # instantiated for the causal mask or not)
         want = {"fwd": ("attn_fwd_bf16_d128_persist", None), "fwd_causal": ("attn_fwd_bf16_d128_sched", None),
                 "softmax": ("softmax_rows_resident", None), "softmax_2pass": ("softmax_rows_streaming", None),
-                "decode": ("decode_split", None),
-                "merge_lse": ("merge_lse", None), "extend": ("decode_split", None),
-                "bwd": ("attn_bwd_dkdv", None), "bwd_causal": ("attn_bwd_dkdv", None),
+                "decode": ("decode_split", 128),
+                "merge_lse": ("merge_lse", None), "extend": ("decode_split", 8),
+                "bwd": ("attn_bwd_dkdv<false>", None), "bwd_causal": ("attn_bwd_dkdv<true>", None),
                 "fwd_fp8": ("attn_fwd_fp8", None)}[name]
         for (short, wg), d in groups.items():
             if want[0] in short and (want[1] is None or wg == want[1]):
@@ -255,19 +262,44 @@ def summarize(name, trace_dir, out):
                    + counters.get(("kernel", "WRITE_SIZE"), 0.0) * 1024 * w_scale)
         lines += [f"copy calibration: {copy_bytes:.0f} bytes read and written by the copy; "
                   f"FETCH_SIZE scale {f_scale:.4f}, WRITE_SIZE scale {w_scale:.4f}", ""]
-    if ("kernel", "SQ_VALU_MFMA_BUSY_CYCLES") in counters and ("kernel", "GRBM_GUI_ACTIVE") in counters and pmc_ns:
+    kc = {c: v for (k, c), v in counters.items() if k == "kernel"}
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in kc and "GRBM_GUI_ACTIVE" in kc and pmc_ns:
         # GRBM_GUI_ACTIVE is summed over the 8 XCDs; SQ_VALU_MFMA_BUSY_CYCLES over
         # the 1024 SIMDs, in cycles of the matrix pipe at its full issue rate
-        cycles = counters[("kernel", "GRBM_GUI_ACTIVE")] / 8
-        busy = counters[("kernel", "SQ_VALU_MFMA_BUSY_CYCLES")] / 1024
+        cycles = kc["GRBM_GUI_ACTIVE"] / 8
+        busy = kc["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024
         ns = sum(pmc_ns) / len(pmc_ns)
         lines += [f"engine clock over the kernel: {cycles / ns:.2f} GHz (GRBM_GUI_ACTIVE per XCD / {ns / 1e3:.1f} us)",
                   f"MFMA busy: {100 * busy / cycles:.1f}% of the kernel's cycles per SIMD "
                   f"(SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / cycles)"]
-        if ("kernel", "SQ_INSTS_VALU_MFMA_MOPS_BF16") in counters:
-            lines.append(f"bf16 MFMA flops executed per launch: "
-                         f"{counters[('kernel', 'SQ_INSTS_VALU_MFMA_MOPS_BF16')] * 512:.4e} (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)")
+        for c, per, what in (("SQ_INSTS_VALU_MFMA_MOPS_BF16", 512, "bf16"), ("SQ_INSTS_VALU_MFMA_MOPS_F8", 512, "fp8")):
+            if c in kc and kc[c] > 0:
+                lines.append(f"{what} MFMA flops executed per launch: {kc[c] * per:.4e} ({c} x {per})")
         lines.append("")
+    if "SQ_INSTS_MFMA" in kc and kc["SQ_INSTS_MFMA"] > 0:
+        # instruction mix per matrix instruction (all counts are per wave
+        # instruction; SQ_INSTS_VALU includes the MFMA instructions themselves)
+        nm = kc["SQ_INSTS_MFMA"]
+        mix = []
+        if "SQ_INSTS_VALU" in kc:
+            mix.append(f"other VALU {(kc['SQ_INSTS_VALU'] - nm) / nm:.2f}")
+        mix += [f"{what} {kc[c] / nm:.2f}" for c, what in
+                (("SQ_INSTS_VALU_TRANS_F32", "of them exp (TRANS_F32)"), ("SQ_INSTS_LDS", "LDS"), ("SQ_INSTS_SALU", "SALU"))
+                if c in kc]
+        lines.append(f"per MFMA instruction ({nm:.4e} per launch): " + ", ".join(mix))
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in kc and "SQ_VALU_MFMA_BUSY_CYCLES" in kc:
+            lines.append(f"MFMA cycles with VALU co-executing: "
+                         f"{100 * kc['SQ_VALU_MFMA_COEXEC_CYCLES'] / kc['SQ_VALU_MFMA_BUSY_CYCLES']:.1f}%")
+        if "SQ_LDS_BANK_CONFLICT" in kc and "SQ_LDS_IDX_ACTIVE" in kc and kc["SQ_LDS_IDX_ACTIVE"] > 0:
+            lines.append(f"LDS bank conflicts: {kc['SQ_LDS_BANK_CONFLICT'] / kc['SQ_LDS_IDX_ACTIVE']:.4f} "
+                         f"of LDS active cycles (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE)")
+        lines.append("")
+    if "SQ_WAVE_CYCLES" in kc and kc["SQ_WAVE_CYCLES"] > 0:
+        wc = kc["SQ_WAVE_CYCLES"]
+        part = [f"{c[3:]}: {100 * kc[c] / wc:.1f}%" for c in
+                ("SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS",
+                 "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY") if c in kc]
+        lines += ["share of wave cycles (SQ_WAVE_CYCLES): " + ", ".join(part), ""]
     lines += [f"kernel_source_sha256_16: {source_hash(name)}",
               f"avg_kernel_us: {avg_ns / 1e3:.2f}" if avg_ns else "avg_kernel_us: null",
               f"traffic_bytes_per_launch: {traffic:.0f}" if traffic else "traffic_bytes_per_launch: null", ""]

@@ -3,8 +3,8 @@
 // context for their roofline fractions (libosm_probe.so; not part of the
 // osm C ABI, used by the benchmark only):
 //
-//  * osmprobe_copy: a streaming device copy, 16 bytes per lane per access,
-//    nontemporal loads and stores, one sweep of 32 KiB per workgroup.  Its
+//  * osmprobe_copy: a streaming device copy, 16-byte buffer accesses per
+//    lane, nontemporal loads and stores, one sweep of 32 KiB per workgroup.  Its
 //    GB/s (bytes read + bytes written per second) is the practical HBM
 //    ceiling of a read-and-write stream.
 //  * osmprobe_mfma_bf16: independent chains of v_mfma_f32_32x32x16_bf16 on
@@ -22,19 +22,27 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Workgroup w copies vectors [2048 w, 2048 (w + 1)) of the buffer: eight
-// 16-byte vectors per lane, all loads issued before the stores, so each
-// workgroup makes one sweep with 32 KiB in flight.
-__global__ void __launch_bounds__(256) copy_nt(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
-                                               size_t n) {
-    const size_t base = (size_t)blockIdx.x * 2048 + threadIdx.x;
+// Workgroup w copies bytes [32768 w, 32768 (w + 1)) of the buffer: eight
+// 16-byte vectors per lane through buffer resources spanning the
+// workgroup's range, nontemporal loads and stores, all loads issued before
+// the stores (one sweep with 32 KiB in flight).  Of the forms tried on
+// MI355X (global or buffer accesses, cached or nontemporal, 8 or 16 vectors
+// per lane), this one copied fastest.
+constexpr int kRsrcWord3 = 0x00020000;   // raw dword access
+constexpr int kAuxNontemporal = 2;
+
+__global__ void __launch_bounds__(256) copy_nt(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst) {
+    const size_t base = (size_t)blockIdx.x * 2048;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4 *>(src + base), 0, 32768, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(dst + base, 0, 32768, kRsrcWord3);
     u32x4 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-        if (base + 256 * u < n) v[u] = __builtin_nontemporal_load(src + base + 256 * u);
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (threadIdx.x + 256 * u) * 16, 0, kAuxNontemporal);
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-        if (base + 256 * u < n) __builtin_nontemporal_store(v[u], dst + base + 256 * u);
+        __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, (threadIdx.x + 256 * u) * 16, 0, kAuxNontemporal);
 }
 
 // Each lane loads eight A and eight B operand fragments (16 bf16 vectors);
@@ -68,18 +76,17 @@ __global__ void __launch_bounds__(512) mfma_loop(const bf16x8 *__restrict__ ops,
 
 extern "C" {
 
-// Copy `bytes` (a multiple of 16; both pointers 16-byte aligned) from src to
-// dst on `stream`, 32 KiB per workgroup of 256 threads.  Returns a
+// Copy `bytes` (a multiple of 32768; both pointers 16-byte aligned) from src
+// to dst on `stream`, 32 KiB per workgroup of 256 threads.  Returns a
 // hipError_t value (0 = launched).
 int osmprobe_copy(const void *src, void *dst, size_t bytes, void *stream) {
-    if (bytes % 16 || (reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 ||
+    if (bytes % 32768 || (reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 ||
         bytes / 32768 >= (size_t)1 << 31)
         return (int)hipErrorInvalidValue;
-    const size_t n = bytes / 16;
-    const unsigned grid = (unsigned)((n + 2047) / 2048);
+    const unsigned grid = (unsigned)(bytes / 32768);
     if (grid == 0) return 0;
     hipLaunchKernelGGL(copy_nt, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
-                       static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), n);
+                       static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst));
     return (int)hipGetLastError();
 }
 
