@@ -71,12 +71,18 @@ __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? l
 __device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // 256-byte LDS rows hold 16 chunks of 16 bytes; chunk c of row r sits in
-// slot c ^ swz(r).  swz is a rotation of the row's low four bits: it takes
-// 16 distinct values over 16 consecutive rows (row-wise 16-byte operand
-// reads are conflict-free), and over rows 4a .. 4a+3 its values differ in
-// their upper three bits (a transposing read of two adjacent chunks from
-// four rows touches eight distinct slots).
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// slot c ^ swz(r), swz(r) = 4 (r % 4) + (r / 4) % 4.  The LDS serves 256
+// bytes per cycle (64 banks of 4 bytes), so a read is free of bank
+// conflicts when every group of lanes served together touches distinct
+// 16-byte (row-wise reads: 16 lanes) or 8-byte (transposing reads: 32
+// lanes) slots of a 256-byte window.  Over 16 consecutive rows swz takes 16
+// distinct values, so the row-wise 16-byte operand reads are conflict-free;
+// over rows 4a .. 4a+3 its upper two bits take four distinct values, so a
+// transposing read of four adjacent chunks from those rows covers four
+// disjoint groups of four slots.  (The previous swizzle, a rotation of the
+// row's low four bits, left the transposing reads two-way conflicted:
+// rocprofv3 counted SQ_LDS_BANK_CONFLICT at 29% of the LDS active cycles.)
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 // gfx950 transposing LDS read: in each 16-lane group, lane i points at
 // row k0 + i/4, columns d0 + 4 (i%4) .. +3 of a row-major bf16 tile, and

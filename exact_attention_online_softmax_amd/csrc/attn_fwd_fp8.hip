@@ -40,9 +40,17 @@
 //    of P~V; its A operand V^T comes from ds_read_b64_tr_b8 reads (lane j of
 //    a 16-lane group receives eight consecutive rows of column j), eight keys
 //    per read, in the same order.
-//  * LDS rows are unpadded, 16-byte chunk c of row r in slot c ^ swz8(r):
-//    both the row-wise K operand reads and the transposing V reads are free
-//    of bank conflicts.
+//  * LDS rows are unpadded, 16-byte chunk c of row r in slot c ^ swz8(r),
+//    swz8(r) = 2 ((r / 2) % 4) + (r / 16) % 2.  The LDS serves 256 bytes per
+//    cycle; a row-wise 16-byte read serves 16 lanes at a time, a transposing
+//    read 32, and each group must touch distinct slots of a 256-byte window
+//    (two 128-byte rows).  The K operand's 16 lanes read rows of both
+//    parities from two groups of four, and swz8 takes eight distinct values
+//    over each parity's rows there; the V^T read's 32 lanes read two chunks
+//    of eight consecutive rows, and swz8 / 2 takes four distinct values over
+//    each parity's four rows.  Both reads are free of bank conflicts (the
+//    previous swizzle left the V^T reads two-way conflicted, 33% of the LDS
+//    active cycles in rocprofv3's counters).
 #include "osm_device.h"
 #include "osm_internal.h"
 
@@ -92,7 +100,7 @@ struct Blk {
 };
 
 // chunk c of LDS row r sits in slot c ^ swz8(r); see the header comment
-__device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 3) | (((r >> 4) & 1) << 2); }
+__device__ __forceinline__ int swz8(int r) { return (((r >> 1) & 3) << 1) | ((r >> 4) & 1); }
 
 __device__ __forceinline__ f32x16 mfma8(const i32x8 &a, const i32x8 &b, const f32x16 &c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kUnitScale, 0, kUnitScale);
