@@ -68,8 +68,10 @@ osm_status osm_attn_fwd(const void *q, const void *k, const void *v, void *o, fl
         heads_q % heads_kv != 0 || !(scale > 0.0f) || !isfinite(scale) || (causal != 0 && causal != 1))
         return OSM_ERR_SHAPE;
     if (dtype != OSM_BF16 || head_dim != 128 || too_many_heads(batch, heads_q)) return OSM_ERR_UNSUPPORTED;
-    // one head's K (or V) rows are addressed with 32-bit byte offsets
-    if ((int64_t)seqlen_k * head_dim * 2 >= ((int64_t)1 << 31)) return OSM_ERR_UNSUPPORTED;
+    // one head's rows of K, V, Q and O are addressed with 32-bit byte offsets
+    if ((int64_t)seqlen_k * head_dim * 2 >= ((int64_t)1 << 31) ||
+        (int64_t)seqlen_q * head_dim * 2 >= ((int64_t)1 << 31))
+        return OSM_ERR_UNSUPPORTED;
     if (seqlen_q == 0) return OSM_OK;
     if (!q || !o || (seqlen_k > 0 && (!k || !v))) return OSM_ERR_NULL;
     // rows are read and written 16 bytes at a time
@@ -89,8 +91,10 @@ osm_status osm_attn_fwd_fp8(const void *q, const void *k, const void *v, void *o
         (causal != 0 && causal != 1))
         return OSM_ERR_SHAPE;
     if (head_dim != 128 || too_many_heads(batch, heads_q)) return OSM_ERR_UNSUPPORTED;
-    // one head's K (or V) rows are addressed with 32-bit byte offsets
-    if ((int64_t)seqlen_k * head_dim >= ((int64_t)1 << 31)) return OSM_ERR_UNSUPPORTED;
+    // one head's rows of K, V, Q (E4M3) and O (bf16) are addressed with 32-bit byte offsets
+    if ((int64_t)seqlen_k * head_dim >= ((int64_t)1 << 31) ||
+        (int64_t)seqlen_q * head_dim * 2 >= ((int64_t)1 << 31))
+        return OSM_ERR_UNSUPPORTED;
     if (seqlen_q == 0) return OSM_OK;
     if (!q || !o || (seqlen_k > 0 && (!k || !v))) return OSM_ERR_NULL;
     // operands are read 16 bytes at a time

@@ -142,8 +142,8 @@ osm_status osm_softmax_rows_twopass(const float *x, float *y, int64_t rows, int6
  * Errors: OSM_ERR_NULL, OSM_ERR_SHAPE (non-positive batch/heads/head_dim,
  * negative seqlens, heads_q % heads_kv != 0, scale not finite or <= 0),
  * OSM_ERR_UNSUPPORTED (other dtype or head_dim, a misaligned pointer,
- * batch * heads_q >= 2^31, or one head's K rows spanning 2 GiB or more:
- * seqlen_k >= 2^23 at head_dim 128), OSM_ERR_HIP.
+ * batch * heads_q >= 2^31, or one head's K, Q or O rows spanning 2 GiB or
+ * more: seqlen_k or seqlen_q >= 2^23 at head_dim 128), OSM_ERR_HIP.
  */
 osm_status osm_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                         osm_dtype dtype, int32_t batch, int32_t heads_q, int32_t heads_kv,
@@ -177,7 +177,8 @@ osm_status osm_attn_fwd(const void *q, const void *k, const void *v, void *o, fl
  * aligned.
  * Errors: OSM_ERR_NULL, OSM_ERR_SHAPE (as osm_attn_fwd, or v_scale not
  * finite), OSM_ERR_UNSUPPORTED (other head_dim, a misaligned pointer,
- * batch * heads_q >= 2^31, seqlen_k >= 2^24), OSM_ERR_HIP.
+ * batch * heads_q >= 2^31, seqlen_k >= 2^24, seqlen_q >= 2^23: one head's
+ * bf16 O rows spanning 2 GiB), OSM_ERR_HIP.
  */
 osm_status osm_attn_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
                             int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t seqlen_q,

@@ -112,6 +112,8 @@ def test_attn_fwd_validation(lib):
     assert call(dtype=osm.OSM_F32) == 3
     assert call(d=64) == 3
     assert call(Nk=1 << 23) == 3                    # one head's K rows would span 2 GiB
+    assert call(Nq=1 << 23) == 3                    # one head's Q (and O) rows would span 2 GiB
+    assert call(Nq=(1 << 23) - 1, q=None) == 1      # just below: accepted as far as the NULL check
     assert call(q=None) == 1
     assert call(o=None) == 1
     assert call(k=None) == 1
@@ -240,6 +242,8 @@ def test_attn_fwd_fp8_validation(lib):
     assert call(causal=3) == 2
     assert call(d=64) == 3
     assert call(Nk=1 << 24) == 3
+    assert call(Nq=1 << 23) == 3                     # one head's bf16 O rows would span 2 GiB
+    assert call(Nq=(1 << 23) - 1, q=None) == 1
     assert call(Nq=0, q=None) == 0
     assert call(q=None) == 1
     assert call(v=None) == 1
