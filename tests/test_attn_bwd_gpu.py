@@ -191,3 +191,30 @@ def test_full_size_causal_varlen_heads(orc):
         assert not np.isnan(gh).any()
         for b, L in enumerate(lens):
             assert np.all(gh[b, :, L:] == 0.0)
+
+
+def test_random_sweep(orc):
+    """Seeded random configurations against the oracle's gradients: GQA
+    group, ragged lengths, masks, scale, NaN-poisoned padding."""
+    g = inputs.rng(4545)
+    for case in range(20):
+        B = int(g.integers(1, 3))
+        Hkv = int(g.choice([1, 2]))
+        Hq = Hkv * int(g.choice([1, 2, 4]))
+        Nq = int(g.integers(1, 400))
+        Nk = int(g.integers(1, 400))
+        causal = bool(g.random() < 0.5)
+        mode = int(g.integers(0, 3))
+        sq = sk = None
+        if mode >= 1:
+            sk = g.integers(1, Nk + 1, size=B).astype(np.int32)
+        if mode == 2:
+            sq = g.integers(1, Nq + 1, size=B).astype(np.int32)
+        scale = float(g.uniform(0.03, 0.12))
+        announce(f"bwd sweep {case}: B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} causal={causal} "
+                 f"seqlens_q={None if sq is None else sq.tolist()} seqlens_k={None if sk is None else sk.tolist()}")
+        seed = 9000 + case
+        inp = inputs.attention_inputs(B, Hq, Hkv, Nq, Nk, 128, seed=seed, causal=causal, scale=scale,
+                                      seqlens_q=sq, seqlens_k=sk, poison=sk is not None)
+        do = inputs.output_grad(B, Hq, Nq, 128, seed + 1, seqlens_q=sq, poison=sq is not None)
+        check_all(run(inp, do), oracle(orc, inp, do), f"sweep {case}")

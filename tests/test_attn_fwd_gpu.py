@@ -323,3 +323,63 @@ def test_scheduled_grid(orc, B, Hq, Hkv, Nq, Nk, causal, lq, lk):
     rows = _sample_rows(np.random.default_rng(Nq + B), B, Hq, Nq, 300, np.maximum(lq, 1))
     o_ref, lse_ref = oracle(orc, inp, rows=rows)
     check_attn(oh.reshape(-1, 128)[rows], lh.reshape(-1)[rows], o_ref, lse_ref, "bf16")
+
+
+def _sweep_config(g, many_heads):
+    """One random configuration: GQA group, ragged lengths, masks, scale.
+    With many_heads, more query blocks than compute units (persistent and
+    scheduled grids); otherwise one block per workgroup."""
+    if many_heads:
+        B = int(g.integers(1, 4))
+        Hkv = int(g.choice([8, 16]))
+        Hq = Hkv * int(g.choice([1, 2, 4]))
+        nqb = 256 // (B * Hq) + 1        # query blocks per head: more blocks than 256 CUs
+        Nq = int(g.integers((nqb - 1) * 256 + 1, nqb * 256 + 1))
+        Nk = int(g.integers(1, 450))
+    else:
+        B = int(g.integers(1, 4))
+        Hkv = int(g.choice([1, 2]))
+        Hq = Hkv * int(g.choice([1, 2, 4]))
+        Nq = int(g.integers(1, 520))
+        Nk = int(g.integers(1, 600))
+    causal = bool(g.random() < 0.5)
+    mode = int(g.integers(0, 3))          # 0: full lengths, 1: key lengths, 2: both
+    sq = sk = None
+    if mode >= 1:
+        sk = g.integers(0, Nk + 1, size=B).astype(np.int32)
+    if mode == 2:
+        sq = g.integers(0, Nq + 1, size=B).astype(np.int32)
+    scale = float(g.uniform(0.03, 0.25))
+    return B, Hq, Hkv, Nq, Nk, causal, sq, sk, scale
+
+
+@pytest.mark.parametrize("many_heads", [False, True])
+def test_random_sweep(orc, many_heads):
+    """Seeded random configurations against the oracle: every row for the
+    small ones, 200 sampled rows plus every padded row for the many-head
+    ones (which run on the persistent or scheduled grids).  Padding is
+    NaN-poisoned wherever a length array marks it."""
+    g = inputs.rng(4242 + many_heads)
+    n = 16 if many_heads else 60
+    for case in range(n):
+        B, Hq, Hkv, Nq, Nk, causal, sq, sk, scale = _sweep_config(g, many_heads)
+        announce(f"fwd sweep {case}: B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} causal={causal} "
+                 f"seqlens_q={None if sq is None else sq.tolist()} seqlens_k={None if sk is None else sk.tolist()} "
+                 f"scale={scale:.4f}")
+        inp = inputs.attention_inputs(B, Hq, Hkv, Nq, Nk, 128, seed=5000 + 100 * many_heads + case, causal=causal,
+                                      scale=scale, seqlens_q=sq, seqlens_k=sk, poison=sk is not None)
+        if many_heads:
+            assert B * Hq * ((Nq + 255) // 256) > torch_mod().cuda.get_device_properties(0).multi_processor_count
+        o, lse = run(inp)
+        oh, lh = host(o), host(lse)
+        assert not np.isnan(oh).any() and not np.isnan(lh).any()
+        if many_heads:
+            rows = _sample_rows(np.random.default_rng(case), B, Hq, Nq, 200)
+            o_ref, lse_ref = oracle(orc, inp, rows=rows)
+            check_attn(oh.reshape(-1, 128)[rows], lh.reshape(-1)[rows], o_ref, lse_ref, "bf16")
+        else:
+            o_ref, lse_ref = oracle(orc, inp)
+            check_attn(oh, lh, o_ref, lse_ref, "bf16")
+        if sq is not None:
+            for b, L in enumerate(sq):       # padded query rows: exactly 0 / -inf
+                assert np.all(oh[b, :, L:] == 0.0) and np.all(np.isneginf(lh[b, :, L:]))

@@ -143,3 +143,26 @@ def test_every_split_instantiation(orc, dtype, d, group):
     qw, kw, vw = e_inp.widened()
     oe_ref, le_ref = orc.attention(qw, kw, vw, scale=e_inp.scale)
     check_attn(host(oe), host(le), oe_ref.reshape(-1, d), le_ref.reshape(-1), dtype)
+
+
+def test_random_sweep(orc):
+    """Seeded random decode configurations against the oracle: element type,
+    head dim, GQA group, cache length, per-sequence lengths (0 included),
+    piece size, NaN poison past the lengths."""
+    g = inputs.rng(4343)
+    for case in range(40):
+        dtype = str(g.choice(["bf16", "f32"]))
+        d = int(g.choice([64, 128]))
+        group = int(g.choice([1, 2, 4, 8]))
+        hkv = int(g.choice([1, 2, 4]))
+        B = int(g.integers(1, 5))
+        lmax = int(g.integers(1, 3000))
+        split = 64 * int(g.integers(1, 1 + min(128, 16384 // (64 * group))))
+        lens = g.integers(0, lmax + 1, size=B).astype(np.int32)
+        announce(f"decode sweep {case}: {dtype} d={d} B={B} hq={hkv * group} hkv={hkv} lmax={lmax} "
+                 f"split={split} lens={lens.tolist()}")
+        inp = inputs.attention_inputs(B, hkv * group, hkv, 1, lmax, d, seed=6000 + case, dtype=dtype,
+                                      seqlens_k=lens, poison=True)
+        o, lse = run_decode(inp, split)
+        o_ref, lse_ref = oracle_decode(orc, inp)
+        check_attn(host(o), host(lse), o_ref, lse_ref, dtype)
