@@ -77,3 +77,20 @@ def test_bench_shape_sampled(orc):
     four chunks of 4096 keys, 512-key pieces."""
     announce("extend B16 Hq32 Hkv8 d128 bf16, 4 x 4096 keys, split 512")
     stream(orc, 16, 32, 8, 128, "bf16", [4096] * 4, 5300, split=512, check_every=False)
+
+
+def test_random_sweep(orc):
+    """Seeded random streams: element type, head dim, group, chunk sizes
+    (1 key to several pieces), piece size; the finalized state checked after
+    the last chunk of each stream."""
+    g = inputs.rng(4747)
+    for case in range(16):
+        dtype = str(g.choice(["bf16", "f32"]))
+        d = int(g.choice([64, 128]))
+        group = int(g.choice([1, 2, 4, 8]))
+        Hkv = int(g.choice([1, 2]))
+        B = int(g.integers(1, 4))
+        chunks = [int(g.integers(1, 900)) for _ in range(int(g.integers(1, 6)))]
+        split = 64 * int(g.integers(1, 1 + min(16, 16384 // (64 * group))))
+        announce(f"extend sweep {case}: {dtype} d={d} B={B} Hq={Hkv * group} Hkv={Hkv} chunks={chunks} split={split}")
+        stream(orc, B, Hkv * group, Hkv, d, dtype, chunks, 9500 + case, split=split, check_every=False)

@@ -256,3 +256,24 @@ def test_twopass_row_stride(orc, cols, ld_x, ld_y):
     y_ref, m_ref, l_ref = orc.softmax_rows(x)
     check_softmax(y[:, :cols], m, l, y_ref, m_ref, l_ref)
     assert np.all(y[:, cols:] == np.float32(-7.25))
+
+
+def test_random_sweep(orc):
+    """Seeded random rows against the oracle through both the one-read and
+    the two-pass kernels: widths on both sides of the resident limit,
+    spikes, -inf entries and whole -inf rows, large offsets."""
+    g = inputs.rng(4646)
+    for case in range(30):
+        rows = int(g.integers(1, 40))
+        cols = int(g.choice([int(g.integers(1, 300)), int(g.integers(300, 20000)), int(g.integers(60000, 140000))]))
+        x = inputs.softmax_rows_input(rows, cols, seed=7000 + case)
+        x += np.float32(g.uniform(-50, 50))
+        if g.random() < 0.5:
+            x[g.integers(0, rows), :] = -np.inf
+        if g.random() < 0.5:
+            x[:, g.integers(0, cols, size=max(1, cols // 5))] = -np.inf
+        for two_pass in (False, True):
+            announce(f"softmax sweep {case}: rows={rows} cols={cols} two_pass={two_pass}")
+            y, m, l = run(x, two_pass)
+            y_ref, m_ref, l_ref = orc.softmax_rows(x)
+            check_softmax(y, m, l, y_ref, m_ref, l_ref)
