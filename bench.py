@@ -20,6 +20,8 @@ inputs already resident in HBM:
                                     matrix instruction; peak 5033 TFLOP/s)
   bwd       osm_attn_bwd            backward of the fwd workload (dQ, dK, dV from O, LSE, dO)
   bwd_causal osm_attn_bwd           backward of the fwd_causal workload
+  fwd_d64   osm_attn_fwd            bf16 B=4 H=64 N=4096 d=64, non-causal (the headline's flops
+                                    and bytes at head dim 64)
 
 Each call is timed with HIP events on the stream it runs on (torch's current
 stream); ``value`` is the headline forward's TFLOP/s (mean over the timed
@@ -62,9 +64,10 @@ def bf16_dev(bits, torch):
 KERNEL_SOURCES = {"fwd": "attn_fwd.hip", "fwd_causal": "attn_fwd.hip", "softmax": "softmax_rows.hip",
                   "softmax_2pass": "softmax_rows.hip",
                   "decode": "decode.hip", "merge_lse": "merge_lse.hip", "extend": "decode.hip",
-                  "bwd": "attn_bwd.hip", "bwd_causal": "attn_bwd.hip", "fwd_fp8": "attn_fwd_fp8.hip"}
+                  "bwd": "attn_bwd.hip", "bwd_causal": "attn_bwd.hip", "fwd_fp8": "attn_fwd_fp8.hip",
+                  "fwd_d64": "attn_fwd.hip"}
 WORKLOADS = ["softmax", "softmax_2pass", "fwd", "fwd_causal", "decode", "merge_lse", "extend", "bwd",
-             "bwd_causal", "fwd_fp8"]
+             "bwd_causal", "fwd_fp8", "fwd_d64"]
 
 
 def source_hash(name):
@@ -191,7 +194,8 @@ def summarize(name, trace_dir, out):
     kern = {"fwd": "attn_fwd_bf16", "fwd_causal": "attn_fwd_bf16", "softmax": "softmax_rows_resident",
             "softmax_2pass": "softmax_rows_streaming",
             "decode": "decode_split", "merge_lse": "merge_lse", "extend": "decode_split",
-            "bwd": "attn_bwd_dkdv", "bwd_causal": "attn_bwd_dkdv", "fwd_fp8": "attn_fwd_fp8"}[name]
+            "bwd": "attn_bwd_dkdv", "bwd_causal": "attn_bwd_dkdv", "fwd_fp8": "attn_fwd_fp8",
+            "fwd_d64": "attn_fwd_bf16_d64"}[name]
     lines = [f"# rocprofv3 summary: {name}", ""]
     trace = os.path.join(trace_dir, "trace", "run_kernel_trace.csv")
     avg_ns = None
@@ -220,7 +224,7 @@ def summarize(name, trace_dir, out):
                 "decode": ("decode_split", 128),
                 "merge_lse": ("merge_lse", None), "extend": ("decode_split", 8),
                 "bwd": ("attn_bwd_dkdv<false>", None), "bwd_causal": ("attn_bwd_dkdv<true>", None),
-                "fwd_fp8": ("attn_fwd_fp8", None)}[name]
+                "fwd_fp8": ("attn_fwd_fp8", None), "fwd_d64": ("attn_fwd_bf16_d64_persist", None)}[name]
         for (short, wg), d in groups.items():
             if want[0] in short and (want[1] is None or wg == want[1]):
                 avg_ns = sum(d) / len(d)
@@ -381,6 +385,16 @@ def main():
                                                 dq=g3[0], dk=g3[1], dv=g3[2])
             # five products per (query, key) pair: S again, dP, dV, dQ, dK
             work["bwd"] = ("mfma", 10.0 * B * H * N * N * d, "backward of B4 H32 N4096 d128 non-causal")
+    if "fwd_d64" in names:
+        log("inputs: fwd B4 H64 N4096 d64")
+        inp64 = inputs.attention_inputs(4, 64, 64, 4096, 4096, 64, seed=inputs.SEED_BASE + 11)
+        q64, k64, v64 = (bf16_dev(a, torch) for a in (inp64.q, inp64.k, inp64.v))
+        o64 = torch.empty_like(q64)
+        l64 = torch.empty(q64.shape[:3], dtype=torch.float32, device="cuda")
+        scale64 = inp64.scale
+        calls["fwd_d64"] = lambda: osm.attn_fwd(q64, k64, v64, scale=scale64, out=o64, lse=l64)
+        work["fwd_d64"] = ("mfma", 4.0 * 4 * 64 * 4096 * 4096 * 64, "B4 H64 N4096 d64 non-causal")
+        del inp64
     if "fwd_causal" in names or "bwd_causal" in names:
         log("inputs: fwd causal B8 H16 N8192 d128 varlen")
         inp4 = inputs.config4()
@@ -528,7 +542,7 @@ def main():
            "config": {"workload": f"attn_fwd {hc['workload']}" if head == "fwd" else hc["workload"],
                       "step": "softmax_rows + softmax_rows_twopass + attn_fwd (non-causal) + attn_fwd (causal varlen) "
                               "+ attn_decode_splitkv + merge_lse + attn_extend + attn_bwd (non-causal) "
-                              "+ attn_bwd (causal varlen) + attn_fwd_fp8" if args.only is None
+                              "+ attn_bwd (causal varlen) + attn_fwd_fp8 + attn_fwd (head dim 64)" if args.only is None
                               else args.only,
                       "global_batch": 4, "seq_len": 4096, "parallelism": "none (1 GPU)"},
            "roofline": roofline, "components": comps}

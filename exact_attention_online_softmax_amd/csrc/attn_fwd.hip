@@ -76,16 +76,37 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int D = 128;            // head dim
 constexpr int NW = 4;             // wavefronts per workgroup (one per SIMD)
 constexpr int QW = 64;            // queries per wavefront (two 32-query blocks)
 constexpr int BQ = QW * NW;       // queries per workgroup
 constexpr int BK = 32;            // keys per tile
 constexpr int NT = 64 * NW;       // threads per workgroup
-constexpr int ROWB = D * 2;       // bytes per K/V row in LDS (unpadded)
-constexpr int TILEB = BK * ROWB;  // bytes per K or V tile (8 KiB)
-constexpr int LPW = TILEB / 1024 / NW;  // 1 KiB loads per wave per K (or V) tile
 constexpr int AHEAD = 3;          // tiles loaded ahead of the one being computed
+
+// Sizes that follow from the head dim (128 or 64).
+template <int HD> struct Geo {
+    static constexpr int ROWB = HD * 2;             // bytes per K/V/Q row in LDS (unpadded)
+    static constexpr int CH = ROWB / 16;            // 16-byte chunks per row
+    static constexpr int RPB = 1024 / ROWB;         // rows per 1 KiB block of an LDS-DMA load
+    static constexpr int TILEB = BK * ROWB;         // bytes per K or V tile (8 or 4 KiB)
+    static constexpr int LPW = TILEB / 1024 / NW;   // 1 KiB loads per wave per K (or V) tile
+    static constexpr int KS = HD / 16;              // k-steps of the score product
+    static constexpr int NDT = HD / 32;             // 32-dim blocks of the output
+    static constexpr int QL = QW * ROWB / 1024;     // 1 KiB loads per wave copying a block's Q
+    static constexpr int STEPS = 2 * KS + 4 * NDT;  // MFMA steps of the tile body
+};
+
+// LDS swizzles at 16-byte granularity (chunk c of row r sits in slot
+// c ^ sw(r)).  K and Q rows: the row-wise operand reads (16 lanes of a
+// ds_read_b128, 16 rows, one chunk) hit 16 distinct 16-byte units of a
+// 256-byte bank window: at 256-byte rows sw = r % 16; at 128-byte rows two
+// rows share a window, so the eight rows of each parity need distinct slots,
+// sw = (r / 2) % 8.  V rows: a transposing read (32 lanes, rows 4a .. 4a+3,
+// four adjacent chunks, 8 bytes each) hits 32 distinct 8-byte units: at
+// 256-byte rows sw = 4 (r % 4); at 128-byte rows rows r and r + 2 share a
+// window half, sw = 4 ((r / 2) % 2).
+template <int HD> __device__ __forceinline__ int swk(int r) { return HD == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int HD> __device__ __forceinline__ int swv(int r) { return HD == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
 
 template <int N> struct Slot { static constexpr int value = N; };
 
@@ -101,8 +122,11 @@ template <int B, int E, typename F> __device__ __forceinline__ void static_for(F
 // element (n%8) + 8 (n/16) of that block's scores) in the order the P~V
 // steps consume them, in groups g = -1 .. kGroups-1: items
 // [item_lo(g), item_lo(g+1)), four in the first group, then one or two.
-constexpr int kGroups = 22;
-constexpr int item_lo(int g) { return g < 0 ? 0 : 4 + (g * 28) / kGroups; }
+// (22 groups over the 32 steps of the head-dim-128 body, 9 over the 16
+// steps of the head-dim-64 body: each P~ operand is converted at least one
+// full step before its first P~V step)
+template <int HD> constexpr int k_groups() { return HD == 128 ? 22 : 9; }
+template <int HD> constexpr int item_lo(int g) { return g < 0 ? 0 : 4 + (g * 28) / k_groups<HD>(); }
 constexpr int item_qb(int n) { return (n >> 3) & 1; }
 constexpr int item_i(int n) { return (n & 7) + 8 * (n >> 4); }
 
@@ -127,10 +151,14 @@ __device__ __forceinline__ void acc_zero(f32x16 &acc, const bf16x8 &z) {
 
 // Before ordinary code reads accumulators written by mfma_acc: wait out the
 // MFMA result latency (the compiler model asks for 12 wait states; 24 here).
-__device__ __forceinline__ void acc_settle(f32x16 (&o)[2][4]) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]),
-                   "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
+template <int NDT> __device__ __forceinline__ void acc_settle(f32x16 (&o)[2][NDT]) {
+    if constexpr (NDT == 4)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]),
+                       "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
+    else
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[1][0]), "+a"(o[1][1]));
 }
 
 // transposing LDS read: see the header comment for the lane layout
@@ -165,11 +193,10 @@ constexpr int kRsrcWord3 = 0x00020000;
 
 // s_waitcnt encodings (gfx9): vmcnt in bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8; a field at its maximum does not wait.
-constexpr int kWaitVm0 = 0x0F70;   // vmcnt(0)
-constexpr int kWaitVm4 = 0x0F74;   // vmcnt(4): one tile's loads of this wave may stay in flight
-constexpr int kWaitVm20 = 0x4F74;  // vmcnt(20)
+constexpr int vmcnt_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+constexpr int kWaitVm0 = vmcnt_wait(0);
 constexpr int kWaitLgkm0 = 0xC07F; // lgkmcnt(0)
-static_assert(2 * LPW == 4, "kWaitVm4 assumes four loads per wave per tile");
+static_assert(vmcnt_wait(4) == 0x0F74 && vmcnt_wait(20) == 0x4F74, "vmcnt encoding");
 
 // (batch, head, KV head, first query, valid query and key lengths) of a
 // query block
@@ -199,14 +226,22 @@ constexpr int kSchedFixed = 10;     // per-block cost outside the tile loop, in 
 //    XCD's workgroups run one or two heads at a time and share their K and V
 //    in L2.  Blocks with no visible key or no valid query only write O = 0,
 //    LSE = -inf; they come last, round robin over the slots.
-template <int MODE>
+template <int MODE, int HD>
 __device__ __forceinline__ void
 attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
               const uint16_t *__restrict__ V, uint16_t *__restrict__ O,
               float *__restrict__ LSE, int B, int Hq, int Hkv, int Nq, int Nk,
               const int32_t *__restrict__ seqlens_q, const int32_t *__restrict__ seqlens_k,
               float scale_log2, int causal_arg, int nqb, int xcd_heads, int nblocks) {
-    // ring of four K slots and four V slots, 8 KiB each
+    using G = Geo<HD>;
+    constexpr int D = HD, ROWB = G::ROWB, CH = G::CH, RPB = G::RPB, TILEB = G::TILEB, LPW = G::LPW;
+    constexpr int KS = G::KS, NDT = G::NDT, QL = G::QL, STEPS = G::STEPS, kGroups = k_groups<HD>();
+    constexpr int kLogCH = CH == 16 ? 4 : 3;
+    // tiles of this wave in flight at the top of an iteration: one; with the
+    // copy of the next block's Q behind them (iterations 0 and 1), also that
+    constexpr int kWaitVmTile = vmcnt_wait(2 * LPW);
+    constexpr int kWaitVmQ = vmcnt_wait(2 * LPW + QL);
+    // ring of four K slots and four V slots (8 KiB each at head dim 128)
     __shared__ __attribute__((aligned(1024))) uint8_t k0[TILEB], k1[TILEB], k2[TILEB], k3[TILEB];
     __shared__ __attribute__((aligned(1024))) uint8_t v0[TILEB], v1[TILEB], v2[TILEB], v3[TILEB];
     // Q of the block (PERSIST), rows swizzled like K
@@ -395,13 +430,13 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 
         // O~^T accumulators, zeroed in the AGPRs by an MFMA of zeros (so they
         // never pass through VGPRs)
-        f32x16 oacc[2][4];
+        f32x16 oacc[2][NDT];
         {
             const bf16x8 z8 = {};
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt) acc_zero(oacc[qb][dt], z8);
+                for (int dt = 0; dt < NDT; ++dt) acc_zero(oacc[qb][dt], z8);
         }
         f32x16 sacc[2];          // S^T of the tile whose softmax is next
 #pragma unroll
@@ -434,10 +469,10 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             const int blk = LPW * wave + i;
-            const int row = 4 * blk + (lane >> 4);
-            const int s = lane & 15;
-            kld[i] = row * ROWB + ((s ^ (row & 15)) << 4);
-            vld[i] = row * ROWB + ((s ^ ((row & 3) << 2)) << 4);
+            const int row = RPB * blk + (lane >> kLogCH);
+            const int s = lane & (CH - 1);
+            kld[i] = row * ROWB + ((s ^ swk<HD>(row)) << 4);
+            vld[i] = row * ROWB + ((s ^ swv<HD>(row)) << 4);
         }
         struct TileRsrc {
             __amdgpu_buffer_rsrc_t k, v;
@@ -499,10 +534,10 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                 const_cast<uint16_t *>(Q) + ((size_t)(n.b * Hq + n.h) * Nq + n.q0) * D, 0,
                 max(0, (SCHED ? n.Lq : Nq) - n.q0) * ROWB, kRsrcWord3);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int blk = 16 * wave + i, row = 4 * blk + (lane >> 4), sl = lane & 15;
+            for (int i = 0; i < QL; ++i) {
+                const int blk = QL * wave + i, row = RPB * blk + (lane >> kLogCH), sl = lane & (CH - 1);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3))) *)(qs + blk * 1024), 16,
-                                                         row * ROWB + ((sl ^ (row & 15)) << 4), 0, 0, 0);
+                                                         row * ROWB + ((sl ^ swk<HD>(row)) << 4), 0, 0, 0);
             }
         };
         if (PERSIST && first) {
@@ -516,19 +551,19 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 
         // ---- Q fragments (B operands of S^T = K Q^T), kept in registers -----
         // lane l holds Q[qw0 + 32 qb + c][64 g + 8 ks + 0..7] for ks = 0..7
-        bf16x8 qf[2][8];
+        bf16x8 qf[2][KS];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const int qi = qw0 + 32 * qb + c;
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
+            for (int ks = 0; ks < KS; ++ks) {
                 if constexpr (PERSIST) {
                     // this wave's rows of qs: row 64 wave + 32 qb + c, chunk 8 g + ks
                     const int row = QW * wave + 32 * qb + c;
-                    qf[qb][ks] = *reinterpret_cast<const bf16x8 *>(qs + row * ROWB + (((8 * g + ks) ^ (row & 15)) << 4));
+                    qf[qb][ks] = *reinterpret_cast<const bf16x8 *>(qs + row * ROWB + ((((CH / 2) * g + ks) ^ swk<HD>(row)) << 4));
                 } else {
                     uint4 w = make_uint4(0, 0, 0, 0);
-                    if (qi < Lq) w = *reinterpret_cast<const uint4 *>(Q + (qhead + qi) * D + 64 * g + 8 * ks);
+                    if (qi < Lq) w = *reinterpret_cast<const uint4 *>(Q + (qhead + qi) * D + (D / 2) * g + 8 * ks);
                     qf[qb][ks] = __builtin_bit_cast(bf16x8, w);
                 }
             }
@@ -537,18 +572,18 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 
         // per-lane LDS byte offsets (within a tile) of the QK A operand: row c,
         // chunk 8 g + ks -> slot (8 g + ks) ^ (c % 16)
-        uint32_t koff[8];
+        uint32_t koff[KS];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) koff[ks] = c * ROWB + ((((8 * g) ^ (c & 15)) ^ ks) << 4);
+        for (int ks = 0; ks < KS; ++ks) koff[ks] = c * ROWB + (((((CH / 2) * g) ^ swk<HD>(c)) ^ ks) << 4);
         // transposing V read: 16-lane group q = lane/16, index i = lane%16:
         // row kb + i/4 (kb a multiple of 4), dims 32 dt + 16 (q%2) + 4 (i%4) ..+3
         const int trq = lane >> 4, tri = lane & 15;
         const int tr_row = 4 * (trq >> 1) + (tri >> 2);
-        const int tr_sw = (tri >> 2) << 2;                  // 4 * (row % 4)
+        const int tr_sw = swv<HD>(tr_row);
         const int tr_half = (tri & 1) * 8;
-        uint32_t voff[4];
+        uint32_t voff[NDT];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+        for (int dt = 0; dt < NDT; ++dt) {
             const int chunk = 4 * dt + 2 * (trq & 1) + ((tri & 3) >> 1);
             voff[dt] = tr_row * ROWB + ((chunk ^ tr_sw) << 4) + tr_half;
         }
@@ -558,7 +593,7 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
         auto qk = [&](const uint8_t *kb, f32x16 (&s)[2]) __attribute__((always_inline)) {
             const f32x16 zero = {};
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
+            for (int ks = 0; ks < KS; ++ks) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb + koff[ks]);
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
@@ -621,7 +656,7 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                                       : (m[qb] == kNegInf ? 0.0f : fast_exp2((m[qb] - mn) * scale_log2));
                     l[qb] *= alpha;
 #pragma unroll
-                    for (int dt = 0; dt < 4; ++dt)
+                    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
                         for (int i = 0; i < 16; ++i) oacc[qb][dt][i] *= alpha;
                     m[qb] = mn;
@@ -653,9 +688,9 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
         // copy and the stores are not waited for there.
         auto enter = [&](int j) __attribute__((always_inline)) {
             if (PERSIST && has_next && j < 2)
-                __builtin_amdgcn_s_waitcnt(kWaitVm20);
+                __builtin_amdgcn_s_waitcnt(kWaitVmQ);
             else
-                __builtin_amdgcn_s_waitcnt(kWaitVm4);
+                __builtin_amdgcn_s_waitcnt(kWaitVmTile);
             tile_barrier();
         };
         auto idle = [&](auto S, int j) __attribute__((always_inline)) {
@@ -685,15 +720,15 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
             float rs[2][4];      // four partial row sums per block, set by their first item
             bf16x8 pb[2][2];
             f32x16 sn[2];
-            bf16x8 ka[8];
-            bf16x8 va[2][4];
+            bf16x8 ka[KS];
+            bf16x8 va[2][NDT];
             float px[2][6];
 
             // stage 0 (fma), 1 (exp2) or 2 (sum, and the bf16 operand after the
             // eighth item of an operand) of the items of group G
             auto stage = [&](auto STAGE, auto G) __attribute__((always_inline)) {
                 constexpr int stg = decltype(STAGE)::value, grp = decltype(G)::value - 1;
-                static_for<item_lo(grp), item_lo(grp + 1)>([&](auto N) __attribute__((always_inline)) {
+                static_for<item_lo<HD>(grp), item_lo<HD>(grp + 1)>([&](auto N) __attribute__((always_inline)) {
                     constexpr int n = decltype(N)::value, qb = item_qb(n), i = item_i(n);
                     if constexpr (stg == 0) {
                         e[qb][i] = fmaf(sacc[qb][i], scale_log2, -msub[qb]);
@@ -730,43 +765,56 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
             rk(1);
             stage(Slot<0>{}, Slot<0>{});          // fma of group -1
             __builtin_amdgcn_sched_barrier(0);
-            static_for<0, 32>([&](auto ST) __attribute__((always_inline)) {
+            static_for<0, STEPS>([&](auto ST) __attribute__((always_inline)) {
                 constexpr int st = decltype(ST)::value;
-                if constexpr (st < 16) {
+                constexpr int SS = 2 * KS;       // score steps, then P~V steps
+                if constexpr (st < SS) {
                     constexpr int ks = st >> 1, qb = st & 1;
                     sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[qb][ks], ks ? sn[qb] : zero, 0, 0, 0);
                 } else {
-                    constexpr int t = st - 16, hh = t >> 3, dt = (t >> 1) & 3, qb = t & 1;
+                    constexpr int t = st - SS, hh = t / (2 * NDT), dt = (t >> 1) % NDT, qb = t & 1;
                     mfma_acc(oacc[qb][dt], va[hh][dt], pb[qb][hh]);
                 }
                 // this wave's loads of tile j+3, one every eight steps
                 if constexpr ((st & 7) == 3) load1(lr, kd, vd, st >> 3);
                 // K operand of step 2 ks is read at step 2 ks - 4
-                if constexpr (st < 12 && !(st & 1)) rk((st + 4) >> 1);
-                // V operand of step 16 + 8 hh + 2 dt is read five steps earlier
-                if constexpr (st >= 11 && st < 27 && (st & 1)) rv((st - 11) >> 3, ((st - 11) >> 1) & 3);
+                if constexpr (st < SS - 4 && !(st & 1)) rk((st + 4) >> 1);
+                // V operand of step SS + 2 NDT hh + 2 dt is read five steps earlier
+                if constexpr (st >= SS - 5 && st < SS - 5 + 4 * NDT && ((st - (SS - 5)) & 1) == 0)
+                    rv(((st - (SS - 5)) >> 1) / NDT, ((st - (SS - 5)) >> 1) % NDT);
                 // exponential pipeline: fma of group st, exp2 of st-1, sum of st-2
                 // (Slot<g + 1> names group g)
                 if constexpr (st < kGroups) stage(Slot<0>{}, Slot<st + 1>{});
                 if constexpr (st <= kGroups) stage(Slot<1>{}, Slot<st>{});
                 if constexpr (st >= 1 && st <= kGroups + 1) stage(Slot<2>{}, Slot<st - 1>{});
                 // masked iterations: mask S(j+1) once its MFMAs are done
-                if constexpr (masked && st >= 17 && st < 25) {
-                    constexpr int qb = (st - 17) >> 2, r = (st - 17) & 3;
-                    const int qi = qw0 + 32 * qb + c;
-                    const int lim = (causal ? min(Lk - 1, qi) : Lk - 1) - (j + 1) * BK - 4 * g;
+                // (the eight (qb, r) row groups over 2 NDT steps from step SS + 1:
+                // one per step at head dim 128, two at 64)
+                constexpr int kMaskPer = 8 / (2 * NDT);
+                if constexpr (masked && st > SS && st <= SS + 2 * NDT) {
+                    constexpr int k = (st - SS - 1) * kMaskPer;
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if (8 * r + u > lim) sn[qb][4 * r + u] = kNegInf;
+                    for (int kk = k; kk < k + kMaskPer; ++kk) {
+                        const int qb = kk >> 2, r = kk & 3;
+                        const int qi = qw0 + 32 * qb + c;
+                        const int lim = (causal ? min(Lk - 1, qi) : Lk - 1) - (j + 1) * BK - 4 * g;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            if (8 * r + u > lim) sn[qb][4 * r + u] = kNegInf;
+                    }
                 }
                 // maximum of tile j+1: five independent max3 per block, then two
-                if constexpr (st >= 25 && st < 30) {
-                    constexpr int k = st - 25;
+                // (head dim 64: k = 0..2 at step 13, 3..4 at 14, joined at 15)
+                static_for<0, 5>([&](auto KK) __attribute__((always_inline)) {
+                    constexpr int k = decltype(KK)::value;
+                    constexpr int kst = HD == 128 ? 25 + k : (k < 3 ? 13 : 14);
+                    if constexpr (st == kst) {
 #pragma unroll
-                    for (int qb = 0; qb < 2; ++qb)
-                        px[qb][k] = fmaxf(fmaxf(sn[qb][3 * k], sn[qb][3 * k + 1]), sn[qb][3 * k + 2]);
-                }
-                if constexpr (st == 30) {
+                        for (int qb = 0; qb < 2; ++qb)
+                            px[qb][k] = fmaxf(fmaxf(sn[qb][3 * k], sn[qb][3 * k + 1]), sn[qb][3 * k + 2]);
+                    }
+                });
+                if constexpr (st == (HD == 128 ? 30 : 15)) {
 #pragma unroll
                     for (int qb = 0; qb < 2; ++qb) {
                         px[qb][0] = fmaxf(fmaxf(px[qb][0], px[qb][1]), px[qb][2]);
@@ -864,7 +912,7 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
             if (qi < Nq) {
                 uint16_t *orow = O + (qhead + qi) * D;
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
+                for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         uint2 w;
@@ -892,23 +940,33 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
         const int32_t *__restrict__ seqlens_q, const int32_t *__restrict__ seqlens_k,               \
         float scale_log2, int causal, int nqb, int xcd_heads, int nblocks
 
-// one query block per workgroup
-__global__ void __launch_bounds__(NT, 1) attn_fwd_bf16_d128(OSM_ATTN_FWD_PARAMS) {
-    attn_fwd_body<0>(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, seqlens_q, seqlens_k, scale_log2, causal, nqb,
-                     xcd_heads, nblocks);
-}
+// Workgroups resident per compute unit: at head dim 128 one (each wave has
+// the 512 registers of its SIMD); at 64 two (a wave fits in 256 registers and
+// a workgroup in 72 KiB of LDS), so that one wave's exponentials overlap the
+// other's matrix products -- the vector work per MFMA is twice that of head
+// dim 128.
+template <int HD> constexpr int kWgPerCu = HD == 128 ? 1 : 2;
 
-// one workgroup per compute unit walking several equal query blocks
-__global__ void __launch_bounds__(NT, 1) attn_fwd_bf16_d128_persist(OSM_ATTN_FWD_PARAMS) {
-    attn_fwd_body<1>(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, seqlens_q, seqlens_k, scale_log2, causal, nqb,
-                     xcd_heads, nblocks);
-}
-
+// Per head dim: one query block per workgroup (attn_fwd_bf16_d<HD>); one
+// workgroup per compute unit walking several equal query blocks (_persist);
 // one workgroup per compute unit walking a static schedule of unequal blocks
-__global__ void __launch_bounds__(NT, 1) attn_fwd_bf16_d128_sched(OSM_ATTN_FWD_PARAMS) {
-    attn_fwd_body<2>(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, seqlens_q, seqlens_k, scale_log2, causal, nqb,
-                     xcd_heads, nblocks);
-}
+// (_sched).
+#define OSM_FWD_KERNELS(HD)                                                                          \
+    __global__ void __launch_bounds__(NT, kWgPerCu<HD>) attn_fwd_bf16_d##HD(OSM_ATTN_FWD_PARAMS) {  \
+        attn_fwd_body<0, HD>(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, seqlens_q, seqlens_k, scale_log2,  \
+                             causal, nqb, xcd_heads, nblocks);                                       \
+    }                                                                                                \
+    __global__ void __launch_bounds__(NT, kWgPerCu<HD>) attn_fwd_bf16_d##HD##_persist(OSM_ATTN_FWD_PARAMS) { \
+        attn_fwd_body<1, HD>(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, seqlens_q, seqlens_k, scale_log2,  \
+                             causal, nqb, xcd_heads, nblocks);                                       \
+    }                                                                                                \
+    __global__ void __launch_bounds__(NT, kWgPerCu<HD>) attn_fwd_bf16_d##HD##_sched(OSM_ATTN_FWD_PARAMS) { \
+        attn_fwd_body<2, HD>(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, seqlens_q, seqlens_k, scale_log2,  \
+                             causal, nqb, xcd_heads, nblocks);                                       \
+    }
+OSM_FWD_KERNELS(128)
+OSM_FWD_KERNELS(64)
+#undef OSM_FWD_KERNELS
 #undef OSM_ATTN_FWD_PARAMS
 
 }  // namespace
@@ -937,13 +995,15 @@ hipError_t launch_attn_fwd(const AttnFwdArgs &a, hipStream_t s) {
     const int64_t per_xcd = xcd_heads ? (int64_t)xcd_heads * nqb : 0;
     const int64_t max_tiles = per_xcd * ((a.seqlen_k + BK - 1) / BK + kSchedFixed);
     int mode = 0;
-    if (cus > 0 && blocks > cus) {
+    // (the persistent grids have kWgPerCu workgroups per compute unit)
+    const int pgrid = cus * (a.head_dim == 128 ? kWgPerCu<128> : kWgPerCu<64>);
+    if (pgrid > 0 && blocks > pgrid) {
         if (uniform) mode = 1;
-        else if (xcd_heads > 0 && xcd_heads <= 64 && cus / 8 <= 64 && per_xcd <= kSchedMax &&
+        else if (xcd_heads > 0 && xcd_heads <= 64 && pgrid / 8 <= 64 && per_xcd <= kSchedMax &&
                  max_tiles < ((int64_t)1 << 24))
             mode = 2;
     }
-    const unsigned grid = mode ? (unsigned)cus : (unsigned)blocks;
+    const unsigned grid = mode ? (unsigned)pgrid : (unsigned)blocks;
     const uint16_t *q = static_cast<const uint16_t *>(a.q), *k = static_cast<const uint16_t *>(a.k),
                    *v = static_cast<const uint16_t *>(a.v);
     uint16_t *o = static_cast<uint16_t *>(a.o);
@@ -951,9 +1011,15 @@ hipError_t launch_attn_fwd(const AttnFwdArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(KERNEL, dim3(grid), dim3(NT), 0, s, q, k, v, o, a.lse, a.batch, a.heads_q,     \
                        a.heads_kv, a.seqlen_q, a.seqlen_k, a.seqlens_q, a.seqlens_k, a.scale * kLog2e, \
                        a.causal, nqb, xcd_heads, (int)blocks)
-    if (mode == 1) OSM_FWD_LAUNCH(attn_fwd_bf16_d128_persist);
-    else if (mode == 2) OSM_FWD_LAUNCH(attn_fwd_bf16_d128_sched);
-    else OSM_FWD_LAUNCH(attn_fwd_bf16_d128);
+    if (a.head_dim == 128) {
+        if (mode == 1) OSM_FWD_LAUNCH(attn_fwd_bf16_d128_persist);
+        else if (mode == 2) OSM_FWD_LAUNCH(attn_fwd_bf16_d128_sched);
+        else OSM_FWD_LAUNCH(attn_fwd_bf16_d128);
+    } else {
+        if (mode == 1) OSM_FWD_LAUNCH(attn_fwd_bf16_d64_persist);
+        else if (mode == 2) OSM_FWD_LAUNCH(attn_fwd_bf16_d64_sched);
+        else OSM_FWD_LAUNCH(attn_fwd_bf16_d64);
+    }
 #undef OSM_FWD_LAUNCH
     return hipGetLastError();
 }

@@ -136,14 +136,15 @@ osm_status osm_softmax_rows_twopass(const float *x, float *y, int64_t rows, int6
  *         written as O = 0, LSE = -inf.
  *   scale multiplies Q K^T (for example 1/sqrt(head_dim)); must be finite and > 0.
  *   causal 0 or 1 (top-left aligned: j <= i).
- * Supported: dtype OSM_BF16, head_dim 128, batch * heads_q < 2^31; q, k,
- * v and o 16-byte aligned; fp32 accumulation of both products, fp32
+ * Supported: dtype OSM_BF16, head_dim 128 or 64, batch * heads_q < 2^31;
+ * q, k, v and o 16-byte aligned; fp32 accumulation of both products, fp32
  * running state, O rounded to bf16 once at the end.
  * Errors: OSM_ERR_NULL, OSM_ERR_SHAPE (non-positive batch/heads/head_dim,
  * negative seqlens, heads_q % heads_kv != 0, scale not finite or <= 0),
  * OSM_ERR_UNSUPPORTED (other dtype or head_dim, a misaligned pointer,
  * batch * heads_q >= 2^31, or one head's K, Q or O rows spanning 2 GiB or
- * more: seqlen_k or seqlen_q >= 2^23 at head_dim 128), OSM_ERR_HIP.
+ * more: seqlen_k or seqlen_q >= 2^23 at head_dim 128, 2^24 at 64),
+ * OSM_ERR_HIP.
  */
 osm_status osm_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                         osm_dtype dtype, int32_t batch, int32_t heads_q, int32_t heads_kv,

@@ -110,8 +110,11 @@ def test_attn_fwd_validation(lib):
     assert call(scale=float("nan")) == 2
     assert call(causal=2) == 2
     assert call(dtype=osm.OSM_F32) == 3
-    assert call(d=64) == 3
+    assert call(d=96) == 3
+    assert call(d=64, q=None) == 1                  # head dim 64 is supported: fails only at the NULL check
     assert call(Nk=1 << 23) == 3                    # one head's K rows would span 2 GiB
+    assert call(d=64, Nk=1 << 23, q=None) == 1      # at head dim 64 the same keys span 1 GiB
+    assert call(d=64, Nk=1 << 24) == 3
     assert call(Nq=1 << 23) == 3                    # one head's Q (and O) rows would span 2 GiB
     assert call(Nq=(1 << 23) - 1, q=None) == 1      # just below: accepted as far as the NULL check
     assert call(q=None) == 1

@@ -325,15 +325,22 @@ def test_scheduled_grid(orc, B, Hq, Hkv, Nq, Nk, causal, lq, lk):
     check_attn(oh.reshape(-1, 128)[rows], lh.reshape(-1)[rows], o_ref, lse_ref, "bf16")
 
 
-def _sweep_config(g, many_heads):
+# Workgroups the forward keeps resident per compute unit: one at head dim 128,
+# two at 64.  Inputs with more query blocks than resident workgroups run on the
+# persistent or scheduled grid.
+WG_PER_CU = {128: 1, 64: 2}
+
+
+def _sweep_config(g, many_heads, d=128):
     """One random configuration: GQA group, ragged lengths, masks, scale.
-    With many_heads, more query blocks than compute units (persistent and
-    scheduled grids); otherwise one block per workgroup."""
+    With many_heads, more query blocks than resident workgroups (persistent
+    and scheduled grids); otherwise one block per workgroup."""
     if many_heads:
         B = int(g.integers(1, 4))
         Hkv = int(g.choice([8, 16]))
         Hq = Hkv * int(g.choice([1, 2, 4]))
-        nqb = 256 // (B * Hq) + 1        # query blocks per head: more blocks than 256 CUs
+        # query blocks per head: more blocks than 256 CUs' resident workgroups
+        nqb = 256 * WG_PER_CU[d] // (B * Hq) + 1
         Nq = int(g.integers((nqb - 1) * 256 + 1, nqb * 256 + 1))
         Nk = int(g.integers(1, 450))
     else:
@@ -353,33 +360,111 @@ def _sweep_config(g, many_heads):
     return B, Hq, Hkv, Nq, Nk, causal, sq, sk, scale
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("many_heads", [False, True])
-def test_random_sweep(orc, many_heads):
+def test_random_sweep(orc, many_heads, d):
     """Seeded random configurations against the oracle: every row for the
     small ones, 200 sampled rows plus every padded row for the many-head
     ones (which run on the persistent or scheduled grids).  Padding is
     NaN-poisoned wherever a length array marks it."""
-    g = inputs.rng(4242 + many_heads)
+    g = inputs.rng(4242 + many_heads + 2 * (d == 64))
     n = 16 if many_heads else 60
     for case in range(n):
-        B, Hq, Hkv, Nq, Nk, causal, sq, sk, scale = _sweep_config(g, many_heads)
-        announce(f"fwd sweep {case}: B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} causal={causal} "
+        B, Hq, Hkv, Nq, Nk, causal, sq, sk, scale = _sweep_config(g, many_heads, d)
+        announce(f"fwd sweep {case}: d={d} B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} causal={causal} "
                  f"seqlens_q={None if sq is None else sq.tolist()} seqlens_k={None if sk is None else sk.tolist()} "
                  f"scale={scale:.4f}")
-        inp = inputs.attention_inputs(B, Hq, Hkv, Nq, Nk, 128, seed=5000 + 100 * many_heads + case, causal=causal,
+        inp = inputs.attention_inputs(B, Hq, Hkv, Nq, Nk, d, seed=5000 + 100 * many_heads + 1000 * (d == 64) + case,
+                                      causal=causal,
                                       scale=scale, seqlens_q=sq, seqlens_k=sk, poison=sk is not None)
         if many_heads:
-            assert B * Hq * ((Nq + 255) // 256) > torch_mod().cuda.get_device_properties(0).multi_processor_count
+            assert B * Hq * ((Nq + 255) // 256) > (torch_mod().cuda.get_device_properties(0).multi_processor_count
+                                                   * WG_PER_CU[d])
         o, lse = run(inp)
         oh, lh = host(o), host(lse)
         assert not np.isnan(oh).any() and not np.isnan(lh).any()
         if many_heads:
             rows = _sample_rows(np.random.default_rng(case), B, Hq, Nq, 200)
             o_ref, lse_ref = oracle(orc, inp, rows=rows)
-            check_attn(oh.reshape(-1, 128)[rows], lh.reshape(-1)[rows], o_ref, lse_ref, "bf16")
+            check_attn(oh.reshape(-1, d)[rows], lh.reshape(-1)[rows], o_ref, lse_ref, "bf16")
         else:
             o_ref, lse_ref = oracle(orc, inp)
             check_attn(oh, lh, o_ref, lse_ref, "bf16")
         if sq is not None:
             for b, L in enumerate(sq):       # padded query rows: exactly 0 / -inf
                 assert np.all(oh[b, :, L:] == 0.0) and np.all(np.isneginf(lh[b, :, L:]))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,causal", [
+    (2, 4, 2, 300, 300, False),
+    (2, 4, 2, 300, 300, True),
+    (1, 2, 1, 129, 517, False),
+    (1, 2, 2, 1, 1, False),
+    (1, 2, 2, 640, 640, True),
+])
+def test_small_d64(orc, B, Hq, Hkv, Nq, Nk, causal):
+    """Head dim 64, element by element against the oracle."""
+    announce(f"fwd d64 B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} causal={causal}")
+    inp = inputs.attention_inputs(B, Hq, Hkv, Nq, Nk, 64, seed=B * 1000 + Nq + Nk + 64, causal=causal)
+    o, lse = run(inp)
+    o_ref, lse_ref = oracle(orc, inp)
+    check_attn(host(o), host(lse), o_ref, lse_ref, "bf16")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_poisoned_d64(orc, causal):
+    """Head dim 64 with NaN past the lengths: against the oracle, padded
+    rows exactly 0 / -inf, and bit-identical to zero padding."""
+    announce(f"fwd d64 varlen poisoned causal={causal}")
+    B, H, N = 4, 2, 400
+    lens = np.array([1, 130, 257, 400], np.int32)
+    inp = inputs.attention_inputs(B, H, H, N, N, 64, seed=33, causal=causal, seqlens_q=lens,
+                                  seqlens_k=lens, poison=True)
+    o, lse = run(inp)
+    o_ref, lse_ref = oracle(orc, inp)
+    oh, lh = host(o), host(lse)
+    check_attn(oh, lh, o_ref, lse_ref, "bf16")
+    for b, L in enumerate(lens):
+        assert np.all(oh[b, :, L:] == 0.0) and np.all(np.isneginf(lh[b, :, L:]))
+    zq, zk, zv = (inputs.bf16_bits_to_f32(a).copy() for a in (inp.q, inp.k, inp.v))
+    for a in (zq, zk, zv):
+        a[np.isnan(a)] = 0.0
+    inp0 = inputs.AttnInputs(inputs.to_bf16_bits(zq), inputs.to_bf16_bits(zk), inputs.to_bf16_bits(zv),
+                             "bf16", lens, lens, inp.scale, causal)
+    o0, l0 = run(inp0)
+    assert np.array_equal(host_bits(o), host_bits(o0))
+    assert np.array_equal(host_bits(lse), host_bits(l0))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,causal,lq,lk", [
+    (4, 32, 8, 4096, 4096, False, None, None),                       # persistent grid
+    (1, 16, 16, 8300, 1, False, None, None),                         # persistent grid, one key
+    (4, 16, 16, 4096, 4096, True, [1, 1000, 2049, 4096], None),      # scheduled grid, causal
+    (4, 16, 8, 3000, 2000, False, [3000, 17, 2999, 0], [0, 2000, 1234, 5]),   # scheduled, no keys / queries
+])
+def test_grids_d64(orc, B, Hq, Hkv, Nq, Nk, causal, lq, lk):
+    """Head dim 64 with more query blocks than compute units (persistent or
+    scheduled grid) against the same blocks one per workgroup, bit for bit;
+    sampled rows against the oracle; padded rows exactly 0 / -inf."""
+    announce(f"fwd d64 grids B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} causal={causal} lq={lq} lk={lk}")
+    torch = torch_mod()
+    assert B * Hq * ((Nq + 255) // 256) > torch.cuda.get_device_properties(0).multi_processor_count * WG_PER_CU[64]
+    if lq is not None:
+        lq = np.array(lq, np.int32)
+        lk = lq.copy() if lk is None else np.array(lk, np.int32)
+    inp = inputs.attention_inputs(B, Hq, Hkv, Nq, Nk, 64, seed=B * 13 + Hq + Nq + Nk, causal=causal,
+                                  seqlens_q=lq, seqlens_k=lk, poison=lq is not None)
+    o1, l1 = run(inp)
+    o2, l2 = _run_in_groups(inp)
+    assert np.array_equal(host_bits(o1), host_bits(o2))
+    assert np.array_equal(host_bits(l1), host_bits(l2))
+    oh, lh = host(o1), host(l1)
+    assert not np.isnan(oh).any()
+    if lq is not None:
+        for b in range(B):
+            dead_from = int(lq[b]) if lk[b] > 0 else 0
+            assert np.all(oh[b, :, dead_from:] == 0.0) and np.all(np.isneginf(lh[b, :, dead_from:]))
+    rows = _sample_rows(np.random.default_rng(Nq + B + 64), B, Hq, Nq, 300,
+                        None if lq is None else np.maximum(lq, 1))
+    o_ref, lse_ref = oracle(orc, inp, rows=rows)
+    check_attn(oh.reshape(-1, 64)[rows], lh.reshape(-1)[rows], o_ref, lse_ref, "bf16")
