@@ -568,6 +568,16 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                 }
             }
         }
+        // At head dim 64 a wave has 128 VGPRs (two waves per SIMD): the
+        // fragments are moved into AGPRs, which the score MFMA reads directly.
+        // Left in VGPRs they do not fit, and the compiler parks them in AGPRs
+        // and copies each one back before every use (32 copies per tile).
+        if constexpr (HD == 64) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+a"(qf[qb][ks]));
+        }
 
 
         // per-lane LDS byte offsets (within a tile) of the QK A operand: row c,
