@@ -108,9 +108,16 @@ __device__ __forceinline__ f32x16 mfma8(const i32x8 &a, const i32x8 &b, const f3
 
 // O~^T accumulation with the accumulator pinned to AGPRs (see the header).
 // The hazard recognizer does not look into inline assembly: the VALU writes
-// of the B operand need wait states before the MFMA reads them.
+// of the B operand need wait states before the MFMA reads them.  NOP: the
+// first P~V MFMA of a tile, right after the conversions that build P~; the
+// others read the same P~ behind it, and A operands that come from LDS reads
+// (covered by the counter waits the compiler inserts).
+template <bool NOP>
 __device__ __forceinline__ void mfma8_acc(f32x16 &acc, const i32x8 &a, const i32x8 &b, int sc) {
-    asm("s_nop 3\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3" : "+a"(acc) : "v"(a), "v"(b), "v"(sc));
+    if constexpr (NOP)
+        asm("s_nop 3\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3" : "+a"(acc) : "v"(a), "v"(b), "v"(sc));
+    else
+        asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3" : "+a"(acc) : "v"(a), "v"(b), "v"(sc));
 }
 
 __device__ __forceinline__ void acc_zero8(f32x16 &acc, const i32x8 &z, int sc) {
@@ -447,7 +454,12 @@ attn_fp8_body(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
                             e[u] = fast_exp2(fmaf(s[kbk][qb][4 * r + u], scale_log2, -msub[qb]));
                             rs[u] = (kbk == 0 && r == 0) ? e[u] : rs[u] + e[u];
                         }
-                        int w = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+                        // (both halves of w are written, so the register the first
+                        // conversion starts from may hold anything: an empty asm
+                        // names one, where a constant would cost a move)
+                        int w;
+                        asm volatile("" : "=v"(w));
+                        w = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], w, false);
                         w = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], w, true);
                         pf[qb][4 * kbk + r] = w;
                     }
@@ -463,7 +475,10 @@ attn_fp8_body(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K,
                 const i32x2 r3 = lds_read_tr8(base + 40 * ROWB);
                 const i32x8 a = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
 #pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) mfma8_acc(oacc[qb][dt], a, pf[qb], unit_scale);
+                for (int qb = 0; qb < NQB; ++qb) {
+                    if (dt == 0 && qb == 0) mfma8_acc<true>(oacc[qb][dt], a, pf[qb], unit_scale);
+                    else mfma8_acc<false>(oacc[qb][dt], a, pf[qb], unit_scale);
+                }
             }
             // interleave the score MFMAs of tile t + 1 with the exponentials
 #pragma unroll
