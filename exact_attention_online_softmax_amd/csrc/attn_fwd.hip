@@ -1,4 +1,4 @@
-// attn_fwd.hip -- fused exact attention forward for gfx950 (bf16, head_dim 128).
+// attn_fwd.hip -- fused exact attention forward for gfx950 (bf16, head_dim 128 and 64).
 //
 // The block step of [P3] "Blocks, the bridge to FlashAttention": hold a block
 // of queries, stream the keys and values past them a block at a time,
@@ -17,6 +17,12 @@
 //    every K or V operand read from LDS feeds two MFMAs (half the LDS traffic
 //    per flop of a 32-query wave).  With one wave per SIMD each wave has 512
 //    registers: the output accumulators live in the AGPRs.
+//  * head dim 64 instantiates the same body (a template over the head dim)
+//    with 16 MFMA steps per tile instead of 32.  A wave then fits in 256
+//    registers (the Q fragments in AGPRs, which the score MFMA reads
+//    directly), so two workgroups run per CU and one wave's exponentials
+//    overlap the other's matrix products: per flop, the vector work is twice
+//    that of head dim 128.
 //  * both products run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
 //    The score tile is computed transposed, S^T = K Q^T, so lane l holds the
 //    scores of one query (l % 32) of each block against 16 of the 32 keys of
@@ -29,16 +35,19 @@
 //    scores of tile j and multiplies them into O~ while the matrix cores
 //    already compute the scores of tile j+1; the vector ALU work of one tile
 //    and the MFMAs of the next interleave in one instruction stream.
-//  * K and V tiles (32 keys x 128 dims, 8 KiB each) go from HBM straight
-//    into LDS with global_load_lds_dwordx4 (no VGPR staging; lane i of a load
-//    writes bytes 16 i .. 16 i + 15 of a 1 KiB LDS block) through a ring of
+//  * K and V tiles (32 keys x head dim: 8 KiB each at 128, 4 KiB at 64) go
+//    from HBM straight into LDS with buffer_load_dwordx4 ... lds (no VGPR
+//    staging; lane i of a load writes bytes 16 i .. 16 i + 15 of a 1 KiB LDS
+//    block) through a ring of
 //    four slots, loaded three tiles ahead.  Each slot is its own LDS object
 //    and the loop is unrolled by four, so every access names its slot
 //    statically: operand reads use immediate offsets, and the compiler can
 //    tell that the loads in flight never alias the slots being read.
-//  * rows are unpadded and XOR-swizzled at 16-byte granularity (K: slot =
-//    chunk ^ (row % 16); V: slot = chunk ^ 4 (row % 4)) so that the K operand
-//    reads and the transposing V reads are free of bank conflicts.
+//  * rows are unpadded and XOR-swizzled at 16-byte granularity (256-byte
+//    rows: K slot = chunk ^ (row % 16), V slot = chunk ^ 4 (row % 4); 128-byte
+//    rows: K slot = chunk ^ ((row / 2) % 8), V slot = chunk ^ 4 ((row / 2) % 2))
+//    so that the K operand reads and the transposing V reads are free of bank
+//    conflicts.
 //  * the V^T operand is read with the gfx950 transposing LDS read
 //    (ds_read_b64_tr_b16): in each 16-lane group, lane i points at
 //    V[k0 + i/4][d0 + 4 (i%4) .. +3] and lane j receives V[k0 + e][d0 + j],
@@ -211,11 +220,11 @@ constexpr int kSchedMax = 2048;
 constexpr int kSchedFixed = 10;     // per-block cost outside the tile loop, in tiles (measured)
 
 // MODE 0: one query block per workgroup.
-// MODE 1 and 2 (PERSIST): one workgroup per CU walks several blocks.  The Q of
-// the next block is copied into LDS (qs) while the current block runs, and
-// the last ring loads of a block fetch the first tiles of the next one, so a
-// block starts with its Q and first tiles on chip, and no CU waits for a new
-// workgroup to be dispatched between blocks.
+// MODE 1 and 2 (PERSIST): one workgroup per CU (two at head dim 64) walks
+// several blocks.  The Q of the next block is copied into LDS (qs) while the
+// current block runs, and the last ring loads of a block fetch the first
+// tiles of the next one, so a block starts with its Q and first tiles on
+// chip, and no CU waits for a new workgroup to be dispatched between blocks.
 //  * MODE 1: full-length non-causal inputs, where every block has the same
 //    work: workgroup L takes blocks L, L + gridDim.x, ...
 //  * MODE 2: causal or varlen inputs.  Every workgroup first builds its list
@@ -995,12 +1004,13 @@ hipError_t launch_attn_fwd(const AttnFwdArgs &a, hipStream_t s) {
             cus = 0;
         cus &= ~7;   // whole XCDs' worth, so block L keeps running on XCD L % 8
     }
-    // Full-length non-causal inputs with more blocks than compute units run on
-    // a persistent grid of one workgroup per compute unit (MODE 1); causal or
-    // varlen inputs on the scheduled persistent grid (MODE 2) when each XCD's
-    // heads and its list fit the schedule's limits (heads per XCD and slots
-    // per XCD at most 64, at most kSchedMax blocks per XCD, slot loads below
-    // 2^24 tiles); everything else one block per workgroup (MODE 0).
+    // Full-length non-causal inputs with more blocks than resident workgroups
+    // run on a persistent grid of kWgPerCu workgroups per compute unit
+    // (MODE 1); causal or varlen inputs on the scheduled persistent grid
+    // (MODE 2) when each XCD's heads and its list fit the schedule's limits
+    // (heads per XCD and slots per XCD at most 64, at most kSchedMax blocks
+    // per XCD, slot loads below 2^24 tiles); everything else one block per
+    // workgroup (MODE 0).
     const bool uniform = !a.causal && !a.seqlens_q && !a.seqlens_k && a.seqlen_k > 0;
     const int64_t per_xcd = xcd_heads ? (int64_t)xcd_heads * nqb : 0;
     const int64_t max_tiles = per_xcd * ((a.seqlen_k + BK - 1) / BK + kSchedFixed);
