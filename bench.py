@@ -31,6 +31,8 @@ After the timed steps, two reference kernels (libosm_probe.so: a streaming
 copy and a matrix-core loop) are timed once as "achievable" context.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
+       python bench.py --sweep      (the forward over sequence lengths 1K-32K, head dims
+                                     128 and 64, causal or not: one JSON line each)
 """
 from __future__ import annotations
 
@@ -213,9 +215,10 @@ def summarize(name, trace_dir, out):
         for (short, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
             lines.append(f"| {short} | {wg} | {len(d)} | {sum(d) / len(d) / 1e3:.1f} | "
                          f"{min(d) / 1e3:.1f} | {max(d) / 1e3:.1f} |")
-        # both forwards run on persistent grids (one workgroup per compute
-        # unit): the full-length one walks equal blocks, the causal varlen one
-        # a schedule built from the lengths
+        # both head-dim-128 forwards run on persistent grids (one workgroup
+        # per compute unit): the full-length one walks equal blocks, the
+        # causal varlen one a schedule built from the lengths; head dim 64
+        # runs one block per workgroup
         # (the piece kernel's grid is (pieces, kv heads, batch): 128 pieces
         # for decode, 8 for extend; the backward's key-major kernel is
         # instantiated for the causal mask or not)
@@ -224,7 +227,7 @@ def summarize(name, trace_dir, out):
                 "decode": ("decode_split", 128),
                 "merge_lse": ("merge_lse", None), "extend": ("decode_split", 8),
                 "bwd": ("attn_bwd_dkdv<false>", None), "bwd_causal": ("attn_bwd_dkdv<true>", None),
-                "fwd_fp8": ("attn_fwd_fp8", None), "fwd_d64": ("attn_fwd_bf16_d64_persist", None)}[name]
+                "fwd_fp8": ("attn_fwd_fp8", None), "fwd_d64": ("attn_fwd_bf16_d64", None)}[name]
         for (short, wg), d in groups.items():
             if want[0] in short and (want[1] is None or wg == want[1]):
                 avg_ns = sum(d) / len(d)
@@ -316,6 +319,49 @@ def summarize(name, trace_dir, out):
     return 0
 
 
+def sweep(args):
+    """The forward (osm_attn_fwd) over sequence lengths 1K-32K at a fixed
+    16384 tokens per head group (B = 16384 / N), head dims 128 (32 heads) and
+    64 (64 heads), full length, causal or not; inputs N(0, 1) rounded to bf16,
+    drawn on the device from a seeded generator.  One JSON line per
+    configuration: median and minimum of the timed calls (HIP events on the
+    current stream) and TFLOP/s of the median against the bf16 peak."""
+    import torch
+    import exact_attention_online_softmax_amd as osm
+
+    osm.load_library()
+    torch.cuda.set_device(0)
+    for d, H in ((128, 32), (64, 64)):
+        for causal in (False, True):
+            for N in (1024, 2048, 4096, 8192, 16384, 32768):
+                B = max(1, 16384 // N)
+                gen = torch.Generator(device="cuda").manual_seed(7000 + N + d + causal)
+                q, k, v = (torch.randn((B, H, N, d), generator=gen, device="cuda").to(torch.bfloat16)
+                           for _ in range(3))
+                o = torch.empty_like(q)
+                lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+                call = lambda: osm.attn_fwd(q, k, v, causal=causal, out=o, lse=lse)
+                for _ in range(args.warmup):
+                    call()
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(args.steps)]
+                torch.cuda.synchronize()
+                for a, b in ev:
+                    a.record()
+                    call()
+                    b.record()
+                torch.cuda.synchronize()
+                ms = sorted(a.elapsed_time(b) for a, b in ev)
+                med = ms[len(ms) // 2]
+                pairs = B * H * (N * (N + 1) / 2 if causal else N * N)
+                tf = 4.0 * d * pairs / (med / 1e3) / 1e12
+                print(json.dumps({"sweep": "attn_fwd", "head_dim": d, "causal": causal, "batch": B, "heads": H,
+                                  "seq_len": N, "ms_median": round(med, 4), "ms_min": round(ms[0], 4),
+                                  "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
+                del q, k, v, o, lse
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -330,6 +376,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB per step (scales rocprof "
                          "FETCH_SIZE/WRITE_SIZE to bytes)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="the forward over sequence lengths and head dims (one JSON line each)")
     ap.add_argument("--summarize", nargs=3, metavar=("NAME", "TRACE_DIR", "OUT"), default=None,
                     help="write a profile summary from rocprofv3 CSV output: NAME is a workload "
                          "name, TRACE_DIR holds run_kernel_stats.csv and pmc_*/ counter dirs")
@@ -340,6 +388,8 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(attention shards by batch and head with no exchange between GPUs)", file=sys.stderr)
         return 2
+    if args.sweep:
+        return sweep(args)
 
     import torch
     import exact_attention_online_softmax_amd as osm

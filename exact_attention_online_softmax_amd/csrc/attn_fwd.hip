@@ -22,7 +22,7 @@
 //    registers (the Q fragments in AGPRs, which the score MFMA reads
 //    directly), so two workgroups run per CU and one wave's exponentials
 //    overlap the other's matrix products: per flop, the vector work is twice
-//    that of head dim 128.
+//    that of head dim 128.  It runs one query block per workgroup.
 //  * both products run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
 //    The score tile is computed transposed, S^T = K Q^T, so lane l holds the
 //    scores of one query (l % 32) of each block against 16 of the 32 keys of
@@ -220,8 +220,8 @@ constexpr int kSchedMax = 2048;
 constexpr int kSchedFixed = 10;     // per-block cost outside the tile loop, in tiles (measured)
 
 // MODE 0: one query block per workgroup.
-// MODE 1 and 2 (PERSIST): one workgroup per CU (two at head dim 64) walks
-// several blocks.  The Q of the next block is copied into LDS (qs) while the
+// MODE 1 and 2 (PERSIST, head dim 128): one workgroup per CU walks several
+// blocks.  The Q of the next block is copied into LDS (qs) while the
 // current block runs, and the last ring loads of a block fetch the first
 // tiles of the next one, so a block starts with its Q and first tiles on
 // chip, and no CU waits for a new workgroup to be dispatched between blocks.
@@ -961,31 +961,27 @@ attn_fwd_body(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 
 // Workgroups resident per compute unit: at head dim 128 one (each wave has
 // the 512 registers of its SIMD); at 64 two (a wave fits in 256 registers and
-// a workgroup in 72 KiB of LDS), so that one wave's exponentials overlap the
+// a workgroup in 33 KiB of LDS), so that one wave's exponentials overlap the
 // other's matrix products -- the vector work per MFMA is twice that of head
 // dim 128.
 template <int HD> constexpr int kWgPerCu = HD == 128 ? 1 : 2;
 
-// Per head dim: one query block per workgroup (attn_fwd_bf16_d<HD>); one
-// workgroup per compute unit walking several equal query blocks (_persist);
-// one workgroup per compute unit walking a static schedule of unequal blocks
-// (_sched).
-#define OSM_FWD_KERNELS(HD)                                                                          \
-    __global__ void __launch_bounds__(NT, kWgPerCu<HD>) attn_fwd_bf16_d##HD(OSM_ATTN_FWD_PARAMS) {  \
-        attn_fwd_body<0, HD>(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, seqlens_q, seqlens_k, scale_log2,  \
-                             causal, nqb, xcd_heads, nblocks);                                       \
-    }                                                                                                \
-    __global__ void __launch_bounds__(NT, kWgPerCu<HD>) attn_fwd_bf16_d##HD##_persist(OSM_ATTN_FWD_PARAMS) { \
-        attn_fwd_body<1, HD>(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, seqlens_q, seqlens_k, scale_log2,  \
-                             causal, nqb, xcd_heads, nblocks);                                       \
-    }                                                                                                \
-    __global__ void __launch_bounds__(NT, kWgPerCu<HD>) attn_fwd_bf16_d##HD##_sched(OSM_ATTN_FWD_PARAMS) { \
-        attn_fwd_body<2, HD>(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, seqlens_q, seqlens_k, scale_log2,  \
-                             causal, nqb, xcd_heads, nblocks);                                       \
+// One query block per workgroup (attn_fwd_bf16_d<HD>); at head dim 128 also
+// one workgroup per compute unit walking several equal query blocks
+// (_persist) or a static schedule of unequal blocks (_sched).  At head dim 64
+// the two workgroups of a compute unit hide each other's block starts and
+// ends, and one block per workgroup measured 6-8% faster than both
+// persistent grids, so those are not built there.
+#define OSM_FWD_KERNEL(HD, MODE, NAME)                                                               \
+    __global__ void __launch_bounds__(NT, kWgPerCu<HD>) NAME(OSM_ATTN_FWD_PARAMS) {                  \
+        attn_fwd_body<MODE, HD>(Q, K, V, O, LSE, B, Hq, Hkv, Nq, Nk, seqlens_q, seqlens_k, scale_log2, \
+                                causal, nqb, xcd_heads, nblocks);                                    \
     }
-OSM_FWD_KERNELS(128)
-OSM_FWD_KERNELS(64)
-#undef OSM_FWD_KERNELS
+OSM_FWD_KERNEL(128, 0, attn_fwd_bf16_d128)
+OSM_FWD_KERNEL(128, 1, attn_fwd_bf16_d128_persist)
+OSM_FWD_KERNEL(128, 2, attn_fwd_bf16_d128_sched)
+OSM_FWD_KERNEL(64, 0, attn_fwd_bf16_d64)
+#undef OSM_FWD_KERNEL
 #undef OSM_ATTN_FWD_PARAMS
 
 }  // namespace
@@ -1004,22 +1000,24 @@ hipError_t launch_attn_fwd(const AttnFwdArgs &a, hipStream_t s) {
             cus = 0;
         cus &= ~7;   // whole XCDs' worth, so block L keeps running on XCD L % 8
     }
-    // Full-length non-causal inputs with more blocks than resident workgroups
-    // run on a persistent grid of kWgPerCu workgroups per compute unit
-    // (MODE 1); causal or varlen inputs on the scheduled persistent grid
+    // Head dim 128: full-length non-causal inputs with more blocks than
+    // compute units run on a persistent grid of one workgroup per compute
+    // unit (MODE 1); causal or varlen inputs on the scheduled persistent grid
     // (MODE 2) when each XCD's heads and its list fit the schedule's limits
-    // (heads per XCD and slots per XCD at most 64, at most kSchedMax blocks
-    // per XCD, slot loads below 2^24 tiles); everything else one block per
-    // workgroup (MODE 0).
+    // (slots per XCD at most 64, at most kSchedMax blocks per XCD, slot loads
+    // below 2^24 tiles) and an XCD has at most 32 heads: with 64 (short
+    // sequences, such as 512 heads of 1024 queries) building the schedule
+    // cost more than it saved, and one block per workgroup measured 12%
+    // faster.  Everything else, and head dim 64, one block per workgroup
+    // (MODE 0).
     const bool uniform = !a.causal && !a.seqlens_q && !a.seqlens_k && a.seqlen_k > 0;
     const int64_t per_xcd = xcd_heads ? (int64_t)xcd_heads * nqb : 0;
     const int64_t max_tiles = per_xcd * ((a.seqlen_k + BK - 1) / BK + kSchedFixed);
     int mode = 0;
-    // (the persistent grids have kWgPerCu workgroups per compute unit)
-    const int pgrid = cus * (a.head_dim == 128 ? kWgPerCu<128> : kWgPerCu<64>);
-    if (pgrid > 0 && blocks > pgrid) {
+    const int pgrid = cus * kWgPerCu<128>;
+    if (a.head_dim == 128 && pgrid > 0 && blocks > pgrid) {
         if (uniform) mode = 1;
-        else if (xcd_heads > 0 && xcd_heads <= 64 && pgrid / 8 <= 64 && per_xcd <= kSchedMax &&
+        else if (xcd_heads > 0 && xcd_heads <= 32 && pgrid / 8 <= 64 && per_xcd <= kSchedMax &&
                  max_tiles < ((int64_t)1 << 24))
             mode = 2;
     }
@@ -1036,9 +1034,7 @@ hipError_t launch_attn_fwd(const AttnFwdArgs &a, hipStream_t s) {
         else if (mode == 2) OSM_FWD_LAUNCH(attn_fwd_bf16_d128_sched);
         else OSM_FWD_LAUNCH(attn_fwd_bf16_d128);
     } else {
-        if (mode == 1) OSM_FWD_LAUNCH(attn_fwd_bf16_d64_persist);
-        else if (mode == 2) OSM_FWD_LAUNCH(attn_fwd_bf16_d64_sched);
-        else OSM_FWD_LAUNCH(attn_fwd_bf16_d64);
+        OSM_FWD_LAUNCH(attn_fwd_bf16_d64);
     }
 #undef OSM_FWD_LAUNCH
     return hipGetLastError();

@@ -326,8 +326,9 @@ def test_scheduled_grid(orc, B, Hq, Hkv, Nq, Nk, causal, lq, lk):
 
 
 # Workgroups the forward keeps resident per compute unit: one at head dim 128,
-# two at 64.  Inputs with more query blocks than resident workgroups run on the
-# persistent or scheduled grid.
+# two at 64.  At head dim 128, inputs with more query blocks than compute units
+# run on the persistent or scheduled grid; head dim 64 runs one block per
+# workgroup on every input, many blocks per compute unit in these cases.
 WG_PER_CU = {128: 1, 64: 2}
 
 
@@ -437,15 +438,16 @@ def test_varlen_poisoned_d64(orc, causal):
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,causal,lq,lk", [
-    (4, 32, 8, 4096, 4096, False, None, None),                       # persistent grid
-    (1, 16, 16, 8300, 1, False, None, None),                         # persistent grid, one key
-    (4, 16, 16, 4096, 4096, True, [1, 1000, 2049, 4096], None),      # scheduled grid, causal
-    (4, 16, 8, 3000, 2000, False, [3000, 17, 2999, 0], [0, 2000, 1234, 5]),   # scheduled, no keys / queries
+    (4, 32, 8, 4096, 4096, False, None, None),                       # full length, GQA 4:1
+    (1, 16, 16, 8300, 1, False, None, None),                         # one key
+    (4, 16, 16, 4096, 4096, True, [1, 1000, 2049, 4096], None),      # causal, ragged
+    (4, 16, 8, 3000, 2000, False, [3000, 17, 2999, 0], [0, 2000, 1234, 5]),   # no keys / no queries
 ])
 def test_grids_d64(orc, B, Hq, Hkv, Nq, Nk, causal, lq, lk):
-    """Head dim 64 with more query blocks than compute units (persistent or
-    scheduled grid) against the same blocks one per workgroup, bit for bit;
-    sampled rows against the oracle; padded rows exactly 0 / -inf."""
+    """Head dim 64 with more query blocks than resident workgroups (several
+    blocks per workgroup slot, XCD-grouped heads) against the same attention
+    computed one call per (batch, group of 8 heads), bit for bit; sampled rows
+    against the oracle; padded rows exactly 0 / -inf."""
     announce(f"fwd d64 grids B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} causal={causal} lq={lq} lk={lk}")
     torch = torch_mod()
     assert B * Hq * ((Nq + 255) // 256) > torch.cuda.get_device_properties(0).multi_processor_count * WG_PER_CU[64]
