@@ -22,6 +22,7 @@ inputs already resident in HBM:
   bwd_causal osm_attn_bwd           backward of the fwd_causal workload
   fwd_d64   osm_attn_fwd            bf16 B=4 H=64 N=4096 d=64, non-causal (the headline's flops
                                     and bytes at head dim 64)
+  bwd_d64   osm_attn_bwd            backward of the fwd_d64 workload
 
 Each call is timed with HIP events on the stream it runs on (torch's current
 stream); ``value`` is the headline forward's TFLOP/s (mean over the timed
@@ -67,9 +68,9 @@ KERNEL_SOURCES = {"fwd": "attn_fwd.hip", "fwd_causal": "attn_fwd.hip", "softmax"
                   "softmax_2pass": "softmax_rows.hip",
                   "decode": "decode.hip", "merge_lse": "merge_lse.hip", "extend": "decode.hip",
                   "bwd": "attn_bwd.hip", "bwd_causal": "attn_bwd.hip", "fwd_fp8": "attn_fwd_fp8.hip",
-                  "fwd_d64": "attn_fwd.hip"}
+                  "fwd_d64": "attn_fwd.hip", "bwd_d64": "attn_bwd.hip"}
 WORKLOADS = ["softmax", "softmax_2pass", "fwd", "fwd_causal", "decode", "merge_lse", "extend", "bwd",
-             "bwd_causal", "fwd_fp8", "fwd_d64"]
+             "bwd_causal", "fwd_fp8", "fwd_d64", "bwd_d64"]
 
 
 def source_hash(name):
@@ -196,8 +197,8 @@ def summarize(name, trace_dir, out):
     kern = {"fwd": "attn_fwd_bf16", "fwd_causal": "attn_fwd_bf16", "softmax": "softmax_rows_resident",
             "softmax_2pass": "softmax_rows_streaming",
             "decode": "decode_split", "merge_lse": "merge_lse", "extend": "decode_split",
-            "bwd": "attn_bwd_dkdv", "bwd_causal": "attn_bwd_dkdv", "fwd_fp8": "attn_fwd_fp8",
-            "fwd_d64": "attn_fwd_bf16_d64"}[name]
+            "bwd": "attn_bwd_dkdv<false, 128>", "bwd_causal": "attn_bwd_dkdv<true, 128>",
+            "fwd_fp8": "attn_fwd_fp8", "fwd_d64": "attn_fwd_bf16_d64", "bwd_d64": "attn_bwd_dkdv<false, 64>"}[name]
     lines = [f"# rocprofv3 summary: {name}", ""]
     trace = os.path.join(trace_dir, "trace", "run_kernel_trace.csv")
     avg_ns = None
@@ -226,8 +227,9 @@ def summarize(name, trace_dir, out):
                 "softmax": ("softmax_rows_resident", None), "softmax_2pass": ("softmax_rows_streaming", None),
                 "decode": ("decode_split", 128),
                 "merge_lse": ("merge_lse", None), "extend": ("decode_split", 8),
-                "bwd": ("attn_bwd_dkdv<false>", None), "bwd_causal": ("attn_bwd_dkdv<true>", None),
-                "fwd_fp8": ("attn_fwd_fp8", None), "fwd_d64": ("attn_fwd_bf16_d64", None)}[name]
+                "bwd": ("attn_bwd_dkdv<false, 128>", None), "bwd_causal": ("attn_bwd_dkdv<true, 128>", None),
+                "fwd_fp8": ("attn_fwd_fp8", None), "fwd_d64": ("attn_fwd_bf16_d64", None),
+                "bwd_d64": ("attn_bwd_dkdv<false, 64>", None)}[name]
         for (short, wg), d in groups.items():
             if want[0] in short and (want[1] is None or wg == want[1]):
                 avg_ns = sum(d) / len(d)
@@ -435,7 +437,7 @@ def main():
                                                 dq=g3[0], dk=g3[1], dv=g3[2])
             # five products per (query, key) pair: S again, dP, dV, dQ, dK
             work["bwd"] = ("mfma", 10.0 * B * H * N * N * d, "backward of B4 H32 N4096 d128 non-causal")
-    if "fwd_d64" in names:
+    if "fwd_d64" in names or "bwd_d64" in names:
         log("inputs: fwd B4 H64 N4096 d64")
         inp64 = inputs.attention_inputs(4, 64, 64, 4096, 4096, 64, seed=inputs.SEED_BASE + 11)
         q64, k64, v64 = (bf16_dev(a, torch) for a in (inp64.q, inp64.k, inp64.v))
@@ -444,6 +446,18 @@ def main():
         scale64 = inp64.scale
         calls["fwd_d64"] = lambda: osm.attn_fwd(q64, k64, v64, scale=scale64, out=o64, lse=l64)
         work["fwd_d64"] = ("mfma", 4.0 * 4 * 64 * 4096 * 4096 * 64, "B4 H64 N4096 d64 non-causal")
+        if "bwd_d64" in names:
+            log("inputs: bwd B4 H64 N4096 d64, output gradient")
+            calls["fwd_d64"]()
+            do64 = bf16_dev(inputs.output_grad(4, 64, 4096, 64, inputs.SEED_BASE + 12), torch)
+            ws64 = torch.empty(osm.attn_bwd_workspace_bytes(4, 64, 4096), dtype=torch.uint8, device="cuda")
+            g64 = [torch.empty_like(t) for t in (q64, k64, v64)]
+            calls["bwd_d64"] = lambda: osm.attn_bwd(q64, k64, v64, o64, l64, do64, scale=scale64,
+                                                    workspace=ws64, dq=g64[0], dk=g64[1], dv=g64[2])
+            work["bwd_d64"] = ("mfma", 10.0 * 4 * 64 * 4096 * 4096 * 64,
+                               "backward of B4 H64 N4096 d64 non-causal")
+        if "fwd_d64" not in names:
+            del calls["fwd_d64"], work["fwd_d64"]
         del inp64
     if "fwd_causal" in names or "bwd_causal" in names:
         log("inputs: fwd causal B8 H16 N8192 d128 varlen")
@@ -592,7 +606,8 @@ def main():
            "config": {"workload": f"attn_fwd {hc['workload']}" if head == "fwd" else hc["workload"],
                       "step": "softmax_rows + softmax_rows_twopass + attn_fwd (non-causal) + attn_fwd (causal varlen) "
                               "+ attn_decode_splitkv + merge_lse + attn_extend + attn_bwd (non-causal) "
-                              "+ attn_bwd (causal varlen) + attn_fwd_fp8 + attn_fwd (head dim 64)" if args.only is None
+                              "+ attn_bwd (causal varlen) + attn_fwd_fp8 + attn_fwd (head dim 64) "
+                              "+ attn_bwd (head dim 64)" if args.only is None
                               else args.only,
                       "global_batch": 4, "seq_len": 4096, "parallelism": "none (1 GPU)"},
            "roofline": roofline, "components": comps}

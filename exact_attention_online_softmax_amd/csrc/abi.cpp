@@ -120,7 +120,8 @@ osm_status osm_attn_bwd(const void *q, const void *k, const void *v, const void 
     if (batch < 1 || heads_q < 1 || heads_kv < 1 || head_dim < 1 || seqlen_q < 0 || seqlen_k < 0 ||
         heads_q % heads_kv != 0 || !(scale > 0.0f) || !isfinite(scale) || (causal != 0 && causal != 1))
         return OSM_ERR_SHAPE;
-    if (dtype != OSM_BF16 || head_dim != 128 || too_many_heads(batch, heads_q)) return OSM_ERR_UNSUPPORTED;
+    if (dtype != OSM_BF16 || (head_dim != 128 && head_dim != 64) || too_many_heads(batch, heads_q))
+        return OSM_ERR_UNSUPPORTED;
     // one head's rows are addressed with 32-bit byte offsets
     if ((int64_t)seqlen_k * head_dim * 2 >= ((int64_t)1 << 31) ||
         (int64_t)seqlen_q * head_dim * 2 >= ((int64_t)1 << 31))

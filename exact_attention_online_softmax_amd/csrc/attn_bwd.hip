@@ -1,5 +1,5 @@
-// attn_bwd.hip -- attention backward for gfx950 (bf16, head_dim 128), with
-// the weights rebuilt from the stored log-sum-exp.
+// attn_bwd.hip -- attention backward for gfx950 (bf16, head_dim 128 and 64),
+// with the weights rebuilt from the stored log-sum-exp.
 //
 // [P3] "From weights to outputs", the log-sum-exp paragraph: lse is one
 // number per query, and it is all a backward pass keeps to rebuild the
@@ -42,6 +42,10 @@
 // buffer loads with LDS destination, whose range check turns rows past the
 // valid length into zeros (NaN padding never reaches an MFMA); LDS rows are
 // XOR-swizzled at 16-byte granularity.
+//
+// The three kernels are templates over the head dim, instantiated for 128
+// and 64: at 64 a row is 128 bytes, a k-step loop has four steps instead of
+// eight and a gradient two 32-dim output tiles instead of four.
 #include "osm_device.h"
 #include "osm_internal.h"
 
@@ -55,15 +59,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int D = 128;            // head dim
-constexpr int ROWB = D * 2;       // bytes per bf16 row
+// per head dim: bytes per bf16 row, 16-byte chunks per row, rows per 1 KiB
+// DMA block, k-steps of 16 dims, output tiles of 32 dims
+template <int HD> struct BGeo {
+    static constexpr int ROWB = HD * 2, CH = ROWB / 16, RPB = 1024 / ROWB, KS = HD / 16, NDT = HD / 32;
+    static constexpr int kLogCH = CH == 16 ? 4 : 3;
+};
 constexpr float kPosInf = __builtin_inff();
 
 // Buffer resource word 3 for raw dword access (DATA_FORMAT = 32 bits).
 constexpr int kRsrcWord3 = 0x00020000;
 // s_waitcnt encodings (gfx9): vmcnt in bits 3:0 and 15:14, lgkmcnt 11:8.
 constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitVm2 = 0x0F72;
 
 template <int N> struct Slot { static constexpr int value = N; };
 
@@ -83,6 +90,16 @@ __device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlan
 // row's low four bits, left the transposing reads two-way conflicted:
 // rocprofv3 counted SQ_LDS_BANK_CONFLICT at 29% of the LDS active cycles.)
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// 128-byte rows (head dim 64) hold 8 chunks; two rows share a 256-byte
+// window, so chunk c of row r lands in 16-byte bank group 8 (r % 2) + slot.
+// swz64(r) = 4 ((r / 2) % 2) + (r / 4) % 4 takes 8 distinct values over the
+// even rows of any 16 consecutive ones and over the odd rows, so the
+// row-wise reads stay conflict-free; rows 4a and 4a + 2 (and 4a + 1, 4a + 3)
+// differ in its bit 2, so a transposing read of four adjacent chunks from
+// rows 4a .. 4a + 3 covers disjoint halves of each window.
+__device__ __forceinline__ int swz64(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+template <int HD> __device__ __forceinline__ int swzh(int r) { return HD == 128 ? swz(r) : swz64(r); }
 
 // gfx950 transposing LDS read: in each 16-lane group, lane i points at
 // row k0 + i/4, columns d0 + 4 (i%4) .. +3 of a row-major bf16 tile, and
@@ -121,6 +138,9 @@ __device__ __forceinline__ void acc_zero(f32x16 &acc, const bf16x8 &z) {
 __device__ __forceinline__ void acc_settle(f32x16 (&o)[4]) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]));
 }
+__device__ __forceinline__ void acc_settle(f32x16 (&o)[2]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o[0]), "+a"(o[1]));
+}
 
 __device__ __forceinline__ bf16x8 cat4(const bf16x4 &lo, const bf16x4 &hi) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -155,20 +175,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int byt
 }
 
 // ---------------------------------------------------------------------------
-// attn_bwd_pre: D = dO . O and lse2 per query row; 16 lanes per row.
+// attn_bwd_pre: D = dO . O and lse2 per query row; HD / 8 lanes per row.
 // ---------------------------------------------------------------------------
 constexpr int PRE_NT = 256;
-constexpr int PRE_ROWS = PRE_NT / 16;
+template <int HD> constexpr int kPreRows = PRE_NT / (HD / 8);
 
+template <int HD>
 __global__ void __launch_bounds__(PRE_NT)
 attn_bwd_pre(const uint16_t *__restrict__ O, const uint16_t *__restrict__ dO,
              const float *__restrict__ LSE, float2 *__restrict__ LD, int64_t rows, int Nq, int Hq,
              const int32_t *__restrict__ seqlens_q) {
-    const int64_t r = (int64_t)blockIdx.x * PRE_ROWS + (threadIdx.x >> 4);
-    const int j = threadIdx.x & 15;
-    if (r >= rows) return;                        // whole 16-lane groups leave together
-    const uint4 o = *reinterpret_cast<const uint4 *>(O + r * D + 8 * j);
-    const uint4 g = *reinterpret_cast<const uint4 *>(dO + r * D + 8 * j);
+    constexpr int LPR = HD / 8;                   // lanes per row, 8 dims each
+    const int64_t r = (int64_t)blockIdx.x * kPreRows<HD> + (threadIdx.x / LPR);
+    const int j = threadIdx.x % LPR;
+    if (r >= rows) return;                        // whole groups of lanes leave together
+    const uint4 o = *reinterpret_cast<const uint4 *>(O + r * HD + 8 * j);
+    const uint4 g = *reinterpret_cast<const uint4 *>(dO + r * HD + 8 * j);
     float acc = bf16_lo(o.x) * bf16_lo(g.x);
     acc = fmaf(bf16_hi(o.x), bf16_hi(g.x), acc);
     acc = fmaf(bf16_lo(o.y), bf16_lo(g.y), acc);
@@ -177,10 +199,8 @@ attn_bwd_pre(const uint16_t *__restrict__ O, const uint16_t *__restrict__ dO,
     acc = fmaf(bf16_hi(o.z), bf16_hi(g.z), acc);
     acc = fmaf(bf16_lo(o.w), bf16_lo(g.w), acc);
     acc = fmaf(bf16_hi(o.w), bf16_hi(g.w), acc);
-    acc += __shfl_xor(acc, 1, 64);
-    acc += __shfl_xor(acc, 2, 64);
-    acc += __shfl_xor(acc, 4, 64);
-    acc += __shfl_xor(acc, 8, 64);
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
     if (j == 0) {
         const int i = (int)(r % Nq);
         const int b = (int)(r / ((int64_t)Nq * Hq));
@@ -203,12 +223,11 @@ constexpr int KV_NT = 64 * KV_NW;
 // with the 16-bit immediate offset; with 128 every read of the second
 // stage's arrays needed its address computed (an OR per read)
 constexpr int KV_QT = 64;
-constexpr int KV_STB = KV_QT * ROWB;           // bytes of Q (or dO) per stage
-constexpr int KV_BLK = KV_STB / 1024 / KV_NW;  // 1 KiB DMA blocks per wave per array per stage
+template <int HD> constexpr int kKvStb = KV_QT * BGeo<HD>::ROWB;   // bytes of Q (or dO) per stage
 static_assert(KV_QT % 32 == 0 && KV_QT / 32 <= KV_NW,
               "waves 0 .. KV_QT/32-1 load a stage's (lse2, D), 256 bytes each");
 
-template <bool CAUSAL>
+template <bool CAUSAL, int HD>
 __global__ void __launch_bounds__(KV_NT, 1)
 attn_bwd_dkdv(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
               const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
@@ -216,6 +235,11 @@ attn_bwd_dkdv(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
               int Hq, int Hkv, int Nq, int Nk, const int32_t *__restrict__ seqlens_q,
               const int32_t *__restrict__ seqlens_k, float scale_log2, float scale, int nkb,
               int xcd_heads) {
+    using G = BGeo<HD>;
+    constexpr int ROWB = G::ROWB, CH = G::CH, RPB = G::RPB, KS = G::KS, NDT = G::NDT;
+    constexpr int KV_STB = kKvStb<HD>;
+    constexpr int KV_BLK = KV_STB / 1024 / KV_NW;  // 1 KiB DMA blocks per wave per array per stage
+    static_assert(KV_BLK >= 1, "every wave loads whole 1 KiB blocks of a stage");
     // two stages of Q rows, dO rows and (lse2, D)
     __shared__ __attribute__((aligned(1024))) uint8_t qs0[KV_STB], qs1[KV_STB];
     __shared__ __attribute__((aligned(1024))) uint8_t os0[KV_STB], os1[KV_STB];
@@ -253,8 +277,8 @@ attn_bwd_dkdv(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     if (kb0 >= Lk) {
         // every key of this block is padding: zero gradients
         const int rows = min(KV_BK, Nk - kb0);
-        for (int i = tid; i < rows * (D / 8); i += KV_NT) {
-            const size_t off = (kvrow0 + kb0 + i / (D / 8)) * D + (i % (D / 8)) * 8;
+        for (int i = tid; i < rows * (HD / 8); i += KV_NT) {
+            const size_t off = (kvrow0 + kb0 + i / (HD / 8)) * HD + (i % (HD / 8)) * 8;
             *reinterpret_cast<uint4 *>(dK + off) = make_uint4(0, 0, 0, 0);
             *reinterpret_cast<uint4 *>(dV + off) = make_uint4(0, 0, 0, 0);
         }
@@ -262,27 +286,27 @@ attn_bwd_dkdv(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     }
 
     // ---- K and V of this wave's keys, as B operands ----------------------
-    // lane (g, c) holds K[kw0 + c][64 g + 8 ks + 0..7] for k-step ks; the
-    // A operands (rows of Q, dO) use the same order of the head dim
-    bf16x8 kf[8], vf[8];
+    // lane (g, c) holds K[kw0 + c][(HD / 2) g + 8 ks + 0..7] for k-step ks;
+    // the A operands (rows of Q, dO) use the same order of the head dim
+    bf16x8 kf[KS], vf[KS];
     {
         const int key = kw0 + c;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
             uint4 wk = make_uint4(0, 0, 0, 0), wv = make_uint4(0, 0, 0, 0);
             if (key < Lk) {
-                wk = *reinterpret_cast<const uint4 *>(K + (kvrow0 + key) * D + 64 * g + 8 * ks);
-                wv = *reinterpret_cast<const uint4 *>(V + (kvrow0 + key) * D + 64 * g + 8 * ks);
+                wk = *reinterpret_cast<const uint4 *>(K + (kvrow0 + key) * HD + (HD / 2) * g + 8 * ks);
+                wv = *reinterpret_cast<const uint4 *>(V + (kvrow0 + key) * HD + (HD / 2) * g + 8 * ks);
             }
             kf[ks] = __builtin_bit_cast(bf16x8, wk);
             vf[ks] = __builtin_bit_cast(bf16x8, wv);
         }
     }
-    f32x16 dka[4], dva[4];
+    f32x16 dka[NDT], dva[NDT];
     {
         const bf16x8 z8 = {};
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+        for (int dt = 0; dt < NDT; ++dt) {
             acc_zero(dka[dt], z8);
             acc_zero(dva[dt], z8);
         }
@@ -294,24 +318,24 @@ attn_bwd_dkdv(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const int per_head = (Lq > qbeg) ? (Lq - qbeg + KV_QT - 1) / KV_QT : 0;
     const int nst = group * per_head;
 
-    // DMA of one stage: wave w fills 1 KiB blocks KV_BLK w .. +KV_BLK-1 (four
-    // rows each) of the Q and dO arrays, lane l row 4 blk + l/16, slot l%16
+    // DMA of one stage: wave w fills 1 KiB blocks KV_BLK w .. +KV_BLK-1 (RPB
+    // rows each) of the Q and dO arrays, lane l row RPB blk + l/CH, slot l%CH
     // (holding global chunk slot ^ swz(row)); waves 0 .. KV_QT/32-1 also load
     // (lse2, D) of rows 32 w .. 32 w + 31.  Rows at or past Lq read as zeros: their Q
     // and dO are 0, so whatever their weight, they add nothing.
     uint32_t dmo[KV_BLK];
 #pragma unroll
     for (int i = 0; i < KV_BLK; ++i) {
-        const int row = 4 * (KV_BLK * wave + i) + (lane >> 4);
-        dmo[i] = row * ROWB + (((lane & 15) ^ swz(row)) << 4);
+        const int row = RPB * (KV_BLK * wave + i) + (lane >> G::kLogCH);
+        dmo[i] = row * ROWB + (((lane & (CH - 1)) ^ swzh<HD>(row)) << 4);
     }
     auto issue = [&](uint8_t *qd, uint8_t *od, float2 *ld, int st) __attribute__((always_inline)) {
         const int hq = hkv * group + st / per_head;
         const int q0 = qbeg + (st % per_head) * KV_QT;
         const size_t row0 = (size_t)(b * Hq + hq) * Nq + q0;
         const int nrows = Lq - q0;               // > 0
-        const __amdgpu_buffer_rsrc_t rq = rsrc(Q + row0 * D, nrows * ROWB);
-        const __amdgpu_buffer_rsrc_t ro = rsrc(dO + row0 * D, nrows * ROWB);
+        const __amdgpu_buffer_rsrc_t rq = rsrc(Q + row0 * HD, nrows * ROWB);
+        const __amdgpu_buffer_rsrc_t ro = rsrc(dO + row0 * HD, nrows * ROWB);
         const __amdgpu_buffer_rsrc_t rl = rsrc(LD + row0, nrows * 8);
 #pragma unroll
         for (int i = 0; i < KV_BLK; ++i) dma16(rq, qd + (KV_BLK * wave + i) * 1024, dmo[i]);
@@ -321,22 +345,22 @@ attn_bwd_dkdv(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     };
 
     // operand offsets within a 32-row block of a stage.  Row-wise A operand
-    // (rows of Q or dO): lane (g, c) reads row c, chunk 8 g + ks.
-    uint32_t aoff[8];
+    // (rows of Q or dO): lane (g, c) reads row c, chunk (CH / 2) g + ks.
+    uint32_t aoff[KS];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) aoff[ks] = c * ROWB + ((((8 * g) + ks) ^ swz(c)) << 4);
+    for (int ks = 0; ks < KS; ++ks) aoff[ks] = c * ROWB + (((((CH / 2) * g) + ks) ^ swzh<HD>(c)) << 4);
     // transposed A operand (Q^T or dO^T, dim rows 32 dt + c): 16-lane group
     // t = lane/16, index i = lane%16 reads query row 4 (t/2) + i/4 (and that
     // + 8), dims 32 dt + 16 (t%2) + 4 (i%4) .. +3
-    uint32_t tlo[4], thi[4];
+    uint32_t tlo[NDT], thi[NDT];
     {
         const int t = lane >> 4, i = lane & 15;
         const int row = 4 * (t >> 1) + (i >> 2);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+        for (int dt = 0; dt < NDT; ++dt) {
             const int chunk = 4 * dt + 2 * (t & 1) + ((i & 3) >> 1);
-            tlo[dt] = row * ROWB + ((chunk ^ swz(row)) << 4) + (i & 1) * 8;
-            thi[dt] = (row + 8) * ROWB + ((chunk ^ swz(row + 8)) << 4) + (i & 1) * 8;
+            tlo[dt] = row * ROWB + ((chunk ^ swzh<HD>(row)) << 4) + (i & 1) * 8;
+            thi[dt] = (row + 8) * ROWB + ((chunk ^ swzh<HD>(row + 8)) << 4) + (i & 1) * 8;
         }
     }
 
@@ -348,7 +372,7 @@ attn_bwd_dkdv(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
         const uint8_t *qb = qd + 32 * sb * ROWB, *ob = od + 32 * sb * ROWB;
         f32x16 s = {}, dp = {};
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
             const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(qb + aoff[ks]);
             const bf16x8 ao = *reinterpret_cast<const bf16x8 *>(ob + aoff[ks]);
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], s, 0, 0, 0);
@@ -380,7 +404,7 @@ attn_bwd_dkdv(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
+            for (int dt = 0; dt < NDT; ++dt) {
                 const bf16x8 ao = cat4(lds_read_tr(ob + 16 * hh * ROWB + tlo[dt]),
                                        lds_read_tr(ob + 16 * hh * ROWB + thi[dt]));
                 const bf16x8 aq = cat4(lds_read_tr(qb + 16 * hh * ROWB + tlo[dt]),
@@ -428,10 +452,10 @@ attn_bwd_dkdv(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const int key = kw0 + c;
     if (key < Nk) {
         const bool valid = key < Lk;
-        uint16_t *dkr = dK + (kvrow0 + key) * D;
-        uint16_t *dvr = dV + (kvrow0 + key) * D;
+        uint16_t *dkr = dK + (kvrow0 + key) * HD;
+        uint16_t *dvr = dV + (kvrow0 + key) * HD;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 uint2 wk, wv;
@@ -454,16 +478,26 @@ constexpr int DQ_NW = 256 / DQ_QW;             // wavefronts per workgroup (two 
 constexpr int DQ_BQ = DQ_QW * DQ_NW;           // queries per workgroup
 constexpr int DQ_BK = 32;                      // keys per tile
 constexpr int DQ_NT = 64 * DQ_NW;
-constexpr int DQ_TILEB = DQ_BK * ROWB;         // bytes per K or V tile
-constexpr int DQ_LPW = DQ_TILEB / 1024 / DQ_NW;  // 1 KiB loads per wave per K (or V) tile
-static_assert(DQ_LPW == 1, "kWaitVm2 assumes two loads per wave per tile");
+template <int HD> constexpr int kDqTileb = DQ_BK * BGeo<HD>::ROWB;   // bytes per K or V tile
 
+template <int HD>
 __global__ void __launch_bounds__(DQ_NT, 1)
 attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
             const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
             const float2 *__restrict__ LD, uint16_t *__restrict__ dQ, int Hq, int Hkv, int Nq,
             int Nk, const int32_t *__restrict__ seqlens_q, const int32_t *__restrict__ seqlens_k,
             float scale_log2, float scale, int causal, int nqb, int xcd_heads) {
+    using G = BGeo<HD>;
+    constexpr int ROWB = G::ROWB, CH = G::CH, RPB = G::RPB, KS = G::KS, NDT = G::NDT;
+    constexpr int DQ_TILEB = kDqTileb<HD>;
+    // 1 KiB DMA blocks per K (or V) tile, and loads per wave per tile: every
+    // wave loads one block of K and one of V (head dim 128), or one block of
+    // K (waves 0-3) or of V (waves 4-7, head dim 64)
+    constexpr int NBLK = DQ_TILEB / 1024;
+    constexpr int LPT = 2 * NBLK / DQ_NW;
+    static_assert(LPT >= 1 && LPT * DQ_NW == 2 * NBLK, "whole 1 KiB loads per wave per tile");
+    // wait for this wave's loads of one tile, those of the next in flight
+    constexpr int kWaitTile = 0x0F70 | LPT;
     // ring of three K slots and three V slots
     __shared__ __attribute__((aligned(1024))) uint8_t k0[DQ_TILEB], k1[DQ_TILEB], k2[DQ_TILEB];
     __shared__ __attribute__((aligned(1024))) uint8_t v0[DQ_TILEB], v1[DQ_TILEB], v2[DQ_TILEB];
@@ -493,14 +527,14 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const int q0 = qb0 * DQ_BQ;
     const int qw0 = q0 + DQ_QW * wave;           // queries qw0 + 32 qb + c
     const size_t qrow0 = (size_t)(b * Hq + h) * Nq;
-    const uint16_t *Kh = K + (size_t)(b * Hkv + kvh) * Nk * D;
-    const uint16_t *Vh = V + (size_t)(b * Hkv + kvh) * Nk * D;
+    const uint16_t *Kh = K + (size_t)(b * Hkv + kvh) * Nk * HD;
+    const uint16_t *Vh = V + (size_t)(b * Hkv + kvh) * Nk * HD;
 
     if (q0 >= Lq || Lk == 0) {
         // every row of this block is padding, or there is no key: dQ = 0
         const int rows = min(DQ_BQ, Nq - q0);
-        for (int i = tid; i < rows * (D / 8); i += DQ_NT)
-            *reinterpret_cast<uint4 *>(dQ + (qrow0 + q0 + i / (D / 8)) * D + (i % (D / 8)) * 8) =
+        for (int i = tid; i < rows * (HD / 8); i += DQ_NT)
+            *reinterpret_cast<uint4 *>(dQ + (qrow0 + q0 + i / (HD / 8)) * HD + (i % (HD / 8)) * 8) =
                 make_uint4(0, 0, 0, 0);
         return;
     }
@@ -515,18 +549,18 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     if (Lk % DQ_BK) wmask = min(wmask, Lk / DQ_BK);
 
     // Q and dO fragments (B operands): lane (g, c) holds row qw0 + 32 qb + c,
-    // dims 64 g + 8 ks + 0..7; rows at or past Lq are zero
-    bf16x8 qf[DQ_NQB][8], df[DQ_NQB][8];
+    // dims (HD / 2) g + 8 ks + 0..7; rows at or past Lq are zero
+    bf16x8 qf[DQ_NQB][KS], df[DQ_NQB][KS];
     float l2[DQ_NQB], dd[DQ_NQB];
 #pragma unroll
     for (int qb = 0; qb < DQ_NQB; ++qb) {
         const int qi = qw0 + 32 * qb + c;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
             uint4 wq = make_uint4(0, 0, 0, 0), wo = make_uint4(0, 0, 0, 0);
             if (qi < Lq) {
-                wq = *reinterpret_cast<const uint4 *>(Q + (qrow0 + qi) * D + 64 * g + 8 * ks);
-                wo = *reinterpret_cast<const uint4 *>(dO + (qrow0 + qi) * D + 64 * g + 8 * ks);
+                wq = *reinterpret_cast<const uint4 *>(Q + (qrow0 + qi) * HD + (HD / 2) * g + 8 * ks);
+                wo = *reinterpret_cast<const uint4 *>(dO + (qrow0 + qi) * HD + (HD / 2) * g + 8 * ks);
             }
             qf[qb][ks] = __builtin_bit_cast(bf16x8, wq);
             df[qb][ks] = __builtin_bit_cast(bf16x8, wo);
@@ -535,50 +569,49 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
         l2[qb] = x.x;
         dd[qb] = x.y;
     }
-    f32x16 dqa[DQ_NQB][4];
+    f32x16 dqa[DQ_NQB][NDT];
     {
         const bf16x8 z8 = {};
 #pragma unroll
         for (int qb = 0; qb < DQ_NQB; ++qb)
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) acc_zero(dqa[qb][dt], z8);
+            for (int dt = 0; dt < NDT; ++dt) acc_zero(dqa[qb][dt], z8);
     }
 
-    // tile DMA: load i of wave w fills LDS block DQ_LPW w + i (rows 4 blk ..
-    // + 3) of a slot; lane l row 4 blk + l/16, slot l%16.  Rows at or past
-    // Lk read as zeros.
-    uint32_t dmo[DQ_LPW];
-#pragma unroll
-    for (int i = 0; i < DQ_LPW; ++i) {
-        const int row = 4 * (DQ_LPW * wave + i) + (lane >> 4);
-        dmo[i] = row * ROWB + (((lane & 15) ^ swz(row)) << 4);
-    }
+    // tile DMA: this wave fills LDS block dblk (rows RPB dblk .. + RPB - 1) of
+    // a K slot and a V slot (head dim 128), or of one of them (head dim 64);
+    // lane l row RPB dblk + l/CH, slot l%CH.  Rows at or past Lk read as zeros.
+    const int dblk = wave % NBLK;
+    const int drow = RPB * dblk + (lane >> G::kLogCH);
+    const uint32_t dmo = drow * ROWB + (((lane & (CH - 1)) ^ swzh<HD>(drow)) << 4);
     auto issue = [&](uint8_t *kd, uint8_t *vd, int t) __attribute__((always_inline)) {
         const int j0 = t * DQ_BK;
         const int bytes = max(0, Lk - j0) * ROWB;
-        const __amdgpu_buffer_rsrc_t rk = rsrc(Kh + (size_t)j0 * D, bytes);
-        const __amdgpu_buffer_rsrc_t rv = rsrc(Vh + (size_t)j0 * D, bytes);
-#pragma unroll
-        for (int i = 0; i < DQ_LPW; ++i) {
-            dma16(rk, kd + (DQ_LPW * wave + i) * 1024, dmo[i]);
-            dma16(rv, vd + (DQ_LPW * wave + i) * 1024, dmo[i]);
+        const __amdgpu_buffer_rsrc_t rk = rsrc(Kh + (size_t)j0 * HD, bytes);
+        const __amdgpu_buffer_rsrc_t rv = rsrc(Vh + (size_t)j0 * HD, bytes);
+        if constexpr (LPT == 2) {
+            dma16(rk, kd + dblk * 1024, dmo);
+            dma16(rv, vd + dblk * 1024, dmo);
+        } else {
+            if (wave < NBLK) dma16(rk, kd + dblk * 1024, dmo);
+            else dma16(rv, vd + dblk * 1024, dmo);
         }
     };
 
-    // row-wise A operand (rows of K or V): lane (g, c) reads row c, chunk 8 g + ks
-    uint32_t aoff[8];
+    // row-wise A operand (rows of K or V): lane (g, c) reads row c, chunk (CH / 2) g + ks
+    uint32_t aoff[KS];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) aoff[ks] = c * ROWB + ((((8 * g) + ks) ^ swz(c)) << 4);
+    for (int ks = 0; ks < KS; ++ks) aoff[ks] = c * ROWB + (((((CH / 2) * g) + ks) ^ swzh<HD>(c)) << 4);
     // transposed A operand K^T (dim rows 32 dt + c): as in attn_bwd_dkdv
-    uint32_t tlo[4], thi[4];
+    uint32_t tlo[NDT], thi[NDT];
     {
         const int t = lane >> 4, i = lane & 15;
         const int row = 4 * (t >> 1) + (i >> 2);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+        for (int dt = 0; dt < NDT; ++dt) {
             const int chunk = 4 * dt + 2 * (t & 1) + ((i & 3) >> 1);
-            tlo[dt] = row * ROWB + ((chunk ^ swz(row)) << 4) + (i & 1) * 8;
-            thi[dt] = (row + 8) * ROWB + ((chunk ^ swz(row + 8)) << 4) + (i & 1) * 8;
+            tlo[dt] = row * ROWB + ((chunk ^ swzh<HD>(row)) << 4) + (i & 1) * 8;
+            thi[dt] = (row + 8) * ROWB + ((chunk ^ swzh<HD>(row + 8)) << 4) + (i & 1) * 8;
         }
     }
 
@@ -601,7 +634,7 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
         const f32x16 zero = {};
         f32x16 s[DQ_NQB], dp[DQ_NQB];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
             const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(kb + aoff[ks]);
             const bf16x8 av = *reinterpret_cast<const bf16x8 *>(vb + aoff[ks]);
 #pragma unroll
@@ -626,7 +659,7 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
+            for (int dt = 0; dt < NDT; ++dt) {
                 const bf16x8 a = cat4(lds_read_tr(kb + 16 * hh * ROWB + tlo[dt]),
                                       lds_read_tr(kb + 16 * hh * ROWB + thi[dt]));
 #pragma unroll
@@ -648,10 +681,10 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     // iteration j (slot j % 3): this wave's loads of tile j are done (those
     // of tile j + 1 may be in flight), the barrier makes every wave's visible
     // and frees slot (j + 2) % 3, which receives tile j + 2.  Every iteration
-    // issues exactly four loads per wave (tiles past the end are zero fills),
+    // issues the same LPT loads per wave (tiles past the end are zero fills),
     // so the wait count is the same everywhere.
     auto iter = [&](auto S, int j) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(kWaitVm2);
+        __builtin_amdgcn_s_waitcnt(kWaitTile);
         tile_barrier();
         issue(kslot(Slot<decltype(S)::value + 2>{}), vslot(Slot<decltype(S)::value + 2>{}), j + 2);
         if (j < wtiles) compute(kslot(S), vslot(S), j, j >= wmask);
@@ -675,9 +708,9 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
         const int qi = qw0 + 32 * qb + c;
         if (qi < Nq) {
             const bool valid = qi < Lq;
-            uint16_t *row = dQ + (qrow0 + qi) * D;
+            uint16_t *row = dQ + (qrow0 + qi) * HD;
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
+            for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     uint2 w;
@@ -691,7 +724,10 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 
 }  // namespace
 
-hipError_t launch_attn_bwd(const AttnBwdArgs &a, hipStream_t s) {
+namespace {
+
+template <int HD>
+hipError_t launch_bwd(const AttnBwdArgs &a, hipStream_t s) {
     const int64_t rows = (int64_t)a.batch * a.heads_q * a.seqlen_q;
     float2 *ld = static_cast<float2 *>(a.workspace);
     const uint16_t *q = static_cast<const uint16_t *>(a.q), *k = static_cast<const uint16_t *>(a.k);
@@ -699,8 +735,8 @@ hipError_t launch_attn_bwd(const AttnBwdArgs &a, hipStream_t s) {
     const uint16_t *dout = static_cast<const uint16_t *>(a.dout);
     const float scale_log2 = a.scale * kLog2e;
     if (rows > 0) {
-        hipLaunchKernelGGL(attn_bwd_pre, dim3((unsigned)((rows + PRE_ROWS - 1) / PRE_ROWS)), dim3(PRE_NT), 0, s,
-                           o, dout, a.lse, ld, rows, a.seqlen_q, a.heads_q, a.seqlens_q);
+        hipLaunchKernelGGL(attn_bwd_pre<HD>, dim3((unsigned)((rows + kPreRows<HD> - 1) / kPreRows<HD>)),
+                           dim3(PRE_NT), 0, s, o, dout, a.lse, ld, rows, a.seqlen_q, a.heads_q, a.seqlens_q);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -710,12 +746,12 @@ hipError_t launch_attn_bwd(const AttnBwdArgs &a, hipStream_t s) {
         const int xcd_heads = (nheads % 8 == 0) ? 1 : 0;
         const dim3 grid((unsigned)((int64_t)nkb * nheads));
         if (a.causal)
-            hipLaunchKernelGGL(attn_bwd_dkdv<true>, grid, dim3(KV_NT), 0, s, q, k, v, dout, ld,
+            hipLaunchKernelGGL((attn_bwd_dkdv<true, HD>), grid, dim3(KV_NT), 0, s, q, k, v, dout, ld,
                                static_cast<uint16_t *>(a.dk), static_cast<uint16_t *>(a.dv), a.heads_q,
                                a.heads_kv, a.seqlen_q, a.seqlen_k, a.seqlens_q, a.seqlens_k, scale_log2,
                                a.scale, nkb, xcd_heads);
         else
-            hipLaunchKernelGGL(attn_bwd_dkdv<false>, grid, dim3(KV_NT), 0, s, q, k, v, dout, ld,
+            hipLaunchKernelGGL((attn_bwd_dkdv<false, HD>), grid, dim3(KV_NT), 0, s, q, k, v, dout, ld,
                                static_cast<uint16_t *>(a.dk), static_cast<uint16_t *>(a.dv), a.heads_q,
                                a.heads_kv, a.seqlen_q, a.seqlen_k, a.seqlens_q, a.seqlens_k, scale_log2,
                                a.scale, nkb, xcd_heads);
@@ -726,12 +762,18 @@ hipError_t launch_attn_bwd(const AttnBwdArgs &a, hipStream_t s) {
         const int nqb = (a.seqlen_q + DQ_BQ - 1) / DQ_BQ;
         const int nheads = a.batch * a.heads_q;
         const int xcd_heads = (nheads % 8 == 0) ? 1 : 0;
-        hipLaunchKernelGGL(attn_bwd_dq, dim3((unsigned)((int64_t)nqb * nheads)), dim3(DQ_NT), 0, s, q, k, v,
+        hipLaunchKernelGGL(attn_bwd_dq<HD>, dim3((unsigned)((int64_t)nqb * nheads)), dim3(DQ_NT), 0, s, q, k, v,
                            dout, ld, static_cast<uint16_t *>(a.dq), a.heads_q, a.heads_kv, a.seqlen_q,
                            a.seqlen_k, a.seqlens_q, a.seqlens_k, scale_log2, a.scale, a.causal, nqb, xcd_heads);
         return hipGetLastError();
     }
     return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(const AttnBwdArgs &a, hipStream_t s) {
+    return a.head_dim == 128 ? launch_bwd<128>(a, s) : launch_bwd<64>(a, s);
 }
 
 }  // namespace osm

@@ -220,12 +220,13 @@ size_t osm_attn_bwd_workspace_bytes(int32_t batch, int32_t heads_q, int32_t seql
  * Three kernels are enqueued on `stream`: the per-row (lse, dO . O), then
  * dK/dV (key-major), then dQ (query-major).  No atomics: the result is
  * deterministic.
- * Supported: dtype OSM_BF16, head_dim 128, batch * heads_q < 2^31; fp32
- * accumulation, P and dS rounded to bf16 as matrix-product operands,
+ * Supported: dtype OSM_BF16, head_dim 128 or 64, batch * heads_q < 2^31;
+ * fp32 accumulation, P and dS rounded to bf16 as matrix-product operands,
  * gradients rounded to bf16 once at the end; every pointer 16-byte aligned.
  * Errors: OSM_ERR_NULL, OSM_ERR_SHAPE (as osm_attn_fwd),
  * OSM_ERR_UNSUPPORTED (other dtype or head_dim, a pointer not 16-byte
- * aligned, batch * heads_q >= 2^31, seqlen_q or seqlen_k >= 2^23),
+ * aligned, batch * heads_q >= 2^31, seqlen_q or seqlen_k >= 2^23 at
+ * head_dim 128, 2^24 at 64),
  * OSM_ERR_WORKSPACE, OSM_ERR_HIP.
  */
 osm_status osm_attn_bwd(const void *q, const void *k, const void *v, const void *o,

@@ -270,9 +270,13 @@ def test_attn_bwd_validation(lib):
     assert call(scale=0.0) == 2
     assert call(scale=float("inf")) == 2
     assert call(causal=2) == 2
-    assert call(d=64) == 3
+    assert call(d=96) == 3
+    assert call(d=256) == 3
     assert call(dtype=osm.OSM_F32) == 3
     assert call(Nk=1 << 23) == 3                    # one head's rows span 2 GiB
+    assert call(d=64, q=None) == 1                  # head dim 64 is supported: fails only at the NULL check
+    assert call(d=64, Nk=1 << 23, q=None) == 1      # at head dim 64 the same keys span 1 GiB
+    assert call(d=64, Nq=1 << 24) == 3
     assert call(Nq=0, Nk=0, q=None, k=None) == 0    # nothing to do
     for name in ("q", "o", "do", "lse", "dq", "k", "v", "dk", "dv"):
         assert call(**{name: None}) == 1, name

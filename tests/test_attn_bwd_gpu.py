@@ -1,7 +1,8 @@
 """osm_attn_bwd on the GPU against the oracle's gradients: element by
 element on small ragged shapes (several tiles, ragged tails, grouped
 heads, padding with NaN poison, empty lengths), whole heads at the full
-benchmark sizes, and the bit-exact causal and padding properties.
+benchmark sizes, and the bit-exact causal and padding properties; head
+dims 128 and 64.
 
 The forward that feeds the backward is the GPU forward (its O and LSE), as
 in use; the oracle differentiates the exact forward of the same bf16 inputs.
@@ -57,6 +58,7 @@ def check_all(got, ref, tag):
         check_grad(host(g), r, f"{tag} {name}")
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,causal", [
     (1, 2, 1, 300, 300, False),
     (1, 2, 1, 300, 300, True),
@@ -67,25 +69,26 @@ def check_all(got, ref, tag):
     (1, 1, 1, 1, 64, True),
     (1, 2, 2, 640, 640, True),
 ])
-def test_small(orc, B, Hq, Hkv, Nq, Nk, causal):
-    announce(f"bwd B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} causal={causal}")
-    seed = 7000 + B * 1000 + Nq + Nk
-    inp = inputs.attention_inputs(B, Hq, Hkv, Nq, Nk, 128, seed=seed, causal=causal)
-    do = inputs.output_grad(B, Hq, Nq, 128, seed + 1)
+def test_small(orc, B, Hq, Hkv, Nq, Nk, causal, d):
+    announce(f"bwd B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} causal={causal}")
+    seed = 7000 + B * 1000 + Nq + Nk + (d == 64)
+    inp = inputs.attention_inputs(B, Hq, Hkv, Nq, Nk, d, seed=seed, causal=causal)
+    do = inputs.output_grad(B, Hq, Nq, d, seed + 1)
     check_all(run(inp, do), oracle(orc, inp, do), "small")
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("causal", [False, True])
-def test_varlen_poisoned(orc, causal):
+def test_varlen_poisoned(orc, causal, d):
     """Right padding with NaN in q, k, v and dO past the lengths: gradients
     match, padded rows are exactly 0, and the result is bit-identical to
     zero padding."""
-    announce(f"bwd varlen poisoned causal={causal}")
+    announce(f"bwd varlen poisoned d={d} causal={causal}")
     B, H, N = 4, 2, 400
     lens = np.array([1, 130, 257, 400], np.int32)
-    inp = inputs.attention_inputs(B, H, H, N, N, 128, seed=61, causal=causal, seqlens_q=lens,
+    inp = inputs.attention_inputs(B, H, H, N, N, d, seed=61, causal=causal, seqlens_q=lens,
                                   seqlens_k=lens, poison=True)
-    do = inputs.output_grad(B, H, N, 128, 62, seqlens_q=lens, poison=True)
+    do = inputs.output_grad(B, H, N, d, 62, seqlens_q=lens, poison=True)
     got = run(inp, do)
     check_all(got, oracle(orc, inp, do), "varlen")
     for g in got:
@@ -102,28 +105,30 @@ def test_varlen_poisoned(orc, causal):
         assert np.array_equal(host_bits(g), host_bits(g0))
 
 
-def test_empty_lengths(orc):
+@pytest.mark.parametrize("d", [128, 64])
+def test_empty_lengths(orc, d):
     """A batch with no valid query and one with no valid key: their
     gradients are exactly zero; the others match."""
-    announce("bwd empty lengths")
+    announce(f"bwd empty lengths d={d}")
     sq = np.array([0, 150, 90], np.int32)
     sk = np.array([200, 0, 37], np.int32)
-    inp = inputs.attention_inputs(3, 4, 2, 150, 200, 128, seed=63, seqlens_q=sq, seqlens_k=sk,
+    inp = inputs.attention_inputs(3, 4, 2, 150, 200, d, seed=63, seqlens_q=sq, seqlens_k=sk,
                                   poison=True)
-    do = inputs.output_grad(3, 4, 150, 128, 64, seqlens_q=sq, poison=True)
+    do = inputs.output_grad(3, 4, 150, d, 64, seqlens_q=sq, poison=True)
     got = run(inp, do)
     check_all(got, oracle(orc, inp, do), "empty")
     dq, dk, dv = (host(g) for g in got)
     assert not dq[0].any() and not dk[1].any() and not dv[1].any() and not dq[1].any()
 
 
-def test_causal_locality():
+@pytest.mark.parametrize("d", [128, 64])
+def test_causal_locality(d):
     """Causal: dQ of rows before 200 does not depend on keys from 200 on, and
     dK, dV of keys from 200 on do not depend on queries before 200 (bit for
     bit)."""
-    announce("bwd causal locality")
-    inp = inputs.attention_inputs(1, 2, 2, 512, 512, 128, seed=65, causal=True)
-    do = inputs.output_grad(1, 2, 512, 128, 66)
+    announce(f"bwd causal locality d={d}")
+    inp = inputs.attention_inputs(1, 2, 2, 512, 512, d, seed=65, causal=True)
+    do = inputs.output_grad(1, 2, 512, d, 66)
     dq1, dk1, dv1 = run(inp, do)
     k2, v2 = inp.k.copy(), inp.v.copy()
     k2[:, :, 200:] = inputs.to_bf16_bits(np.full(k2[:, :, 200:].shape, 0.5, np.float32))
@@ -139,10 +144,11 @@ def test_causal_locality():
     assert np.array_equal(host_bits(dv1)[:, :, 200:], host_bits(dv3)[:, :, 200:])
 
 
-def test_deterministic():
-    announce("bwd deterministic")
-    inp = inputs.attention_inputs(2, 4, 1, 333, 333, 128, seed=67, causal=True)
-    do = inputs.output_grad(2, 4, 333, 128, 68)
+@pytest.mark.parametrize("d", [128, 64])
+def test_deterministic(d):
+    announce(f"bwd deterministic d={d}")
+    inp = inputs.attention_inputs(2, 4, 1, 333, 333, d, seed=67, causal=True)
+    do = inputs.output_grad(2, 4, 333, d, 68)
     a, b = run(inp, do), run(inp, do)
     for x, y in zip(a, b):
         assert np.array_equal(host_bits(x), host_bits(y))
@@ -193,11 +199,28 @@ def test_full_size_causal_varlen_heads(orc):
             assert np.all(gh[b, :, L:] == 0.0)
 
 
-def test_random_sweep(orc):
+def test_full_size_heads_d64(orc):
+    """B4 H64 N4096 d64 non-causal (the head-dim-64 forward's benchmark
+    shape): two whole heads of every gradient against the oracle."""
+    announce("bwd B4 H64 N4096 d64 full size, two heads")
+    inp = inputs.attention_inputs(4, 64, 64, 4096, 4096, 64, seed=inputs.SEED_BASE + 11)
+    do = inputs.output_grad(4, 64, 4096, 64, inputs.SEED_BASE + 12)
+    dq, dk, dv = run(inp, do)
+    heads = [0, 63]
+    sub, dsub = _head_slice(inp, do, 3, heads)
+    ref = oracle(orc, sub, dsub)
+    for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        check_grad(host(g[3:4, heads]), r, f"full d64 {name}")
+    for g in (dq, dk, dv):
+        assert not np.isnan(host(g)).any()
+
+
+@pytest.mark.parametrize("d,seed0,cases", [(128, 4545, 20), (64, 4546, 12)])
+def test_random_sweep(orc, d, seed0, cases):
     """Seeded random configurations against the oracle's gradients: GQA
     group, ragged lengths, masks, scale, NaN-poisoned padding."""
-    g = inputs.rng(4545)
-    for case in range(20):
+    g = inputs.rng(seed0)
+    for case in range(cases):
         B = int(g.integers(1, 3))
         Hkv = int(g.choice([1, 2]))
         Hq = Hkv * int(g.choice([1, 2, 4]))
@@ -211,10 +234,10 @@ def test_random_sweep(orc):
         if mode == 2:
             sq = g.integers(1, Nq + 1, size=B).astype(np.int32)
         scale = float(g.uniform(0.03, 0.12))
-        announce(f"bwd sweep {case}: B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} causal={causal} "
+        announce(f"bwd sweep d={d} {case}: B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} causal={causal} "
                  f"seqlens_q={None if sq is None else sq.tolist()} seqlens_k={None if sk is None else sk.tolist()}")
-        seed = 9000 + case
-        inp = inputs.attention_inputs(B, Hq, Hkv, Nq, Nk, 128, seed=seed, causal=causal, scale=scale,
+        seed = 9000 + case + (100 if d == 64 else 0)
+        inp = inputs.attention_inputs(B, Hq, Hkv, Nq, Nk, d, seed=seed, causal=causal, scale=scale,
                                       seqlens_q=sq, seqlens_k=sk, poison=sk is not None)
-        do = inputs.output_grad(B, Hq, Nq, 128, seed + 1, seqlens_q=sq, poison=sq is not None)
-        check_all(run(inp, do), oracle(orc, inp, do), f"sweep {case}")
+        do = inputs.output_grad(B, Hq, Nq, d, seed + 1, seqlens_q=sq, poison=sq is not None)
+        check_all(run(inp, do), oracle(orc, inp, do), f"sweep d={d} {case}")
