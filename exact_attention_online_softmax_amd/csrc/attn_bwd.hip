@@ -387,11 +387,26 @@ attn_bwd_dkdv(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
             const float dd[4] = {x0.y, x0.w, x1.y, x1.w};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                float e = fast_exp2(fmaf(s[4 * r + u], scale_log2, -l2[u]));
-                if (CAUSAL) e = (kw0 + c > qs0 + 8 * r + 4 * g + u) ? 0.0f : e;
+                const float e = fast_exp2(fmaf(s[4 * r + u], scale_log2, -l2[u]));
                 p[4 * r + u] = e;
                 ds[4 * r + u] = e * (dp[4 * r + u] - dd[u]);
             }
+        }
+        // causal: only a block that crosses the diagonal (some key of the
+        // wave after some query of the block) has weights to zero, so the
+        // selects sit behind a wave-uniform branch.  P and dS are both
+        // zeroed there, which keeps every value the branch joins already
+        // live in the unmasked body (80 VALU per block against 128 when
+        // every block selected).
+        if (CAUSAL && kw0 + 31 > qs0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const bool after = kw0 + c > qs0 + 8 * r + 4 * g + u;
+                    p[4 * r + u] = after ? 0.0f : p[4 * r + u];
+                    ds[4 * r + u] = after ? 0.0f : ds[4 * r + u];
+                }
         }
         bf16x8 pb[2], db[2];
 #pragma unroll
