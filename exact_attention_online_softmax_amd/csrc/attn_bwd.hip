@@ -30,7 +30,7 @@
 //    sum over the whole head group in registers: no atomics.
 //  * attn_bwd_dq: query-major, laid out like the forward.  A workgroup owns
 //    256 queries (32 per wave, eight waves, two per SIMD; Q and dO fragments
-//    in registers, dQ accumulators in the AGPRs) and streams K and V tiles of
+//    and the dQ accumulators in registers) and streams K and V tiles of
 //    32 keys through a ring of three LDS slots: S^T = K Q^T, dP^T = V dO^T,
 //    dS^T, and dQ^T += K^T dS^T.
 // Splitting dQ from dK/dV computes S and dP twice (7 matrix products per
@@ -110,12 +110,15 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t *p) {
     return __builtin_bit_cast(bf16x4, r);
 }
 
-// Accumulation MFMA with the accumulator pinned to AGPRs.  The products
-// whose results the vector ALU reads (S, dP) write VGPRs (the file is built
-// with the VGPR form of the MFMA builtins); the gradient accumulators, read
-// only at the end, fit only in the AGPRs, so their MFMAs are inline
-// assembly.  The hazard recognizer does not look into inline assembly: two
-// wait states let a VALU-written operand settle before the MFMA reads it.
+// Accumulation MFMA with the accumulator pinned to AGPRs (attn_bwd_dkdv).
+// The products whose results the vector ALU reads (S, dP) write VGPRs (the
+// builtins' VGPR form); dK and dV, read only at the end, fit only in the
+// AGPRs, so their MFMAs are inline assembly.  (A kernel that uses AGPRs gets
+// at most half of its registers as VGPRs; attn_bwd_dq, whose 64 accumulator
+// registers fit beside everything else, keeps them in VGPRs and has the
+// whole budget for them.)  The hazard recognizer does not look into inline
+// assembly: two wait states let a VALU-written operand settle before the
+// MFMA reads it.
 //
 // NOP: the two wait states, for the first MFMA that reads a P or dS operand
 // converted just before it.  Later uses of the same operand come after that
@@ -585,13 +588,12 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
         dd[qb] = x.y;
     }
     f32x16 dqa[DQ_NQB][NDT];
-    {
-        const bf16x8 z8 = {};
 #pragma unroll
-        for (int qb = 0; qb < DQ_NQB; ++qb)
+    for (int qb = 0; qb < DQ_NQB; ++qb)
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) acc_zero(dqa[qb][dt], z8);
-    }
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) dqa[qb][dt][i] = 0.0f;
 
     // tile DMA: this wave fills LDS block dblk (rows RPB dblk .. + RPB - 1) of
     // a K slot and a V slot (head dim 128), or of one of them (head dim 64);
@@ -648,15 +650,29 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     auto compute = [&](const uint8_t *kb, const uint8_t *vb, int t, bool masked) __attribute__((always_inline)) {
         const f32x16 zero = {};
         f32x16 s[DQ_NQB], dp[DQ_NQB];
+        // K and V operands read DQ_RA k-steps ahead of their MFMAs (at head
+        // dim 64 one: a deeper read-ahead takes the kernel past 128 VGPRs, and
+        // with it two workgroups per CU)
+        constexpr int DQ_RA = HD == 128 ? 3 : 1;
+        bf16x8 ak[KS], av[KS];
+#pragma unroll
+        for (int ks = 0; ks < DQ_RA; ++ks) {
+            ak[ks] = *reinterpret_cast<const bf16x8 *>(kb + aoff[ks]);
+            av[ks] = *reinterpret_cast<const bf16x8 *>(vb + aoff[ks]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(kb + aoff[ks]);
-            const bf16x8 av = *reinterpret_cast<const bf16x8 *>(vb + aoff[ks]);
+            if (ks + DQ_RA < KS) {
+                ak[ks + DQ_RA] = *reinterpret_cast<const bf16x8 *>(kb + aoff[ks + DQ_RA]);
+                av[ks + DQ_RA] = *reinterpret_cast<const bf16x8 *>(vb + aoff[ks + DQ_RA]);
+            }
 #pragma unroll
             for (int qb = 0; qb < DQ_NQB; ++qb) {
-                s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[qb][ks], ks ? s[qb] : zero, 0, 0, 0);
-                dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, df[qb][ks], ks ? dp[qb] : zero, 0, 0, 0);
+                s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[ks], qf[qb][ks], ks ? s[qb] : zero, 0, 0, 0);
+                dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks], df[qb][ks], ks ? dp[qb] : zero, 0, 0, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (masked) mask(s, t);
         // dS^T = P^T (dP^T - D), P^T = exp2(S^T scale log2e - lse2): one query per lane
@@ -678,10 +694,8 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                 const bf16x8 a = cat4(lds_read_tr(kb + 16 * hh * ROWB + tlo[dt]),
                                       lds_read_tr(kb + 16 * hh * ROWB + thi[dt]));
 #pragma unroll
-                for (int qb = 0; qb < DQ_NQB; ++qb) {
-                    if (dt == 0) mfma_acc<true>(dqa[qb][dt], a, db[qb][hh]);
-                    else mfma_acc<false>(dqa[qb][dt], a, db[qb][hh]);
-                }
+                for (int qb = 0; qb < DQ_NQB; ++qb)
+                    dqa[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, db[qb][hh], dqa[qb][dt], 0, 0, 0);
             }
     };
 
@@ -716,8 +730,6 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     __builtin_amdgcn_s_waitcnt(kWaitVm0);       // no load outlives the kernel
 
     // ---- epilogue: dQ = scale dQ~; rows past Lq get zeros ------------------
-#pragma unroll
-    for (int qb = 0; qb < DQ_NQB; ++qb) acc_settle(dqa[qb]);
 #pragma unroll
     for (int qb = 0; qb < DQ_NQB; ++qb) {
         const int qi = qw0 + 32 * qb + c;
