@@ -22,7 +22,10 @@
 //    per 64-dim k-step).  The softmax VALU per MFMA clock is twice the bf16
 //    kernel's (an FP8 MFMA does twice the work per clock), so the second wave
 //    on the SIMD is what keeps the matrix core fed while one wave
-//    exponentiates; 208 registers per wave make that possible.
+//    exponentiates.  That leaves a wave 256 registers: 128 VGPRs and the
+//    AGPRs, which hold O~ and some of the spilled values (the compiler caps
+//    the VGPRs of a kernel that uses AGPRs at half); the rest, 36 bytes per
+//    lane (92 on the persistent grid), goes to scratch, two reloads per tile.
 //  * tiles of 64 keys (the MFMA's k for P~V): K and V tiles of 64 rows x 128
 //    bytes go from HBM straight into LDS through buffer loads with LDS
 //    destination (rows past Lk read as zeros), through a ring of four slots
