@@ -126,6 +126,30 @@ def _device_tensor(t, name, dtypes):
     return t
 
 
+def _out_tensor(t, name, shape, dtype, device):
+    """A caller-supplied output: the kernels write exactly ``shape`` contiguous
+    elements of ``dtype`` through its pointer, so anything else is refused
+    before the launch."""
+    _device_tensor(t, name, (dtype,))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device} (got {t.device})")
+    return t
+
+
+def _workspace(ws, nbytes, device):
+    """The caller's device workspace (bytes), or a new one of ``nbytes``; the
+    library checks its size, this checks that it is device memory."""
+    torch = _torch()
+    if ws is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    _device_tensor(ws, "workspace", (torch.uint8,))
+    if ws.device != device:
+        raise ValueError(f"workspace must be on {device} (got {ws.device})")
+    return ws
+
+
 def _dtype_code(dt):
     torch = _torch()
     return {torch.float32: OSM_F32, torch.bfloat16: OSM_BF16}[dt]
@@ -186,8 +210,9 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, seqlens_q=None, seqlens_k=Non
         raise ValueError("q, k, v shapes are inconsistent")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(q) if out is None else out
-    lse_t = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = torch.empty_like(q) if out is None else _out_tensor(out, "out", q.shape, q.dtype, q.device)
+    lse_t = (torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None
+             else _out_tensor(lse, "lse", (B, Hq, Nq), torch.float32, q.device))
     sq = _lengths(seqlens_q, "seqlens_q", B, q.device)
     sk = _lengths(seqlens_k, "seqlens_k", B, q.device)
     _check(lib.osm_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t),
@@ -214,8 +239,10 @@ def attn_fwd_fp8(q, k, v, *, scale=None, v_scale=1.0, causal=False, seqlens_q=No
         raise ValueError("q, k, v shapes are inconsistent")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=q.device) if out is None else out
-    lse_t = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = (torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=q.device) if out is None
+         else _out_tensor(out, "out", (B, Hq, Nq, d), torch.bfloat16, q.device))
+    lse_t = (torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None
+             else _out_tensor(lse, "lse", (B, Hq, Nq), torch.float32, q.device))
     sq = _lengths(seqlens_q, "seqlens_q", B, q.device)
     sk = _lengths(seqlens_k, "seqlens_k", B, q.device)
     _check(lib.osm_attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, Hq, Hkv, Nq, Nk, d,
@@ -249,12 +276,10 @@ def attn_bwd(q, k, v, o, lse, dout, *, scale=None, causal=False, seqlens_q=None,
         scale = 1.0 / math.sqrt(d)
     sq = _lengths(seqlens_q, "seqlens_q", B, q.device)
     sk = _lengths(seqlens_k, "seqlens_k", B, q.device)
-    nbytes = attn_bwd_workspace_bytes(B, Hq, Nq)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    workspace = _workspace(workspace, attn_bwd_workspace_bytes(B, Hq, Nq), q.device)
+    dq = torch.empty_like(q) if dq is None else _out_tensor(dq, "dq", q.shape, q.dtype, q.device)
+    dk = torch.empty_like(k) if dk is None else _out_tensor(dk, "dk", k.shape, k.dtype, q.device)
+    dv = torch.empty_like(v) if dv is None else _out_tensor(dv, "dv", v.shape, v.dtype, q.device)
     _check(lib.osm_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                             _ptr(dk), _ptr(dv), _dtype_code(q.dtype), B, Hq, Hkv, Nq, Nk, d, _ptr(sq),
                             _ptr(sk), float(scale), int(bool(causal)), _ptr(workspace),
@@ -280,15 +305,16 @@ def attn_decode_splitkv(q, k_cache, v_cache, seqlens_k, *, scale=None, split_siz
     if q.dim() != 3 or k_cache.dim() != 4 or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("q must be [B, Hq, d]; caches [B, Hkv, Lmax, d]")
     B, Hq, d = q.shape
-    _, Hkv, Lmax, _ = k_cache.shape
+    Bk, Hkv, Lmax, dk_ = k_cache.shape
+    if Bk != B or dk_ != d:
+        raise ValueError("the caches' batch and head_dim must match q's")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     sk = _lengths(seqlens_k, "seqlens_k", B, q.device)
-    nbytes = decode_workspace_bytes(B, Hq, Lmax, d, split_size)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q) if out is None else out
-    lse_t = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    workspace = _workspace(workspace, decode_workspace_bytes(B, Hq, Lmax, d, split_size), q.device)
+    o = torch.empty_like(q) if out is None else _out_tensor(out, "out", q.shape, q.dtype, q.device)
+    lse_t = (torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None
+             else _out_tensor(lse, "lse", (B, Hq), torch.float32, q.device))
     _check(lib.osm_attn_decode_splitkv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o),
                                        _ptr(lse_t), _dtype_code(q.dtype), B, Hq, Hkv, Lmax, d,
                                        _ptr(sk), float(scale), int(split_size), _ptr(workspace),
@@ -329,8 +355,10 @@ def merge_lse(o_parts, lse_parts, out_dtype=None, out=None, lse=None):
     if tuple(lse_parts.shape) != (S, rows):
         raise ValueError("lse_parts shape does not match o_parts")
     out_dtype = o_parts.dtype if out_dtype is None else out_dtype
-    o = torch.empty((rows, d), dtype=out_dtype, device=o_parts.device) if out is None else out
-    lse_t = torch.empty(rows, dtype=torch.float32, device=o_parts.device) if lse is None else lse
+    o = (torch.empty((rows, d), dtype=out_dtype, device=o_parts.device) if out is None
+         else _out_tensor(out, "out", (rows, d), out_dtype, o_parts.device))
+    lse_t = (torch.empty(rows, dtype=torch.float32, device=o_parts.device) if lse is None
+             else _out_tensor(lse, "lse", (rows,), torch.float32, o_parts.device))
     _check(lib.osm_merge_lse(_ptr(o_parts), _ptr(lse_parts), rows, S, d, _dtype_code(o_parts.dtype),
                              _ptr(o), _dtype_code(out_dtype), _ptr(lse_t), _stream()))
     return o, lse_t
@@ -353,16 +381,20 @@ def attn_extend(q, k_new, v_new, state, *, scale=None, split_size=512, workspace
     lib = load_library()
     for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new)):
         _device_tensor(t, name, (torch.float32, torch.bfloat16))
-    sm, sl, so = state
-    for name, t in (("state_m", sm), ("state_l", sl), ("state_o", so)):
-        _device_tensor(t, name, (torch.float32,))
+    if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+        raise TypeError("q, k_new and v_new must have one dtype")
+    if q.dim() != 3 or k_new.dim() != 4 or tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError("q must be [B, Hq, d]; k_new, v_new [B, Hkv, n, d]")
     B, Hq, d = q.shape
-    _, Hkv, n, _ = k_new.shape
+    Bk, Hkv, n, dk_ = k_new.shape
+    if Bk != B or dk_ != d:
+        raise ValueError("k_new's batch and head_dim must match q's")
+    sm, sl, so = state
+    for name, t, shape in (("state_m", sm, (B * Hq,)), ("state_l", sl, (B * Hq,)), ("state_o", so, (B * Hq, d))):
+        _out_tensor(t, name, shape, torch.float32, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    nbytes = decode_workspace_bytes(B, Hq, max(n, 1), d, split_size)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, decode_workspace_bytes(B, Hq, max(n, 1), d, split_size), q.device)
     _check(lib.osm_attn_extend(_ptr(q), _ptr(k_new), _ptr(v_new), _dtype_code(q.dtype), B, Hq, Hkv, n, d,
                                float(scale), _ptr(sm), _ptr(sl), _ptr(so), int(split_size),
                                _ptr(workspace), workspace.numel(), _stream()))
