@@ -49,7 +49,7 @@ typedef enum {
     OSM_OK = 0,
     OSM_ERR_NULL = 1,        /* a required pointer is NULL */
     OSM_ERR_SHAPE = 2,       /* a size is negative, zero where it must not be, or inconsistent */
-    OSM_ERR_UNSUPPORTED = 3, /* valid request this build does not implement (dtype, head_dim, alignment) */
+    OSM_ERR_UNSUPPORTED = 3, /* valid request this library does not implement (dtype, head_dim, alignment) */
     OSM_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than osm_decode_workspace_bytes() */
     OSM_ERR_HIP = 5          /* a HIP runtime call failed (no device, launch failure) */
 } osm_status;
