@@ -1,8 +1,8 @@
 """osm_attn_bwd on the GPU against the oracle's gradients: element by
 element on small ragged shapes (several tiles, ragged tails, grouped
 heads, padding with NaN poison, empty lengths), whole heads at the full
-benchmark sizes, and the bit-exact causal and padding properties; head
-dims 128 and 64.
+benchmark sizes, the longest key sequences the ABI accepts, and the
+bit-exact causal and padding properties; head dims 128 and 64.
 
 The forward that feeds the backward is the GPU forward (its O and LSE), as
 in use; the oracle differentiates the exact forward of the same bf16 inputs.
@@ -241,3 +241,46 @@ def test_random_sweep(orc, d, seed0, cases):
                                       seqlens_q=sq, seqlens_k=sk, poison=sk is not None)
         do = inputs.output_grad(B, Hq, Nq, d, seed + 1, seqlens_q=sq, poison=sq is not None)
         check_all(run(inp, do), oracle(orc, inp, do), f"sweep d={d} {case}")
+
+
+@pytest.mark.parametrize("d,Nk", [(128, (1 << 23) - 1), (64, (1 << 24) - 1)])
+def test_max_key_length_and_head_offsets(orc, d, Nk):
+    """The longest key sequence the backward accepts at each head dim (one
+    head's K just under 2 GiB, a ragged last key block), on three KV heads,
+    so that the last head starts 4 GiB into K, V, dK and dV; GQA 2:1, four
+    queries.  dQ of the last query head and sampled dK, dV rows of the last
+    KV head (both of its query heads summed) against the oracle; every
+    gradient finite."""
+    import torch
+    B, Hq, Hkv, Nq = 1, 6, 3, 4
+    announce(f"bwd max key length B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d}")
+    ktab, kidx = inputs.tiled_rows(Hkv * Nk, d, seed=inputs.SEED_BASE + 71 + d)
+    vtab, vidx = inputs.tiled_rows(Hkv * Nk, d, seed=inputs.SEED_BASE + 72 + d)
+    qbits = inputs.to_bf16_bits(inputs.normal_f32(inputs.rng(inputs.SEED_BASE + 73 + d), (B, Hq, Nq, d)))
+    dobits = inputs.output_grad(B, Hq, Nq, d, inputs.SEED_BASE + 74 + d)
+    k = dev_bf16(ktab)[torch.from_numpy(kidx).to("cuda")].view(B, Hkv, Nk, d)
+    v = dev_bf16(vtab)[torch.from_numpy(vidx).to("cuda")].view(B, Hkv, Nk, d)
+    q, do = dev_bf16(qbits), dev_bf16(dobits)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = osm.attn_fwd(q, k, v, scale=scale)
+    dq, dk, dv = osm.attn_bwd(q, k, v, o, lse, do, scale=scale)
+    g = Hkv - 1                          # the last KV head and its query heads
+    heads = [2 * g, 2 * g + 1]
+    keys = np.array([0, 1, 31, 256, 1 << 20, Nk // 2 + 5, Nk - 2, Nk - 1])
+    dqh = host(dq[0, heads])
+    dkh = host(dk[0, g, torch.from_numpy(keys).to("cuda")])
+    dvh = host(dv[0, g, torch.from_numpy(keys).to("cuda")])
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all().item()
+    del k, v, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    sel = slice(g * Nk, (g + 1) * Nk)
+    kh = inputs.bf16_bits_to_f32(ktab)[kidx[sel]][None, None]
+    vh = inputs.bf16_bits_to_f32(vtab)[vidx[sel]][None, None]
+    qh = inputs.bf16_bits_to_f32(qbits[:, heads])
+    doh = inputs.bf16_bits_to_f32(dobits[:, heads])
+    dq_ref, dk_ref, dv_ref = orc.attention_bwd(qh, kh, vh, doh, scale=scale)
+    del kh, vh
+    check_grad(dqh, dq_ref[0], f"max keys d={d} dq")
+    check_grad(dkh, dk_ref[0, 0, keys], f"max keys d={d} dk")
+    check_grad(dvh, dv_ref[0, 0, keys], f"max keys d={d} dv")
