@@ -284,3 +284,47 @@ def test_max_key_length_and_head_offsets(orc, d, Nk):
     check_grad(dqh, dq_ref[0], f"max keys d={d} dq")
     check_grad(dkh, dk_ref[0, 0, keys], f"max keys d={d} dk")
     check_grad(dvh, dv_ref[0, 0, keys], f"max keys d={d} dv")
+
+
+@pytest.mark.parametrize("d,Nq", [(128, (1 << 23) - 1), (64, (1 << 24) - 1)])
+def test_max_query_length_and_head_offsets(orc, d, Nq):
+    """The longest query sequence the ABI accepts at each head dim, on three
+    query heads (the last starts 4 GiB into Q, O, dO and dQ), five keys, no
+    GQA.  The forward runs on its persistent grid (more blocks than compute
+    units); sampled O, LSE and dQ rows of the last head and all of its dK and
+    dV rows (sums over every query) against the oracle; every output finite."""
+    import torch
+    B, Hq, Hkv, Nk = 1, 3, 3, 5
+    announce(f"fwd+bwd max query length B={B} Hq={Hq} Nq={Nq} Nk={Nk} d={d}")
+    qtab, qidx = inputs.tiled_rows(Hq * Nq, d, seed=inputs.SEED_BASE + 81 + d)
+    gtab, gidx = inputs.tiled_rows(Hq * Nq, d, seed=inputs.SEED_BASE + 82 + d)
+    kbits = inputs.to_bf16_bits(inputs.normal_f32(inputs.rng(inputs.SEED_BASE + 83 + d), (B, Hkv, Nk, d)))
+    vbits = inputs.to_bf16_bits(inputs.normal_f32(inputs.rng(inputs.SEED_BASE + 84 + d), (B, Hkv, Nk, d)))
+    q = dev_bf16(qtab)[torch.from_numpy(qidx).to("cuda")].view(B, Hq, Nq, d)
+    do = dev_bf16(gtab)[torch.from_numpy(gidx).to("cuda")].view(B, Hq, Nq, d)
+    k, v = dev_bf16(kbits), dev_bf16(vbits)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = osm.attn_fwd(q, k, v, scale=scale)
+    dq, dk, dv = osm.attn_bwd(q, k, v, o, lse, do, scale=scale)
+    h = Hq - 1
+    rows = np.array([0, 1, 255, 256, 1 << 20, Nq // 2 + 3, Nq - 2, Nq - 1])
+    ridx = torch.from_numpy(rows).to("cuda")
+    oh, lh, dqh = host(o[0, h, ridx]), host(lse[0, h, ridx]), host(dq[0, h, ridx])
+    dkh, dvh = host(dk[0, h]), host(dv[0, h])
+    for t in (o, lse, dq, dk, dv):
+        assert torch.isfinite(t.float()).all().item()
+    del q, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    sel = slice(h * Nq, (h + 1) * Nq)
+    qh = inputs.bf16_bits_to_f32(qtab)[qidx[sel]][None, None]
+    doh = inputs.bf16_bits_to_f32(gtab)[gidx[sel]][None, None]
+    kh = inputs.bf16_bits_to_f32(kbits[:, h:h + 1])
+    vh = inputs.bf16_bits_to_f32(vbits[:, h:h + 1])
+    o_ref, lse_ref = orc.attention(np.ascontiguousarray(qh[:, :, rows]), kh, vh, scale=scale)
+    assert np.abs(oh - o_ref[0, 0]).max() <= 2e-2
+    assert np.abs(lh - lse_ref[0, 0]).max() <= 1e-3
+    dq_ref, dk_ref, dv_ref = orc.attention_bwd(qh, kh, vh, doh, scale=scale)
+    del qh, doh
+    check_grad(dqh, dq_ref[0, 0, rows], f"max queries d={d} dq")
+    check_grad(dkh, dk_ref[0, 0], f"max queries d={d} dk")
+    check_grad(dvh, dv_ref[0, 0], f"max queries d={d} dv")
