@@ -34,6 +34,7 @@ copy and a matrix-core loop) are timed once as "achievable" context.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
        python bench.py --sweep      (the forward over sequence lengths 1K-32K, head dims
                                      128 and 64, causal or not: one JSON line each)
+       python bench.py --sweep --sweep-bwd   (the same for the backward)
 """
 from __future__ import annotations
 
@@ -322,12 +323,16 @@ def summarize(name, trace_dir, out):
 
 
 def sweep(args):
-    """The forward (osm_attn_fwd) over sequence lengths 1K-32K at a fixed
-    16384 tokens per head group (B = 16384 / N), head dims 128 (32 heads) and
-    64 (64 heads), full length, causal or not; inputs N(0, 1) rounded to bf16,
-    drawn on the device from a seeded generator.  One JSON line per
-    configuration: median and minimum of the timed calls (HIP events on the
-    current stream) and TFLOP/s of the median against the bf16 peak."""
+    """The forward (osm_attn_fwd), or with --sweep-bwd the backward
+    (osm_attn_bwd, from the forward's O and LSE and an N(0, 1) output
+    gradient), over sequence lengths 1K-32K at a fixed 16384 tokens per head
+    group (B = 16384 / N), head dims 128 (32 heads) and 64 (64 heads), full
+    length, causal or not; inputs N(0, 1) rounded to bf16, drawn on the
+    device from a seeded generator.  One JSON line per configuration: median
+    and minimum of the timed calls (HIP events on the current stream) and
+    TFLOP/s of the median against the bf16 peak (4 N^2 d flop per head for
+    the forward, 10 N^2 d for the backward; halved, plus the diagonal, with
+    the causal mask)."""
     import torch
     import exact_attention_online_softmax_amd as osm
 
@@ -343,6 +348,13 @@ def sweep(args):
                 o = torch.empty_like(q)
                 lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
                 call = lambda: osm.attn_fwd(q, k, v, causal=causal, out=o, lse=lse)
+                if args.sweep_bwd:
+                    call()
+                    do = torch.randn((B, H, N, d), generator=gen, device="cuda").to(torch.bfloat16)
+                    ws = torch.empty(osm.attn_bwd_workspace_bytes(B, H, N), dtype=torch.uint8, device="cuda")
+                    grads = [torch.empty_like(q) for _ in range(3)]
+                    call = lambda: osm.attn_bwd(q, k, v, o, lse, do, causal=causal, workspace=ws,
+                                                dq=grads[0], dk=grads[1], dv=grads[2])
                 for _ in range(args.warmup):
                     call()
                 ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -356,11 +368,13 @@ def sweep(args):
                 ms = sorted(a.elapsed_time(b) for a, b in ev)
                 med = ms[len(ms) // 2]
                 pairs = B * H * (N * (N + 1) / 2 if causal else N * N)
-                tf = 4.0 * d * pairs / (med / 1e3) / 1e12
-                print(json.dumps({"sweep": "attn_fwd", "head_dim": d, "causal": causal, "batch": B, "heads": H,
+                tf = (10.0 if args.sweep_bwd else 4.0) * d * pairs / (med / 1e3) / 1e12
+                print(json.dumps({"sweep": "attn_bwd" if args.sweep_bwd else "attn_fwd", "head_dim": d, "causal": causal, "batch": B, "heads": H,
                                   "seq_len": N, "ms_median": round(med, 4), "ms_min": round(ms[0], 4),
                                   "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
-                del q, k, v, o, lse
+                del q, k, v, o, lse, call
+                if args.sweep_bwd:
+                    del do, ws, grads
     return 0
 
 
@@ -378,6 +392,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB per step (scales rocprof "
                          "FETCH_SIZE/WRITE_SIZE to bytes)")
+    ap.add_argument("--sweep-bwd", action="store_true",
+                    help="with --sweep: the backward instead of the forward")
     ap.add_argument("--sweep", action="store_true",
                     help="the forward over sequence lengths and head dims (one JSON line each)")
     ap.add_argument("--summarize", nargs=3, metavar=("NAME", "TRACE_DIR", "OUT"), default=None,
