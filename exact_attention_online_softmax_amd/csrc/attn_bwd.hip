@@ -11,11 +11,16 @@
 // D_i equals dO_i . O_i (O_i = sum_j P_ij v_j), which is how it is computed
 // here: one dot product per row instead of a pass over the row of P.
 //
-// Three kernels, enqueued in order on one stream:
-//  * attn_bwd_pre: per query row, D = dO . O and the log-sum-exp in base-2
-//    units (lse2 = lse log2 e, so P = exp2(s scale log2 e - lse2)).  Rows
-//    that see no key (padding, or lse = -inf) get (lse2, D) = (+inf, 0): their
-//    rebuilt weights are exactly 0 and they add nothing.
+// Two kernels, enqueued in order on one stream:
+//  * attn_bwd_dq: query-major, laid out like the forward.  A workgroup owns
+//    256 queries (32 per wave, eight waves, two per SIMD; Q and dO fragments
+//    and the dQ accumulators in registers) and streams K and V tiles of
+//    32 keys through a ring of three LDS slots: S^T = K Q^T, dP^T = V dO^T,
+//    dS^T, and dQ^T += K^T dS^T.  Before its first tile it forms, per query
+//    row, D = dO . O and the log-sum-exp in base-2 units (lse2 = lse log2 e,
+//    so P = exp2(s scale log2 e - lse2)), and stores (lse2, D) for the next
+//    kernel.  Rows that see no key (lse = -inf) get (lse2, D) = (+inf, 0):
+//    their rebuilt weights are exactly 0 and they add nothing.
 //  * attn_bwd_dkdv: key-major.  A workgroup owns 256 keys of one key/value
 //    head, 32 per wave, eight waves (two per SIMD, so one wave's matrix
 //    products overlap the other's exponentials and LDS reads); each wave's
@@ -28,11 +33,6 @@
 //    - lse2), dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS, the
 //    transposed operands read from LDS with ds_read_b64_tr_b16.  dK and dV
 //    sum over the whole head group in registers: no atomics.
-//  * attn_bwd_dq: query-major, laid out like the forward.  A workgroup owns
-//    256 queries (32 per wave, eight waves, two per SIMD; Q and dO fragments
-//    and the dQ accumulators in registers) and streams K and V tiles of
-//    32 keys through a ring of three LDS slots: S^T = K Q^T, dP^T = V dO^T,
-//    dS^T, and dQ^T += K^T dS^T.
 // Splitting dQ from dK/dV computes S and dP twice (7 matrix products per
 // score tile instead of 5) but needs no atomic accumulation, so the result
 // is deterministic.
@@ -43,7 +43,7 @@
 // valid length into zeros (NaN padding never reaches an MFMA); LDS rows are
 // XOR-swizzled at 16-byte granularity.
 //
-// The three kernels are templates over the head dim, instantiated for 128
+// The two kernels are templates over the head dim, instantiated for 128
 // and 64: at 64 a row is 128 bytes, a k-step loop has four steps instead of
 // eight and a gradient two 32-dim output tiles instead of four.
 #include "osm_device.h"
@@ -175,43 +175,6 @@ __device__ __forceinline__ void dma4(const __amdgpu_buffer_rsrc_t &r, void *lds,
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, kRsrcWord3);
-}
-
-// ---------------------------------------------------------------------------
-// attn_bwd_pre: D = dO . O and lse2 per query row; HD / 8 lanes per row.
-// ---------------------------------------------------------------------------
-constexpr int PRE_NT = 256;
-template <int HD> constexpr int kPreRows = PRE_NT / (HD / 8);
-
-template <int HD>
-__global__ void __launch_bounds__(PRE_NT)
-attn_bwd_pre(const uint16_t *__restrict__ O, const uint16_t *__restrict__ dO,
-             const float *__restrict__ LSE, float2 *__restrict__ LD, int64_t rows, int Nq, int Hq,
-             const int32_t *__restrict__ seqlens_q) {
-    constexpr int LPR = HD / 8;                   // lanes per row, 8 dims each
-    const int64_t r = (int64_t)blockIdx.x * kPreRows<HD> + (threadIdx.x / LPR);
-    const int j = threadIdx.x % LPR;
-    if (r >= rows) return;                        // whole groups of lanes leave together
-    const uint4 o = *reinterpret_cast<const uint4 *>(O + r * HD + 8 * j);
-    const uint4 g = *reinterpret_cast<const uint4 *>(dO + r * HD + 8 * j);
-    float acc = bf16_lo(o.x) * bf16_lo(g.x);
-    acc = fmaf(bf16_hi(o.x), bf16_hi(g.x), acc);
-    acc = fmaf(bf16_lo(o.y), bf16_lo(g.y), acc);
-    acc = fmaf(bf16_hi(o.y), bf16_hi(g.y), acc);
-    acc = fmaf(bf16_lo(o.z), bf16_lo(g.z), acc);
-    acc = fmaf(bf16_hi(o.z), bf16_hi(g.z), acc);
-    acc = fmaf(bf16_lo(o.w), bf16_lo(g.w), acc);
-    acc = fmaf(bf16_hi(o.w), bf16_hi(g.w), acc);
-#pragma unroll
-    for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
-    if (j == 0) {
-        const int i = (int)(r % Nq);
-        const int b = (int)(r / ((int64_t)Nq * Hq));
-        const int Lq = seqlens_q ? clampi(seqlens_q[b], 0, Nq) : Nq;
-        const float lse = LSE[r];
-        const bool live = (i < Lq) && (lse != kNegInf);
-        LD[r] = live ? make_float2(lse * kLog2e, acc) : make_float2(kPosInf, 0.0f);
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -501,8 +464,9 @@ template <int HD> constexpr int kDqTileb = DQ_BK * BGeo<HD>::ROWB;   // bytes pe
 template <int HD>
 __global__ void __launch_bounds__(DQ_NT, 1)
 attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
-            const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
-            const float2 *__restrict__ LD, uint16_t *__restrict__ dQ, int Hq, int Hkv, int Nq,
+            const uint16_t *__restrict__ V, const uint16_t *__restrict__ O,
+            const uint16_t *__restrict__ dO, const float *__restrict__ LSE,
+            float2 *__restrict__ LD, uint16_t *__restrict__ dQ, int Hq, int Hkv, int Nq,
             int Nk, const int32_t *__restrict__ seqlens_q, const int32_t *__restrict__ seqlens_k,
             float scale_log2, float scale, int causal, int nqb, int xcd_heads) {
     using G = BGeo<HD>;
@@ -567,25 +531,31 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     if (Lk % DQ_BK) wmask = min(wmask, Lk / DQ_BK);
 
     // Q and dO fragments (B operands): lane (g, c) holds row qw0 + 32 qb + c,
-    // dims (HD / 2) g + 8 ks + 0..7; rows at or past Lq are zero
+    // dims (HD / 2) g + 8 ks + 0..7; rows at or past Lq are zero.
+    // The row's D = dO . O and lse2 = lse log2 e are formed here from the
+    // same fragments of dO and O (lanes c and c + 32 hold the two halves of
+    // the row) and stored for attn_bwd_dkdv, which runs after this kernel.
+    // A row that sees no key (lse = -inf) gets (lse2, D) = (+inf, 0): its
+    // rebuilt weights are exactly 0.
     bf16x8 qf[DQ_NQB][KS], df[DQ_NQB][KS];
-    float l2[DQ_NQB], dd[DQ_NQB];
+    uint4 wx[DQ_NQB][KS];
+    float lse[DQ_NQB], l2[DQ_NQB], dd[DQ_NQB];
 #pragma unroll
     for (int qb = 0; qb < DQ_NQB; ++qb) {
         const int qi = qw0 + 32 * qb + c;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             uint4 wq = make_uint4(0, 0, 0, 0), wo = make_uint4(0, 0, 0, 0);
+            wx[qb][ks] = make_uint4(0, 0, 0, 0);
             if (qi < Lq) {
                 wq = *reinterpret_cast<const uint4 *>(Q + (qrow0 + qi) * HD + (HD / 2) * g + 8 * ks);
                 wo = *reinterpret_cast<const uint4 *>(dO + (qrow0 + qi) * HD + (HD / 2) * g + 8 * ks);
+                wx[qb][ks] = *reinterpret_cast<const uint4 *>(O + (qrow0 + qi) * HD + (HD / 2) * g + 8 * ks);
             }
             qf[qb][ks] = __builtin_bit_cast(bf16x8, wq);
             df[qb][ks] = __builtin_bit_cast(bf16x8, wo);
         }
-        const float2 x = (qi < Lq) ? LD[qrow0 + qi] : make_float2(kPosInf, 0.0f);
-        l2[qb] = x.x;
-        dd[qb] = x.y;
+        lse[qb] = (qi < Lq) ? LSE[qrow0 + qi] : kNegInf;
     }
     f32x16 dqa[DQ_NQB][NDT];
 #pragma unroll
@@ -721,6 +691,30 @@ attn_bwd_dq(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
 
     issue(k0, v0, 0);
     issue(k1, v1, 1);
+    // (lse2, D) of this wave's rows, under the first tiles' loads
+#pragma unroll
+    for (int qb = 0; qb < DQ_NQB; ++qb) {
+        const int qi = qw0 + 32 * qb + c;
+        float acc = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const uint4 o = wx[qb][ks];
+            const uint4 d = __builtin_bit_cast(uint4, df[qb][ks]);
+            acc = fmaf(bf16_lo(o.x), bf16_lo(d.x), acc);
+            acc = fmaf(bf16_hi(o.x), bf16_hi(d.x), acc);
+            acc = fmaf(bf16_lo(o.y), bf16_lo(d.y), acc);
+            acc = fmaf(bf16_hi(o.y), bf16_hi(d.y), acc);
+            acc = fmaf(bf16_lo(o.z), bf16_lo(d.z), acc);
+            acc = fmaf(bf16_hi(o.z), bf16_hi(d.z), acc);
+            acc = fmaf(bf16_lo(o.w), bf16_lo(d.w), acc);
+            acc = fmaf(bf16_hi(o.w), bf16_hi(d.w), acc);
+        }
+        acc += __shfl_xor(acc, 32, 64);
+        const bool live = lse[qb] != kNegInf;
+        l2[qb] = live ? lse[qb] * kLog2e : kPosInf;
+        dd[qb] = live ? acc : 0.0f;
+        if (g == 0 && qi < Lq) LD[qrow0 + qi] = make_float2(l2[qb], dd[qb]);
+    }
     const int nend = ((ntiles + 2) / 3) * 3;
     for (int j = 0; j < nend; j += 3) {
         iter(Slot<0>{}, j);
@@ -761,9 +755,14 @@ hipError_t launch_bwd(const AttnBwdArgs &a, hipStream_t s) {
     const uint16_t *v = static_cast<const uint16_t *>(a.v), *o = static_cast<const uint16_t *>(a.o);
     const uint16_t *dout = static_cast<const uint16_t *>(a.dout);
     const float scale_log2 = a.scale * kLog2e;
+    // attn_bwd_dq first: it stores the (lse2, D) rows that attn_bwd_dkdv reads
     if (rows > 0) {
-        hipLaunchKernelGGL(attn_bwd_pre<HD>, dim3((unsigned)((rows + kPreRows<HD> - 1) / kPreRows<HD>)),
-                           dim3(PRE_NT), 0, s, o, dout, a.lse, ld, rows, a.seqlen_q, a.heads_q, a.seqlens_q);
+        const int nqb = (a.seqlen_q + DQ_BQ - 1) / DQ_BQ;
+        const int nheads = a.batch * a.heads_q;
+        const int xcd_heads = (nheads % 8 == 0) ? 1 : 0;
+        hipLaunchKernelGGL(attn_bwd_dq<HD>, dim3((unsigned)((int64_t)nqb * nheads)), dim3(DQ_NT), 0, s, q, k, v,
+                           o, dout, a.lse, ld, static_cast<uint16_t *>(a.dq), a.heads_q, a.heads_kv, a.seqlen_q,
+                           a.seqlen_k, a.seqlens_q, a.seqlens_k, scale_log2, a.scale, a.causal, nqb, xcd_heads);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -782,16 +781,6 @@ hipError_t launch_bwd(const AttnBwdArgs &a, hipStream_t s) {
                                static_cast<uint16_t *>(a.dk), static_cast<uint16_t *>(a.dv), a.heads_q,
                                a.heads_kv, a.seqlen_q, a.seqlen_k, a.seqlens_q, a.seqlens_k, scale_log2,
                                a.scale, nkb, xcd_heads);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (rows > 0) {
-        const int nqb = (a.seqlen_q + DQ_BQ - 1) / DQ_BQ;
-        const int nheads = a.batch * a.heads_q;
-        const int xcd_heads = (nheads % 8 == 0) ? 1 : 0;
-        hipLaunchKernelGGL(attn_bwd_dq<HD>, dim3((unsigned)((int64_t)nqb * nheads)), dim3(DQ_NT), 0, s, q, k, v,
-                           dout, ld, static_cast<uint16_t *>(a.dq), a.heads_q, a.heads_kv, a.seqlen_q,
-                           a.seqlen_k, a.seqlens_q, a.seqlens_k, scale_log2, a.scale, a.causal, nqb, xcd_heads);
         return hipGetLastError();
     }
     return hipSuccess;

@@ -217,9 +217,9 @@ size_t osm_attn_bwd_workspace_bytes(int32_t batch, int32_t heads_q, int32_t seql
  *         a query row that sees no key contributes nothing.
  *   workspace  DEVICE memory of at least osm_attn_bwd_workspace_bytes()
  *         bytes (caller-owned, 256-byte aligned, contents on entry ignored).
- * Three kernels are enqueued on `stream`: the per-row (lse, dO . O), then
- * dK/dV (key-major), then dQ (query-major).  No atomics: the result is
- * deterministic.
+ * Two kernels are enqueued on `stream`: dQ (query-major), which also stores
+ * each row's (lse, dO . O) in the workspace, then dK/dV (key-major).  No
+ * atomics: the result is deterministic.
  * Supported: dtype OSM_BF16, head_dim 128 or 64, batch * heads_q < 2^31;
  * fp32 accumulation, P and dS rounded to bf16 as matrix-product operands,
  * gradients rounded to bf16 once at the end; every pointer 16-byte aligned.
